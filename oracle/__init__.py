@@ -1,0 +1,183 @@
+"""fp64 CPU oracle for paged variable-length attention -- TEST INFRASTRUCTURE.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never does: it
+shares no code with the HIP path, and a product call that reached this code
+would be a CPU fallback.
+
+The arithmetic lives in ``pa_oracle.c`` (plain C, fp64, compiled with gcc -O2,
+no fast-math).  This wrapper only marshals host tensors into it.  Every
+function cites, in the C header, the passage of the pages it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libpa_oracle.so")
+_lib = None
+
+F32, BF16 = 0, 1
+
+
+def build(force: bool = False, out_path: Optional[str] = None, src_path: Optional[str] = None) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, strict IEEE).  Returns the .so path."""
+    out_path = out_path or _LIB_PATH
+    src_path = src_path or _SRC
+    if force or not os.path.exists(out_path) or os.path.getmtime(out_path) < os.path.getmtime(src_path):
+        tmp = out_path + f".tmp{os.getpid()}"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+               "-ffp-contract=off", "-I", _HERE, src_path, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out_path)
+    return out_path
+
+
+def _load(path: Optional[str] = None):
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    if _lib is None:
+        _lib = _declare(ctypes.CDLL(build()))
+    return _lib
+
+
+def _declare(lib):
+    P, I, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_double
+    lib.pa_ref_num_threads.restype = ctypes.c_int
+    lib.pa_ref_reshape_and_cache.argtypes = [P, P, P, P, P, I, I, I, I, I, I]
+    lib.pa_ref_expand_block_tables.argtypes = [P, P, I, I, I, I, I]
+    lib.pa_ref_attention.argtypes = [P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, I, I, I, D, I]
+    lib.pa_ref_attention_partials.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
+                                              D, I, I, I]
+    lib.pa_ref_split_reduce.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I]
+    for f in ("pa_ref_reshape_and_cache", "pa_ref_expand_block_tables", "pa_ref_attention",
+              "pa_ref_attention_partials", "pa_ref_split_reduce"):
+        getattr(lib, f).restype = ctypes.c_int
+    return lib
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    if t is None:
+        return ctypes.c_void_p(0)
+    if isinstance(t, np.ndarray):
+        assert t.flags["C_CONTIGUOUS"]
+        return ctypes.c_void_p(t.ctypes.data)
+    assert t.device.type == "cpu" and t.is_contiguous()
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return F32
+    if dt == torch.bfloat16:
+        return BF16
+    raise TypeError(f"oracle supports float32 and bfloat16, not {dt}")
+
+
+def num_threads(lib=None) -> int:
+    return int((lib or _load()).pa_ref_num_threads())
+
+
+def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, lib=None) -> None:
+    """In place on host tensors: caches[slot // bs, slot % bs] = rows; slot < 0 skipped."""
+    lib = lib or _load()
+    T, hkv, d = key.shape
+    nb, bs = key_cache.shape[:2]
+    rc = lib.pa_ref_reshape_and_cache(_ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+                                      _ptr(slot_mapping), T, hkv, d, nb, bs, _dtype_code(key.dtype))
+    if rc:
+        raise ValueError("oracle reshape_and_cache: bad arguments")
+
+
+def expand_block_tables(block_tables: torch.Tensor, ratio: int, lib=None) -> torch.Tensor:
+    lib = lib or _load()
+    B, nb = block_tables.shape
+    dst = torch.empty((B, nb * ratio), dtype=torch.int32)
+    rc = lib.pa_ref_expand_block_tables(_ptr(dst), _ptr(block_tables), B, nb, nb, nb * ratio, ratio)
+    if rc:
+        raise ValueError("oracle expand_block_tables: bad arguments")
+    return dst
+
+
+def _common(w_q, key_cache, cu, seq_lens, block_tables):
+    TQ, hq, d = w_q.shape
+    nb, bs, hkv, _ = key_cache.shape
+    return TQ, hq, d, nb, bs, hkv, int(seq_lens.numel()), int(block_tables.shape[1])
+
+
+def attention(q, key_cache, value_cache, cu_seqlens_q, seq_lens, block_tables, scale: float,
+              rows: Optional[Sequence[Sequence[int]]] = None, lib=None) -> torch.Tensor:
+    """fp64 masked softmax(QK^T*scale)V through the block tables.
+    rows=None -> [total_q, Hq, D]; rows=[(t, h), ...] -> [n, D]."""
+    lib = lib or _load()
+    TQ, hq, d, nb, bs, hkv, B, mb = _common(q, key_cache, cu_seqlens_q, seq_lens, block_tables)
+    if rows is None:
+        out = torch.empty((TQ, hq, d), dtype=torch.float64)
+        tok = head = None
+        n = 0
+    else:
+        rows = np.asarray(rows, dtype=np.int32).reshape(-1, 2)
+        tok = np.ascontiguousarray(rows[:, 0])
+        head = np.ascontiguousarray(rows[:, 1])
+        n = len(rows)
+        out = torch.empty((n, d), dtype=torch.float64)
+    rc = lib.pa_ref_attention(_ptr(out), _ptr(tok), _ptr(head), n, _ptr(q), _ptr(key_cache),
+                              _ptr(value_cache), _ptr(cu_seqlens_q), _ptr(seq_lens),
+                              _ptr(block_tables), B, TQ, mb, hq, hkv, d, nb, bs, float(scale),
+                              _dtype_code(q.dtype))
+    if rc:
+        raise ValueError("oracle attention: bad arguments")
+    return out
+
+
+def max_partitions(max_seq_len: int, partition_size: int) -> int:
+    return (max_seq_len + partition_size - 1) // partition_size
+
+
+def attention_partials(q, key_cache, value_cache, cu_seqlens_q, seq_lens, block_tables,
+                       scale: float, partition_size: int, max_parts: Optional[int] = None, lib=None):
+    """Split-KV partials (o, m, l) in the log2-space contract; untouched entries are NaN."""
+    lib = lib or _load()
+    TQ, hq, d, nb, bs, hkv, B, mb = _common(q, key_cache, cu_seqlens_q, seq_lens, block_tables)
+    mp = max_parts or max_partitions(int(seq_lens.max()), partition_size)
+    o = torch.full((TQ, hq, mp, d), float("nan"), dtype=torch.float64)
+    m = torch.full((TQ, hq, mp), float("nan"), dtype=torch.float64)
+    l = torch.full((TQ, hq, mp), float("nan"), dtype=torch.float64)
+    rc = lib.pa_ref_attention_partials(_ptr(o), _ptr(m), _ptr(l), _ptr(q), _ptr(key_cache),
+                                       _ptr(value_cache), _ptr(cu_seqlens_q), _ptr(seq_lens),
+                                       _ptr(block_tables), B, TQ, mb, hq, hkv, d, nb, bs,
+                                       float(scale), _dtype_code(q.dtype), partition_size, mp)
+    if rc:
+        raise ValueError("oracle attention_partials: bad arguments")
+    return o, m, l
+
+
+def split_reduce(o, m, l, cu_seqlens_q, seq_lens, partition_size: int, lib=None) -> torch.Tensor:
+    lib = lib or _load()
+    TQ, hq, mp, d = o.shape
+    out = torch.empty((TQ, hq, d), dtype=torch.float64)
+    rc = lib.pa_ref_split_reduce(_ptr(out), _ptr(o), _ptr(m), _ptr(l), _ptr(cu_seqlens_q),
+                                 _ptr(seq_lens), int(seq_lens.numel()), TQ, hq, d, partition_size, mp)
+    if rc:
+        raise ValueError("oracle split_reduce: bad arguments")
+    return out
+
+
+def run_workload(w, rows=None, lib=None) -> torch.Tensor:
+    """Oracle result for a ``workloads.Workload``: applies its cache write first
+    (on copies of the caches) when it has one, then attention on the stored
+    block size."""
+    kc, vc = w.key_cache, w.value_cache
+    if w.slot_mapping is not None:
+        kc, vc = kc.clone(), vc.clone()
+        reshape_and_cache(w.new_key, w.new_value, kc, vc, w.slot_mapping, lib=lib)
+    return attention(w.q, kc, vc, w.cu_seqlens_q, w.seq_lens, w.block_tables, w.scale, rows=rows,
+                     lib=lib)

@@ -1,0 +1,100 @@
+/*
+ * pa_oracle.h -- plain fp64 CPU oracle for paged variable-length attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes
+ * or calls this code; only the tests, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no source with the HIP path.
+ *
+ * It computes, slowly and directly, what the pages define:
+ *   - the cache write that scatters projected K/V rows into fixed-size pages
+ *     (vllm-metal kernel walkthrough, "three Metal kernels": reshape_and_cache);
+ *   - masked softmax(Q K^T * scale) V over keys gathered through per-request
+ *     block tables (same page, "What is Paged Attention"), for queries packed
+ *     as [total_q, Hq, D] with request boundaries in cu_seqlens
+ *     (v0.28.0 release post, "Packed queries and paged KV");
+ *   - the split-KV form: per partition, the log2-space (max, exp-sum)
+ *     statistics and the normalised partial output, and their merge
+ *     (kernel walkthrough, GQA decode tip 4 "Split-KV partitions").
+ *
+ * Readings where the pages are silent (all of them stated in the design notes):
+ *   - seq_lens[r] counts every key request r sees, its own new tokens included;
+ *   - causal alignment is bottom-right: query j of request r sits at absolute
+ *     position ctx + j, ctx = seq_lens[r] - q_len[r], and sees keys 0..ctx+j;
+ *   - query head h reads KV head h / (Hq / Hkv);
+ *   - caches are [num_blocks, block_size, Hkv, D]; logical key i of request r
+ *     lives in block block_tables[r][i / block_size], slot i % block_size;
+ *   - slot_mapping < 0 means "skip this token".
+ *
+ * Element types: PA_REF_F32 = IEEE float32, PA_REF_BF16 = bfloat16 (the upper
+ * 16 bits of a float32).  Every input value is widened exactly to double and
+ * all arithmetic is double; results are returned unrounded in double.
+ *
+ * Return value of every function: 0 on success, -1 on an argument the oracle
+ * cannot interpret (bad dtype, negative sizes, a key index outside the block
+ * table or the pool, or ctx < 0).
+ */
+#ifndef PA_ORACLE_H
+#define PA_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { PA_REF_F32 = 0, PA_REF_BF16 = 1 };
+
+/* Threads the OpenMP runtime will use for the row loops. */
+int pa_ref_num_threads(void);
+
+/* Cache write: for t in [0, T): s = slot_mapping[t]; s < 0 -> skip;
+ * caches[s / bs][s % bs][:][:] = rows[t][:][:], for K and V.  A byte copy. */
+int pa_ref_reshape_and_cache(const void *key, const void *value, void *key_cache,
+                             void *value_cache, const int64_t *slot_mapping, int32_t num_tokens,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                             int32_t block_size, int32_t dtype);
+
+/* Kernel-page view of a block table whose blocks hold `ratio` kernel pages:
+ * dst[r][ratio*b + j] = ratio * src[r][b] + j, and -1 stays -1. */
+int pa_ref_expand_block_tables(int32_t *dst, const int32_t *src, int32_t num_seqs,
+                               int32_t src_stride, int32_t src_blocks, int32_t dst_stride,
+                               int32_t ratio);
+
+/* Attention for selected (token, head) pairs: out[n][D] (double) for
+ * n in [0, n_rows), row n = (tok[n], head[n]).  Pass tok = head = NULL to
+ * compute every (t, h) in the natural order t*Hq + h (out = [total_q][Hq][D]). */
+int pa_ref_attention(double *out, const int32_t *tok, const int32_t *head, int32_t n_rows,
+                     const void *q, const void *key_cache, const void *value_cache,
+                     const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                     const int32_t *block_tables, int32_t num_seqs, int32_t total_q,
+                     int32_t max_blocks_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t num_blocks, int32_t block_size, double scale,
+                     int32_t dtype);
+
+/* Split-KV partials for every (t, h): partition k of the query at absolute
+ * position p covers keys [k*P, min((k+1)*P, p+1)), k < ceil((p+1)/P).
+ *   m[t][h][k]    = max over the partition of s_i * log2(e),  s_i = scale * q.k_i
+ *   l[t][h][k]    = sum 2^(s_i*log2(e) - m)
+ *   o[t][h][k][:] = sum 2^(s_i*log2(e) - m) * v_i / l
+ * Entries for k >= ceil((p+1)/P) are left untouched.  Arrays are dense with
+ * max_parts partitions per (t, h). */
+int pa_ref_attention_partials(double *o, double *m, double *l, const void *q,
+                              const void *key_cache, const void *value_cache,
+                              const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                              const int32_t *block_tables, int32_t num_seqs, int32_t total_q,
+                              int32_t max_blocks_per_seq, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                              int32_t block_size, double scale, int32_t dtype,
+                              int32_t partition_size, int32_t max_parts);
+
+/* Merge of the partials above: with n = ceil((p+1)/P), M = max_k m_k,
+ * w_k = l_k * 2^(m_k - M):  out[t][h][:] = sum_k w_k o_k / sum_k w_k. */
+int pa_ref_split_reduce(double *out, const double *o, const double *m, const double *l,
+                        const int32_t *cu_seqlens_q, const int32_t *seq_lens, int32_t num_seqs,
+                        int32_t total_q, int32_t num_q_heads, int32_t head_dim,
+                        int32_t partition_size, int32_t max_parts);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

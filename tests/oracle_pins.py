@@ -1,0 +1,358 @@
+"""Pins for the fp64 oracle: checks that tie it to something other than itself.
+
+Each ``pin_*`` takes an oracle library handle so the same checks can run
+against a deliberately broken build of the oracle (see
+``test_oracle.py::test_pins_catch_planted_mistakes``).  They use:
+
+* hand-derived closed-form cases in ``tests/golden/`` (each cites its passage);
+* independent dense computations -- numpy fp64 with an explicit mask, and
+  torch's scaled_dot_product_attention in fp64 on the CPU -- over K/V gathered
+  contiguously through the block table;
+* invariances the pages imply: physical page order, page size (including a
+  144-token block seen as nine 16-token pages), the split-KV partition size,
+  and running a request alone in a contiguous cache;
+* closed forms of softmax attention (single key, equal keys, constant V,
+  zero query, a dominant key, repeated KV heads, plain top-left causal).
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------- helpers
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name + ".json")) as f:
+        return json.load(f)
+
+
+def golden_inputs(c):
+    dt = torch.float32
+    hkv, d, bs, nb = c["num_kv_heads"], c["head_dim"], c["block_size"], c["num_blocks"]
+    kc = torch.full((nb, bs, hkv, d), float("nan"), dtype=dt)
+    vc = torch.full((nb, bs, hkv, d), float("nan"), dtype=dt)
+    bt = torch.tensor(c["block_tables"], dtype=torch.int32)
+    for pos, rows in c["cache_rows"].items():
+        i = int(pos)
+        blk = int(bt[0, i // bs])
+        kc[blk, i % bs] = torch.tensor(rows["k"], dtype=dt)[0]
+        vc[blk, i % bs] = torch.tensor(rows["v"], dtype=dt)[0]
+    q = torch.tensor(c["q"], dtype=dt)
+    cu = torch.tensor(c["cu_seqlens_q"], dtype=torch.int32)
+    sl = torch.tensor(c["seq_lens"], dtype=torch.int32)
+    return q, kc, vc, cu, sl, bt, float(c["scale"])
+
+
+def run(w, lib, rows=None):
+    return oracle.run_workload(w, rows=rows, lib=lib)
+
+
+def gather_request(w, r):
+    """Contiguous K/V [L, Hkv, D] (fp64) of request r, read through its block table."""
+    L = int(w.seq_lens[r])
+    pos = np.arange(L)
+    blocks = w.block_tables[r].numpy()[pos // w.block_size]
+    offs = pos % w.block_size
+    K = w.key_cache.double().numpy()[blocks, offs]
+    V = w.value_cache.double().numpy()[blocks, offs]
+    return K, V
+
+
+def dense_numpy(w):
+    """softmax(QK^T*scale + mask)V per request on contiguous K/V, numpy fp64."""
+    q = w.q.double().numpy()
+    out = np.zeros(q.shape)
+    G = w.num_q_heads // w.num_kv_heads
+    cu = w.cu_seqlens_q.numpy()
+    for r in range(w.num_seqs):
+        K, V = gather_request(w, r)
+        L, ql = K.shape[0], cu[r + 1] - cu[r]
+        if ql == 0:
+            continue
+        ctx = L - ql
+        Kx, Vx = np.repeat(K, G, axis=1), np.repeat(V, G, axis=1)
+        Q = q[cu[r]:cu[r + 1]]
+        S = np.einsum("jhd,ihd->hji", Q, Kx) * w.scale
+        mask = np.arange(L)[None, :] <= (ctx + np.arange(ql))[:, None]
+        S = np.where(mask[None], S, -np.inf)
+        S = S - S.max(axis=-1, keepdims=True)
+        P = np.exp(S)
+        P /= P.sum(axis=-1, keepdims=True)
+        out[cu[r]:cu[r + 1]] = np.einsum("hji,ihd->jhd", P, Vx)
+    return torch.from_numpy(out)
+
+
+def dense_sdpa(w):
+    """torch scaled_dot_product_attention in fp64 on the CPU, KV heads repeated."""
+    q = w.q.double()
+    out = torch.zeros_like(q)
+    G = w.num_q_heads // w.num_kv_heads
+    cu = w.cu_seqlens_q.numpy()
+    for r in range(w.num_seqs):
+        K, V = gather_request(w, r)
+        L, ql = K.shape[0], int(cu[r + 1] - cu[r])
+        if ql == 0:
+            continue
+        ctx = L - ql
+        Kt = torch.from_numpy(K).repeat_interleave(G, dim=1).permute(1, 0, 2)
+        Vt = torch.from_numpy(V).repeat_interleave(G, dim=1).permute(1, 0, 2)
+        Qt = q[cu[r]:cu[r + 1]].permute(1, 0, 2)
+        mask = torch.arange(L)[None, :] <= (ctx + torch.arange(ql))[:, None]
+        o = F.scaled_dot_product_attention(Qt, Kt, Vt, attn_mask=mask, scale=w.scale)
+        out[cu[r]:cu[r + 1]] = o.permute(1, 0, 2)
+    return out
+
+
+def micro_cases():
+    """Small ragged batches spanning the geometries, page sizes and dtypes."""
+    specs = [
+        dict(num_seqs=3, max_q=1, max_ctx=39, num_q_heads=4, num_kv_heads=1, head_dim=64, block_size=16),
+        dict(num_seqs=2, max_q=5, max_ctx=35, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=8),
+        dict(num_seqs=3, max_q=4, max_ctx=30, num_q_heads=6, num_kv_heads=1, head_dim=256, block_size=32),
+        dict(num_seqs=2, max_q=9, max_ctx=20, num_q_heads=2, num_kv_heads=2, head_dim=64, block_size=16),
+    ]
+    out = []
+    for i, s in enumerate(specs):
+        for dt in (torch.float32, torch.bfloat16):
+            out.append(W.random_case(100 + 2 * i + (dt == torch.bfloat16), dtype=dt, **s))
+    return out
+
+
+def with_cache(w, key_cache, value_cache, block_tables, block_size):
+    import dataclasses
+    return dataclasses.replace(w, key_cache=key_cache, value_cache=value_cache,
+                               block_tables=block_tables, block_size=block_size,
+                               num_blocks=key_cache.shape[0])
+
+
+def relayout(w, block_size, seed, ratio=1):
+    """Same logical K/V stored with another page size, pages in a random order.
+    With ratio > 1 the pool holds blocks of block_size*ratio tokens."""
+    rng = np.random.default_rng(seed)
+    bsz = block_size * ratio
+    pages = [(int(s) + bsz - 1) // bsz for s in w.seq_lens]
+    nb = sum(pages) + 2
+    perm = rng.permutation(nb)
+    kc = torch.full((nb, bsz, w.num_kv_heads, w.head_dim), float("nan"), dtype=w.dtype)
+    vc = kc.clone()
+    bt = torch.full((w.num_seqs, max(pages)), -1, dtype=torch.int32)
+    o = 0
+    for r in range(w.num_seqs):
+        bt[r, :pages[r]] = torch.from_numpy(perm[o:o + pages[r]].astype(np.int32))
+        o += pages[r]
+        L = int(w.seq_lens[r])
+        pos = np.arange(L)
+        src_b = w.block_tables[r].numpy()[pos // w.block_size]
+        src_o = pos % w.block_size
+        dst_b = bt[r].numpy()[pos // bsz]
+        dst_o = pos % bsz
+        kc[dst_b, dst_o] = w.key_cache[src_b, src_o]
+        vc[dst_b, dst_o] = w.value_cache[src_b, src_o]
+    return with_cache(w, kc, vc, bt, bsz)
+
+
+def bitwise_equal(a, b):
+    return a.shape == b.shape and torch.equal(a.view(torch.int64), b.view(torch.int64))
+
+
+# ------------------------------------------------------------------- pins
+
+def pin_golden_attention(lib):
+    for name in ("two_keys_weights", "causal_bottom_right", "gqa_head_map", "paged_walk"):
+        c = golden(name)
+        q, kc, vc, cu, sl, bt, scale = golden_inputs(c)
+        out = oracle.attention(q, kc, vc, cu, sl, bt, scale, lib=lib)
+        exp = torch.tensor(c["expected_out"], dtype=torch.float64)
+        assert torch.allclose(out, exp, rtol=1e-13, atol=1e-13), (name, out, exp)
+
+
+def pin_golden_split(lib):
+    c = golden("split_partials_log2")
+    q, kc, vc, cu, sl, bt, scale = golden_inputs(c)
+    P = c["partition_size"]
+    o, m, l = oracle.attention_partials(q, kc, vc, cu, sl, bt, scale, P, lib=lib)
+    assert torch.allclose(m, torch.tensor(c["expected_m"], dtype=torch.float64), rtol=1e-13, atol=1e-13), m
+    assert torch.allclose(l, torch.tensor(c["expected_l"], dtype=torch.float64), rtol=1e-13, atol=1e-13), l
+    assert torch.allclose(o, torch.tensor(c["expected_o"], dtype=torch.float64), rtol=1e-13, atol=1e-13), o
+    out = oracle.split_reduce(o, m, l, cu, sl, P, lib=lib)
+    assert torch.allclose(out, torch.tensor(c["expected_out"], dtype=torch.float64), rtol=1e-13, atol=1e-13)
+
+
+def pin_golden_cache_write(lib):
+    c = golden("reshape_and_cache_scatter")
+    key = torch.tensor(c["key"], dtype=torch.float32)
+    value = torch.tensor(c["value"], dtype=torch.float32)
+    nb, bs = c["num_blocks"], c["block_size"]
+    kc = torch.zeros((nb, bs) + tuple(key.shape[1:]), dtype=torch.float32)
+    vc = torch.zeros_like(kc)
+    oracle.reshape_and_cache(key, value, kc, vc, torch.tensor(c["slot_mapping"], dtype=torch.int64), lib=lib)
+    assert torch.equal(kc, torch.tensor(c["expected_key_cache"], dtype=torch.float32)), kc
+    assert torch.equal(vc, torch.tensor(c["expected_value_cache"], dtype=torch.float32)), vc
+    g = golden("expand_block_tables_9x16")
+    dst = oracle.expand_block_tables(torch.tensor(g["src"], dtype=torch.int32), g["ratio"], lib=lib)
+    assert torch.equal(dst, torch.tensor(g["expected"], dtype=torch.int32)), dst
+
+
+def pin_dense(lib):
+    for w in micro_cases() + [W.tiny_decode_f32()]:
+        out = run(w, lib)
+        ref_np = dense_numpy(w)
+        ref_t = dense_sdpa(w)
+        assert torch.isfinite(out).all()
+        assert (out - ref_np).abs().max() <= 1e-12, (w.name, (out - ref_np).abs().max())
+        assert (out - ref_t).abs().max() <= 1e-12, (w.name, (out - ref_t).abs().max())
+
+
+def pin_cache_write_vs_index_copy(lib):
+    rng = np.random.default_rng(7)
+    for dt, hkv, d, bs, nb, T in ((torch.bfloat16, 2, 128, 16, 9, 40), (torch.float32, 1, 64, 8, 5, 30)):
+        key = torch.from_numpy(rng.standard_normal((T, hkv, d), dtype=np.float32)).to(dt)
+        value = torch.from_numpy(rng.standard_normal((T, hkv, d), dtype=np.float32)).to(dt)
+        slots = torch.from_numpy(rng.choice(nb * bs, size=T, replace=False).astype(np.int64))
+        slots[rng.choice(T, size=T // 5, replace=False)] = -1
+        # poison: random bit patterns in every slot
+        bits = torch.from_numpy(rng.integers(0, 2 ** 15, size=(nb, bs, hkv, d), dtype=np.int16))
+        if dt == torch.float32:
+            bits = torch.from_numpy(rng.integers(-2 ** 31, 2 ** 31 - 1, size=(nb, bs, hkv, d),
+                                                 dtype=np.int32))
+        kc = bits.clone().view(dt)
+        vc = (bits.clone() ^ 0x55).view(dt)
+        ref_k, ref_v = kc.clone(), vc.clone()
+        valid = slots >= 0
+        ref_k.view(-1, hkv, d).index_copy_(0, slots[valid], key[valid])
+        ref_v.view(-1, hkv, d).index_copy_(0, slots[valid], value[valid])
+        oracle.reshape_and_cache(key, value, kc, vc, slots, lib=lib)
+        iv = torch.int16 if dt == torch.bfloat16 else torch.int32
+        assert torch.equal(kc.view(iv), ref_k.view(iv))
+        assert torch.equal(vc.view(iv), ref_v.view(iv))
+
+
+def pin_page_permutation(lib):
+    for w in micro_cases()[:4]:
+        base = run(w, lib)
+        w2 = relayout(w, w.block_size, seed=11)
+        assert bitwise_equal(base, run(w2, lib)), w.name
+
+
+def pin_page_size(lib):
+    for w in micro_cases()[:4]:
+        base = run(w, lib)
+        for bs in (8, 16, 32):
+            assert bitwise_equal(base, run(relayout(w, bs, seed=bs), lib)), (w.name, bs)
+        # 144-token blocks, then the same bytes seen as nine 16-token pages
+        w144 = relayout(w, 16, seed=5, ratio=9)
+        out144 = run(w144, lib)
+        assert bitwise_equal(base, out144), w.name
+        kbt = oracle.expand_block_tables(w144.block_tables, 9, lib=lib)
+        nb = w144.key_cache.shape[0]
+        kview = w144.key_cache.view(nb * 9, 16, w.num_kv_heads, w.head_dim)
+        vview = w144.value_cache.view(nb * 9, 16, w.num_kv_heads, w.head_dim)
+        assert bitwise_equal(base, run(with_cache(w, kview, vview, kbt, 16), lib)), w.name
+
+
+def pin_split_invariance(lib):
+    for w in micro_cases()[:6] + [W.tiny_decode_f32()]:
+        base = run(w, lib)
+        for P in (8, 16, 32):
+            o, m, l = oracle.attention_partials(w.q, w.key_cache, w.value_cache, w.cu_seqlens_q,
+                                                w.seq_lens, w.block_tables, w.scale, P, lib=lib)
+            out = oracle.split_reduce(o, m, l, w.cu_seqlens_q, w.seq_lens, P, lib=lib)
+            err = ((out - base).abs() / base.abs().clamp_min(1e-3)).max()
+            assert err <= 1e-12, (w.name, P, err)
+
+
+def pin_single_request(lib):
+    import dataclasses
+    for w in micro_cases()[:4]:
+        base = run(w, lib)
+        cu = w.cu_seqlens_q.numpy()
+        for r in range(w.num_seqs):
+            L = int(w.seq_lens[r])
+            n = (L + w.block_size - 1) // w.block_size
+            pos = np.arange(L)
+            src_b = w.block_tables[r].numpy()[pos // w.block_size]
+            kc = torch.full((n, w.block_size, w.num_kv_heads, w.head_dim), float("nan"), dtype=w.dtype)
+            vc = kc.clone()
+            kc.view(-1, w.num_kv_heads, w.head_dim)[:L] = w.key_cache[src_b, pos % w.block_size]
+            vc.view(-1, w.num_kv_heads, w.head_dim)[:L] = w.value_cache[src_b, pos % w.block_size]
+            ql = int(cu[r + 1] - cu[r])
+            wr = dataclasses.replace(
+                w, q=w.q[cu[r]:cu[r + 1]].contiguous(), key_cache=kc, value_cache=vc,
+                cu_seqlens_q=torch.tensor([0, ql], dtype=torch.int32),
+                seq_lens=w.seq_lens[r:r + 1].contiguous(),
+                block_tables=torch.arange(n, dtype=torch.int32)[None], num_blocks=n)
+            assert bitwise_equal(base[cu[r]:cu[r + 1]], run(wr, lib)), (w.name, r)
+
+
+def _single(L, ql, hq, hkv, d, seed, dt=torch.float32, bs=16):
+    return W.build("cf", seed=seed, q_lens=[ql], seq_lens=[L], num_q_heads=hq, num_kv_heads=hkv,
+                   head_dim=d, block_size=bs, num_blocks=(L + bs - 1) // bs + 1, dtype=dt)
+
+
+def pin_closed_forms(lib):
+    import dataclasses
+    # (i) one visible key -> its V row, exactly
+    w = _single(1, 1, 4, 2, 64, 21)
+    out = run(w, lib)
+    K, V = gather_request(w, 0)
+    assert torch.equal(out[0], torch.from_numpy(np.repeat(V[0], 2, axis=0)))
+    # (ii) all keys equal -> uniform mean of the visible V rows (per query)
+    w = _single(30, 3, 2, 1, 64, 22)
+    blk = w.block_tables[0, 0]
+    w.key_cache[w.block_tables[0, :2].long()] = w.key_cache[blk, 0].clone()
+    out = run(w, lib)
+    K, V = gather_request(w, 0)
+    for j in range(3):
+        exp = V[:28 + j, 0].mean(axis=0)
+        assert np.abs(out[j, :, :].numpy() - exp[None]).max() <= 1e-13
+    # (iii) V constant -> that constant
+    w = _single(45, 2, 4, 1, 128, 23)
+    w.value_cache[w.block_tables[0, :3].long()] = 0.375
+    out = run(w, lib)
+    assert (out - 0.375).abs().max() <= 1e-14
+    # (iv) q = 0 -> mean of visible V
+    w = _single(20, 4, 2, 2, 64, 24)
+    w.q.zero_()
+    out = run(w, lib)
+    K, V = gather_request(w, 0)
+    for j in range(4):
+        assert np.abs(out[j].numpy() - V[:17 + j].mean(axis=0)).max() <= 1e-13
+    # (v) a dominant key: huge scale, distinct scores -> V of the argmax key
+    w = _single(33, 1, 2, 1, 64, 25)
+    w = dataclasses.replace(w, scale=1e6)
+    out = run(w, lib)
+    K, V = gather_request(w, 0)
+    qv = w.q.double().numpy()[0]
+    for h in range(2):
+        i = int(np.argmax(K[:, 0] @ qv[h]))
+        assert torch.equal(out[0, h], torch.from_numpy(V[i, 0]))
+    # (vi) GQA == MHA with every KV head repeated for its query heads, exactly
+    w = W.random_case(26, num_seqs=2, max_q=3, max_ctx=30, num_q_heads=8, num_kv_heads=2,
+                      head_dim=64, block_size=16, dtype=torch.bfloat16)
+    rep_k = w.key_cache.repeat_interleave(4, dim=2).contiguous()
+    rep_v = w.value_cache.repeat_interleave(4, dim=2).contiguous()
+    w_mha = dataclasses.replace(w, num_kv_heads=8, key_cache=rep_k, value_cache=rep_v)
+    assert bitwise_equal(run(w, lib), run(w_mha, lib))
+    # (vii) no cached prefix -> standard top-left causal attention
+    w = _single(37, 37, 4, 4, 64, 27)
+    out = run(w, lib)
+    K, V = gather_request(w, 0)
+    ref = F.scaled_dot_product_attention(w.q.double().permute(1, 0, 2), torch.from_numpy(K).permute(1, 0, 2),
+                                         torch.from_numpy(V).permute(1, 0, 2), is_causal=True,
+                                         scale=w.scale).permute(1, 0, 2)
+    assert (out - ref).abs().max() <= 1e-12
+
+
+ALL_PINS = [pin_golden_attention, pin_golden_split, pin_golden_cache_write, pin_dense,
+            pin_cache_write_vs_index_copy, pin_page_permutation, pin_page_size,
+            pin_split_invariance, pin_single_request, pin_closed_forms]
