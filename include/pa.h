@@ -1,0 +1,194 @@
+/*
+ * pa.h -- C ABI of libpa: paged variable-length attention for AMD MI355X (gfx950).
+ *
+ * The operations are those of the vllm-metal pages:
+ *   - reshape_and_cache: scatter projected K/V rows into a paged cache
+ *     (kernel walkthrough, "three Metal kernels");
+ *   - varlen attention: packed queries [total_q, Hq, D] with request
+ *     boundaries in cu_seqlens_q (v0.28.0 release post, "Packed queries and
+ *     paged KV"), keys/values gathered through per-request block tables
+ *     (kernel walkthrough, "What is Paged Attention"), grouped-query heads
+ *     (kernel walkthrough, GQA decode section), causal masking of each
+ *     request's new tokens against its cached prefix;
+ *   - split-KV: long key ranges cut into 256- or 512-token partitions whose
+ *     log2-space (max, exp-sum) statistics and normalised partial outputs are
+ *     merged by a separate reduce (kernel walkthrough, GQA decode tip 4);
+ *   - the block-size view: a large cache block seen as several kernel pages
+ *     with no data moved (unified-memory article, section six).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers unless the parameter says "host".  The
+ *    library never frees, keeps or allocates them; buffers must stay alive
+ *    until the work queued on `stream` has finished.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *    Every call only enqueues work on it and returns without synchronising.
+ *  - Tensors are dense and row-major with the shapes given; no strides.
+ *  - dtype: PA_F32 (IEEE float32) or PA_BF16 (bfloat16, the upper half of a
+ *    float32).  Q, the caches and `out` share one dtype.  Partials are float32.
+ *  - Layouts:
+ *      q, out            [total_q, num_q_heads, head_dim]
+ *      key/value rows    [num_tokens, num_kv_heads, head_dim]
+ *      key/value caches  [num_blocks, block_size, num_kv_heads, head_dim]
+ *      block_tables      int32 [num_seqs, max_blocks_per_seq]; entries past a
+ *                        request's last page are never read (use -1)
+ *      cu_seqlens_q      int32 [num_seqs + 1], cu[0] = 0, cu[num_seqs] = total_q,
+ *                        non-decreasing
+ *      seq_lens          int32 [num_seqs]; keys visible to request r AFTER this
+ *                        step, its own new tokens included: seq_lens[r] >= q_len(r)
+ *      partials          tmp_out float32 [total_q, num_q_heads, max_partitions, head_dim]
+ *                        max_logits, exp_sums float32 [total_q, num_q_heads, max_partitions]
+ *  - Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *  - Causal alignment is bottom-right: query j of request r is at absolute
+ *    position p = seq_lens[r] - q_len(r) + j and sees keys 0..p.
+ *  - Cache slots past seq_lens[r] (page tails, unused pages) are never read
+ *    into a result, whatever they hold (NaN included).
+ *
+ * Errors: every check a host can make is made before anything is enqueued; a
+ * failing call returns a nonzero status and has written nothing.  Device-side
+ * contents (cu_seqlens monotone, seq_len >= q_len, block ids < num_blocks,
+ * slots < num_blocks*block_size, unique slots) are caller contracts and are not
+ * checked.  A HIP launch error returns PA_EHIP.  No C++ exception crosses this
+ * ABI.  There are no fallback paths: an unsupported case returns an error.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { PA_F32 = 0, PA_BF16 = 1 };
+
+enum {
+    PA_OK = 0,
+    PA_EINVAL = 1,        /* null pointer, negative/zero size, inconsistent sizes */
+    PA_EUNSUPPORTED = 2,  /* valid but not implemented: head_dim, block_size, dtype, group size */
+    PA_EWORKSPACE = 3,    /* partials buffers missing or too small for the partition count */
+    PA_EHIP = 4           /* the HIP runtime reported an error while enqueuing */
+};
+
+/* Limits of this build. */
+#define PA_MAX_GROUP 8          /* num_q_heads / num_kv_heads */
+#define PA_MAX_SEQS 65535       /* requests per call */
+#define PA_SPLIT_WG_PER_CU 2    /* workgroups per CU the partition policy aims for */
+
+/*
+ * pa_reshape_and_cache -- write new K/V rows into the paged cache
+ * (kernel walkthrough, "three Metal kernels": reshape_and_cache).
+ *
+ * For every t in [0, num_tokens): s = slot_mapping[t]; if s < 0 the token is
+ * skipped; otherwise key_cache[s / block_size][s % block_size][:][:] = key[t]
+ * and likewise for value.  A bit copy: bytes land unchanged.  Slots must be
+ * unique among the tokens of one call (else which row wins is unspecified).
+ *   key, value        [num_tokens, num_kv_heads, head_dim], dtype
+ *   key/value_cache   [num_blocks, block_size, num_kv_heads, head_dim], dtype
+ *   slot_mapping      int64 [num_tokens]
+ * block_size may be any positive value here (e.g. 144): a slot is the same
+ * memory position in every page-size view of the cache.
+ * Errors: PA_EINVAL (null pointer with num_tokens > 0, sizes <= 0),
+ *         PA_EUNSUPPORTED (dtype; num_kv_heads*head_dim*elt not a multiple of 16 bytes).
+ */
+int pa_reshape_and_cache(const void *key, const void *value, void *key_cache, void *value_cache,
+                         const int64_t *slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t dtype,
+                         void *stream);
+
+/*
+ * pa_expand_block_tables -- kernel-page view of a block table whose cache
+ * blocks hold `ratio` kernel pages each (unified-memory article, section six:
+ * one 144-token block = nine 16-token pages, the cache viewed as
+ * [num_blocks * ratio, block_size / ratio, ...] with no byte moved).
+ *   dst[r][ratio*b + j] = ratio * src[r][b] + j  for b < src_blocks, j < ratio;
+ *   negative src entries map to -1.
+ *   src int32 [num_seqs, src_stride] (first src_blocks columns used),
+ *   dst int32 [num_seqs, dst_stride], dst_stride >= src_blocks * ratio.
+ * Errors: PA_EINVAL.
+ */
+int pa_expand_block_tables(int32_t *dst, const int32_t *src, int32_t num_seqs, int32_t src_stride,
+                           int32_t src_blocks, int32_t dst_stride, int32_t ratio, void *stream);
+
+/*
+ * pa_varlen_attention -- unified paged variable-length attention.
+ *
+ * out[t][h][:] = sum_i softmax_i(scale * q[t][h] . k_i) v_i over the keys
+ * i = 0..p of t's request, read through block_tables (see the conventions
+ * above).  One call serves decode tokens, verify windows and prefill chunks
+ * of any mix of requests.
+ *
+ * partition_size = 0: no split; `out` receives every row.
+ * partition_size = P in {256, 512}: the keys of a row at position p are cut
+ *   into n = ceil((p + 1) / P) partitions [kP, min((k+1)P, p+1)).
+ *   Rows with n == 1 are written straight to `out`.  For rows with n >= 2,
+ *   partition k < n writes
+ *     max_logits[t][h][k] = max_i s_i,  s_i = scale * log2(e) * q.k_i
+ *     exp_sums[t][h][k]   = sum_i 2^(s_i - max_logits)
+ *     tmp_out[t][h][k][:] = sum_i 2^(s_i - max_logits) v_i / exp_sums
+ *   and pa_split_kv_reduce must then be called to produce those rows of `out`.
+ *   Entries for k >= n are not written.
+ *   max_partitions >= ceil(max_seq_len / P) is the capacity of the partials.
+ *
+ * Host scalars: max_q_len = max over requests of q_len (>= 1 unless
+ * total_q == 0), max_seq_len = max of seq_lens; both must be upper bounds.
+ * Supported: dtype PA_F32 / PA_BF16; head_dim 64, 128, 256; block_size 8, 16,
+ * 32; num_q_heads % num_kv_heads == 0 with group size <= PA_MAX_GROUP.
+ * Errors: PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE (P > 0 and a partial
+ * buffer is NULL or max_partitions too small), PA_EHIP.
+ */
+int pa_varlen_attention(void *out, const void *q, const void *key_cache, const void *value_cache,
+                        const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                        const int32_t *block_tables, int32_t num_seqs, int32_t total_q,
+                        int32_t max_q_len, int32_t max_seq_len, int32_t max_blocks_per_seq,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t num_blocks, int32_t block_size, float scale, int32_t dtype,
+                        int32_t partition_size, float *tmp_out, float *max_logits,
+                        float *exp_sums, int32_t max_partitions, void *stream);
+
+/*
+ * pa_split_kv_reduce -- merge split-KV partials (kernel walkthrough, GQA decode
+ * tip 4: the shared reducer).  For every row (t, h) with n >= 2 partitions
+ * (n as above): M = max_k max_logits[k], w_k = exp_sums[k] * 2^(max_logits[k] - M),
+ * out[t][h][:] = sum_k w_k tmp_out[k][:] / sum_k w_k, cast to dtype with
+ * round-to-nearest-even.  Rows with n == 1 are left untouched.
+ * Arguments mean what they mean in pa_varlen_attention.
+ * Errors: PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP.
+ */
+int pa_split_kv_reduce(void *out, const float *tmp_out, const float *max_logits,
+                       const float *exp_sums, const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                       int32_t num_seqs, int32_t total_q, int32_t num_q_heads, int32_t head_dim,
+                       int32_t partition_size, int32_t max_partitions, int32_t dtype, void *stream);
+
+/*
+ * pa_pick_partition_size -- host-only partition policy for decode batches
+ * (kernel walkthrough, "dispatch layer": a work budget proportional to the
+ * number of GPU cores, 512-token partitions tried first, then 256, and only
+ * full partitions counted toward the budget).  With
+ *   budget = PA_SPLIT_WG_PER_CU * num_cus,
+ *   unsplit = num_kv_heads * num_seqs   (workgroups without a split),
+ *   W(P)    = num_kv_heads * sum_r floor(seq_lens[r] / P):
+ * returns 0 if no sequence is longer than 256 or unsplit >= 2 * budget,
+ * else 512 if W(512) >= budget, else 256.
+ * host_seq_lens is a HOST array.  num_cus <= 0 asks the current device.
+ * Returns -1 on bad arguments.  Enqueues nothing.
+ */
+int32_t pa_pick_partition_size(const int32_t *host_seq_lens, int32_t num_seqs,
+                               int32_t num_kv_heads, int32_t num_cus);
+
+/* Bytes needed for the partials of a split call (tmp_out; max_logits and
+ * exp_sums each).  Returns PA_EINVAL on bad sizes. */
+int pa_partials_bytes(int32_t total_q, int32_t num_q_heads, int32_t head_dim,
+                      int32_t max_partitions, size_t *tmp_out_bytes, size_t *stats_bytes);
+
+/* Static text for a status code. */
+const char *pa_status_string(int status);
+
+/* Version of this ABI (major * 100 + minor). */
+int pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,211 @@
+"""paged_varlen_attention_amd -- paged variable-length attention on AMD MI355X.
+
+A thin ctypes binding over ``libpa.so`` (C ABI in ``include/pa.h``).  This
+layer only checks tensors and marshals pointers: every step of the path runs
+in the HIP kernels of the library.  PyTorch supplies device memory and the
+current HIP stream.  If the library is missing, importing this package fails
+loudly; there is no CPU fallback.
+
+Entry points (same names as the C ABI, without the ``pa_`` prefix):
+``reshape_and_cache``, ``expand_block_tables``, ``varlen_attention``,
+``split_kv_reduce``, plus ``pick_partition_size`` and ``alloc_partials``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_F32, PA_BF16 = 0, 1
+PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP = 0, 1, 2, 3, 4
+
+
+class PAError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m paged_varlen_attention_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    lib.pa_reshape_and_cache.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
+    lib.pa_expand_block_tables.argtypes = [P, P, I, I, I, I, I, P]
+    lib.pa_varlen_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I,
+                                        I, P, P, P, I, P]
+    lib.pa_split_kv_reduce.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+    lib.pa_pick_partition_size.argtypes = [P, I, I, I]
+    lib.pa_pick_partition_size.restype = ctypes.c_int32
+    lib.pa_partials_bytes.argtypes = [I, I, I, I, ctypes.POINTER(ctypes.c_size_t),
+                                      ctypes.POINTER(ctypes.c_size_t)]
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    for f in ("pa_reshape_and_cache", "pa_expand_block_tables", "pa_varlen_attention",
+              "pa_split_kv_reduce", "pa_partials_bytes", "pa_abi_version"):
+        getattr(lib, f).restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != PA_OK:
+        raise PAError(fn, status, lib.pa_status_string(status).decode())
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return PA_F32
+    if dt == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported dtype {dt}; use float32 or bfloat16")
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None, device=None) -> ctypes.c_void_p:
+    """Pointer of a dense device tensor (non-contiguous or negative strides refused)."""
+    if t is None:
+        return ctypes.c_void_p(0)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (no strides, no negative strides)")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class Partials(NamedTuple):
+    tmp_out: torch.Tensor     # float32 [total_q, Hq, max_parts, D]
+    max_logits: torch.Tensor  # float32 [total_q, Hq, max_parts]
+    exp_sums: torch.Tensor    # float32 [total_q, Hq, max_parts]
+
+    @property
+    def max_parts(self) -> int:
+        return int(self.max_logits.shape[2])
+
+
+def max_partitions(max_seq_len: int, partition_size: int) -> int:
+    return max(1, (max_seq_len + partition_size - 1) // partition_size) if partition_size else 0
+
+
+def alloc_partials(total_q: int, num_q_heads: int, head_dim: int, max_parts: int,
+                   device) -> Partials:
+    return Partials(
+        torch.empty((total_q, num_q_heads, max_parts, head_dim), dtype=torch.float32, device=device),
+        torch.empty((total_q, num_q_heads, max_parts), dtype=torch.float32, device=device),
+        torch.empty((total_q, num_q_heads, max_parts), dtype=torch.float32, device=device))
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                      value_cache: torch.Tensor, slot_mapping: torch.Tensor) -> None:
+    """key/value [T, Hkv, D]; caches [num_blocks, block_size, Hkv, D]; slot_mapping int64 [T]."""
+    T, hkv, d = key.shape
+    nb, bs, chkv, cd = key_cache.shape
+    if (chkv, cd) != (hkv, d) or value.shape != key.shape or value_cache.shape != key_cache.shape:
+        raise ValueError("reshape_and_cache: shape mismatch")
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    dev = key.device
+    st = lib.pa_reshape_and_cache(
+        _dev(key, "key", device=dev), _dev(value, "value", key.dtype, dev),
+        _dev(key_cache, "key_cache", key.dtype, dev), _dev(value_cache, "value_cache", key.dtype, dev),
+        _dev(slot_mapping, "slot_mapping", torch.int64, dev), T, hkv, d, nb, bs,
+        _dtype_code(key.dtype), _stream(dev))
+    _check("pa_reshape_and_cache", st)
+
+
+def expand_block_tables(block_tables: torch.Tensor, ratio: int,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Kernel-page view of a block table of ``ratio``-page blocks (int32 on the GPU)."""
+    B, nb = block_tables.shape
+    if out is None:
+        out = torch.empty((B, nb * ratio), dtype=torch.int32, device=block_tables.device)
+    st = lib.pa_expand_block_tables(_dev(out, "out", torch.int32),
+                                    _dev(block_tables, "block_tables", torch.int32), B, nb, nb,
+                                    out.shape[1], ratio, _stream(block_tables.device))
+    _check("pa_expand_block_tables", st)
+    return out
+
+
+def varlen_attention(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                     cu_seqlens_q: torch.Tensor, seq_lens: torch.Tensor, block_tables: torch.Tensor,
+                     *, max_q_len: int, max_seq_len: int, scale: float, partition_size: int = 0,
+                     out: Optional[torch.Tensor] = None, partials: Optional[Partials] = None,
+                     reduce: bool = True) -> torch.Tensor:
+    """Paged varlen attention; with partition_size > 0 and reduce=True the split
+    partials are merged by pa_split_kv_reduce on the same stream."""
+    TQ, hq, d = q.shape
+    nb, bs, hkv, cd = key_cache.shape
+    if cd != d or value_cache.shape != key_cache.shape:
+        raise ValueError("cache shape mismatch")
+    B = seq_lens.shape[0]
+    if cu_seqlens_q.shape != (B + 1,) or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("metadata shape mismatch")
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if partition_size and partials is None:
+        partials = alloc_partials(TQ, hq, d, max_partitions(max_seq_len, partition_size), dev)
+    tmp = ml = es = None
+    mp = 0
+    if partials is not None and partition_size:
+        tmp, ml, es = partials
+        mp = partials.max_parts
+    s = _stream(dev)
+    st = lib.pa_varlen_attention(
+        _dev(out, "out", q.dtype, dev), _dev(q, "q", device=dev),
+        _dev(key_cache, "key_cache", q.dtype, dev), _dev(value_cache, "value_cache", q.dtype, dev),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev), _dev(seq_lens, "seq_lens", torch.int32, dev),
+        _dev(block_tables, "block_tables", torch.int32, dev), B, TQ, int(max_q_len),
+        int(max_seq_len), block_tables.shape[1], hq, hkv, d, nb, bs, float(scale),
+        _dtype_code(q.dtype), int(partition_size), _dev(tmp, "tmp_out", torch.float32, dev),
+        _dev(ml, "max_logits", torch.float32, dev), _dev(es, "exp_sums", torch.float32, dev), mp, s)
+    _check("pa_varlen_attention", st)
+    if partition_size and reduce:
+        split_kv_reduce(out, partials, cu_seqlens_q, seq_lens, partition_size)
+    return out
+
+
+def split_kv_reduce(out: torch.Tensor, partials: Partials, cu_seqlens_q: torch.Tensor,
+                    seq_lens: torch.Tensor, partition_size: int) -> torch.Tensor:
+    TQ, hq, d = out.shape
+    dev = out.device
+    tmp, ml, es = partials
+    if tmp.shape[:2] != (TQ, hq) or tmp.shape[3] != d:
+        raise ValueError("partials shape mismatch")
+    st = lib.pa_split_kv_reduce(
+        _dev(out, "out", device=dev), _dev(tmp, "tmp_out", torch.float32, dev),
+        _dev(ml, "max_logits", torch.float32, dev), _dev(es, "exp_sums", torch.float32, dev),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev), _dev(seq_lens, "seq_lens", torch.int32, dev),
+        seq_lens.shape[0], TQ, hq, d, int(partition_size), partials.max_parts,
+        _dtype_code(out.dtype), _stream(dev))
+    _check("pa_split_kv_reduce", st)
+    return out
+
+
+def pick_partition_size(seq_lens: Sequence[int], num_kv_heads: int, num_cus: int = 0) -> int:
+    """Host-side partition policy (0, 256 or 512); seq_lens is a host sequence."""
+    arr = (ctypes.c_int32 * len(seq_lens))(*[int(s) for s in seq_lens])
+    r = lib.pa_pick_partition_size(ctypes.cast(arr, ctypes.c_void_p), len(seq_lens), num_kv_heads,
+                                   num_cus)
+    if r < 0:
+        raise ValueError("pick_partition_size: bad arguments")
+    return int(r)

@@ -1,0 +1,255 @@
+// pa_api.cpp -- the extern "C" entry points of libpa: argument validation,
+// routing and launch.  Every check that the host can make happens here, before
+// anything is enqueued, so a failing call has no side effects.  No exception
+// crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <mutex>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elt_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_BF16 ? 2 : 0); }
+
+int log2_exact(int32_t v) {
+    int l = 0;
+    while ((1 << l) < v) ++l;
+    return (1 << l) == v ? l : -1;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_EHIP; }
+
+// Grid dimensions y and z are limited to 65535 workgroups.
+constexpr int32_t GRID_YZ_MAX = 65535;
+
+int check_partitions(int32_t partition_size, int32_t max_seq_len, const float *tmp_out,
+                     const float *max_logits, const float *exp_sums, int32_t max_partitions) {
+    if (partition_size == 0) return PA_OK;
+    if (partition_size != 256 && partition_size != 512) return PA_EUNSUPPORTED;
+    if (!tmp_out || !max_logits || !exp_sums) return PA_EWORKSPACE;
+    if (!aligned16(tmp_out)) return PA_EINVAL;
+    const int64_t need = ((int64_t)max_seq_len + partition_size - 1) / partition_size;
+    if (max_partitions < need || max_partitions <= 0) return PA_EWORKSPACE;
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_abi_version(void) { return 100; }
+
+const char *pa_status_string(int status) {
+    switch (status) {
+        case PA_OK: return "ok";
+        case PA_EINVAL: return "invalid argument";
+        case PA_EUNSUPPORTED: return "unsupported configuration";
+        case PA_EWORKSPACE: return "split-KV partial buffers missing or too small";
+        case PA_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int pa_partials_bytes(int32_t total_q, int32_t num_q_heads, int32_t head_dim,
+                      int32_t max_partitions, size_t *tmp_out_bytes, size_t *stats_bytes) {
+    if (total_q < 0 || num_q_heads <= 0 || head_dim <= 0 || max_partitions <= 0 ||
+        !tmp_out_bytes || !stats_bytes)
+        return PA_EINVAL;
+    const size_t rows = (size_t)total_q * num_q_heads * max_partitions;
+    *tmp_out_bytes = rows * head_dim * sizeof(float);
+    *stats_bytes = rows * sizeof(float);
+    return PA_OK;
+}
+
+int pa_reshape_and_cache(const void *key, const void *value, void *key_cache, void *value_cache,
+                         const int64_t *slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t dtype,
+                         void *stream) {
+    try {
+        const int eb = elt_bytes(dtype);
+        if (!eb) return PA_EUNSUPPORTED;
+        if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 ||
+            block_size <= 0)
+            return PA_EINVAL;
+        if (num_tokens == 0) return PA_OK;
+        if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PA_EINVAL;
+        const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * eb;
+        if (row_bytes % 16 != 0 || row_bytes > (1 << 30)) return PA_EUNSUPPORTED;
+        if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) ||
+            !aligned16(value_cache))
+            return PA_EINVAL;
+        return hip_status(pa::launch_reshape_and_cache(
+            key, value, key_cache, value_cache, slot_mapping, num_tokens, (int32_t)row_bytes,
+            (int64_t)num_blocks * block_size, (hipStream_t)stream));
+    } catch (...) {
+        return PA_EHIP;
+    }
+}
+
+int pa_expand_block_tables(int32_t *dst, const int32_t *src, int32_t num_seqs, int32_t src_stride,
+                           int32_t src_blocks, int32_t dst_stride, int32_t ratio, void *stream) {
+    try {
+        if (num_seqs < 0 || src_blocks < 0 || ratio <= 0 || src_stride < src_blocks ||
+            (int64_t)dst_stride < (int64_t)src_blocks * ratio || num_seqs > GRID_YZ_MAX)
+            return PA_EINVAL;
+        if (num_seqs == 0 || src_blocks == 0) return PA_OK;
+        if (!dst || !src) return PA_EINVAL;
+        return hip_status(pa::launch_expand_block_tables(dst, src, num_seqs, src_stride,
+                                                         src_blocks, dst_stride, ratio,
+                                                         (hipStream_t)stream));
+    } catch (...) {
+        return PA_EHIP;
+    }
+}
+
+int pa_varlen_attention(void *out, const void *q, const void *key_cache, const void *value_cache,
+                        const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                        const int32_t *block_tables, int32_t num_seqs, int32_t total_q,
+                        int32_t max_q_len, int32_t max_seq_len, int32_t max_blocks_per_seq,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t num_blocks, int32_t block_size, float scale, int32_t dtype,
+                        int32_t partition_size, float *tmp_out, float *max_logits,
+                        float *exp_sums, int32_t max_partitions, void *stream) {
+    try {
+        if (!elt_bytes(dtype)) return PA_EUNSUPPORTED;
+        if (num_seqs < 0 || total_q < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+            num_blocks <= 0 || block_size <= 0 || head_dim <= 0 || max_blocks_per_seq < 0)
+            return PA_EINVAL;
+        if (num_q_heads % num_kv_heads != 0) return PA_EINVAL;
+        if (!std::isfinite(scale)) return PA_EINVAL;
+        const int32_t group = num_q_heads / num_kv_heads;
+        if (group > PA_MAX_GROUP) return PA_EUNSUPPORTED;
+        if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PA_EUNSUPPORTED;
+        const int lbs = log2_exact(block_size);
+        if (block_size < 8 || block_size > 32 || lbs < 0) return PA_EUNSUPPORTED;
+        if (partition_size != 0 && partition_size != 256 && partition_size != 512)
+            return PA_EUNSUPPORTED;
+        if (total_q == 0 || num_seqs == 0) return PA_OK;
+        if (num_seqs > GRID_YZ_MAX || num_kv_heads > GRID_YZ_MAX) return PA_EUNSUPPORTED;
+        if (max_q_len < 1 || max_seq_len < max_q_len) return PA_EINVAL;
+        if ((int64_t)max_blocks_per_seq * block_size < max_seq_len) return PA_EINVAL;
+        if (!out || !q || !key_cache || !value_cache || !cu_seqlens_q || !seq_lens ||
+            !block_tables)
+            return PA_EINVAL;
+        if (!aligned16(out) || !aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache))
+            return PA_EINVAL;
+        const int st = check_partitions(partition_size, max_seq_len, tmp_out, max_logits,
+                                        exp_sums, max_partitions);
+        if (st != PA_OK) return st;
+
+        pa::AttnParams p{};
+        p.out = out;
+        p.q = q;
+        p.kc = key_cache;
+        p.vc = value_cache;
+        p.cu_q = cu_seqlens_q;
+        p.seq_lens = seq_lens;
+        p.bt = block_tables;
+        p.tmp_out = tmp_out;
+        p.max_logits = max_logits;
+        p.exp_sums = exp_sums;
+        p.num_seqs = num_seqs;
+        p.total_q = total_q;
+        p.max_q_len = max_q_len;
+        p.max_seq_len = max_seq_len;
+        p.bt_stride = max_blocks_per_seq;
+        p.hq = num_q_heads;
+        p.hkv = num_kv_heads;
+        p.group = group;
+        p.head_dim = head_dim;
+        p.num_blocks = num_blocks;
+        p.block_size = block_size;
+        p.log2_bs = lbs;
+        p.partition = partition_size;
+        p.max_parts = partition_size ? max_partitions : 1;
+        p.scale_log2 = scale * 1.44269504088896340736f;
+        p.dtype = dtype;
+
+        if (max_q_len == 1) {
+            if (!pa::decode_supported(dtype, head_dim, group)) return PA_EUNSUPPORTED;
+            const int64_t parts =
+                partition_size ? ((int64_t)max_seq_len + partition_size - 1) / partition_size : 1;
+            if (parts > 0x7fffffff) return PA_EUNSUPPORTED;
+            return hip_status(pa::launch_decode(p, (hipStream_t)stream));
+        }
+        if (!pa::prefill_supported(dtype, head_dim, group)) return PA_EUNSUPPORTED;
+        return hip_status(pa::launch_prefill(p, (hipStream_t)stream));
+    } catch (...) {
+        return PA_EHIP;
+    }
+}
+
+int pa_split_kv_reduce(void *out, const float *tmp_out, const float *max_logits,
+                       const float *exp_sums, const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                       int32_t num_seqs, int32_t total_q, int32_t num_q_heads, int32_t head_dim,
+                       int32_t partition_size, int32_t max_partitions, int32_t dtype,
+                       void *stream) {
+    try {
+        if (!elt_bytes(dtype)) return PA_EUNSUPPORTED;
+        if (num_seqs < 0 || total_q < 0 || num_q_heads <= 0 || head_dim <= 0) return PA_EINVAL;
+        if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PA_EUNSUPPORTED;
+        if (partition_size != 256 && partition_size != 512) return PA_EUNSUPPORTED;
+        if (total_q == 0 || num_seqs == 0) return PA_OK;
+        if (num_q_heads > GRID_YZ_MAX) return PA_EUNSUPPORTED;
+        if (!out || !cu_seqlens_q || !seq_lens) return PA_EINVAL;
+        if (!tmp_out || !max_logits || !exp_sums || max_partitions <= 0) return PA_EWORKSPACE;
+        if (!aligned16(out) || !aligned16(tmp_out)) return PA_EINVAL;
+        pa::ReduceParams p{};
+        p.out = out;
+        p.tmp_out = tmp_out;
+        p.max_logits = max_logits;
+        p.exp_sums = exp_sums;
+        p.cu_q = cu_seqlens_q;
+        p.seq_lens = seq_lens;
+        p.num_seqs = num_seqs;
+        p.total_q = total_q;
+        p.hq = num_q_heads;
+        p.head_dim = head_dim;
+        p.partition = partition_size;
+        p.max_parts = max_partitions;
+        p.dtype = dtype;
+        return hip_status(pa::launch_reduce(p, (hipStream_t)stream));
+    } catch (...) {
+        return PA_EHIP;
+    }
+}
+
+int32_t pa_pick_partition_size(const int32_t *host_seq_lens, int32_t num_seqs,
+                               int32_t num_kv_heads, int32_t num_cus) {
+    try {
+        if (num_seqs < 0 || num_kv_heads <= 0 || (num_seqs > 0 && !host_seq_lens)) return -1;
+        if (num_cus <= 0) {
+            int dev = 0;
+            if (hipGetDevice(&dev) != hipSuccess) return -1;
+            if (hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                hipSuccess)
+                return -1;
+        }
+        int64_t full512 = 0, full256 = 0;
+        int32_t max_len = 0;
+        for (int32_t r = 0; r < num_seqs; ++r) {
+            const int32_t s = host_seq_lens[r];
+            if (s < 0) return -1;
+            full512 += s / 512;
+            full256 += s / 256;
+            max_len = s > max_len ? s : max_len;
+        }
+        // Workgroups an unsplit launch already has, and the work budget.
+        const int64_t unsplit = (int64_t)num_kv_heads * num_seqs;
+        const int64_t budget = (int64_t)PA_SPLIT_WG_PER_CU * num_cus;
+        if (max_len <= 256 || unsplit >= 2 * budget) return 0;
+        if ((int64_t)num_kv_heads * full512 >= budget) return 512;
+        return 256;
+    } catch (...) {
+        return -1;
+    }
+}
+
+}  // extern "C"

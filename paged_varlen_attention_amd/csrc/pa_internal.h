@@ -1,0 +1,75 @@
+// pa_internal.h -- launch parameters and launcher entry points shared by the
+// C-ABI layer (pa_api.cpp) and the HIP kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Kernel page geometry.  Decode stages K/V through LDS in chunks of CHUNK
+// tokens whatever the cache page size is (8, 16 or 32 tokens).
+constexpr int CHUNK = 16;
+
+struct AttnParams {
+    void *out;
+    const void *q;
+    const void *kc;
+    const void *vc;
+    const int32_t *cu_q;
+    const int32_t *seq_lens;
+    const int32_t *bt;
+    float *tmp_out;
+    float *max_logits;
+    float *exp_sums;
+    int32_t num_seqs;
+    int32_t total_q;
+    int32_t max_q_len;
+    int32_t max_seq_len;
+    int32_t bt_stride;
+    int32_t hq;
+    int32_t hkv;
+    int32_t group;          // hq / hkv
+    int32_t head_dim;
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t log2_bs;
+    int32_t partition;      // 0 = no split
+    int32_t max_parts;
+    float scale_log2;       // scale * log2(e)
+    int32_t dtype;
+};
+
+struct ReduceParams {
+    void *out;
+    const float *tmp_out;
+    const float *max_logits;
+    const float *exp_sums;
+    const int32_t *cu_q;
+    const int32_t *seq_lens;
+    int32_t num_seqs;
+    int32_t total_q;
+    int32_t hq;
+    int32_t head_dim;
+    int32_t partition;
+    int32_t max_parts;
+    int32_t dtype;
+};
+
+// Each launcher returns hipSuccess or the error of the launch; it assumes the
+// caller validated every host-visible argument.
+hipError_t launch_reshape_and_cache(const void *key, const void *value, void *kc, void *vc,
+                                    const int64_t *slots, int32_t num_tokens, int32_t row_bytes,
+                                    int64_t num_slots, hipStream_t stream);
+hipError_t launch_expand_block_tables(int32_t *dst, const int32_t *src, int32_t num_seqs,
+                                      int32_t src_stride, int32_t src_blocks, int32_t dst_stride,
+                                      int32_t ratio, hipStream_t stream);
+hipError_t launch_decode(const AttnParams &p, hipStream_t stream);
+hipError_t launch_prefill(const AttnParams &p, hipStream_t stream);
+hipError_t launch_reduce(const ReduceParams &p, hipStream_t stream);
+
+// Whether a decode instantiation exists for this geometry.
+bool decode_supported(int dtype, int head_dim, int group);
+bool prefill_supported(int dtype, int head_dim, int group);
+
+}  // namespace pa

@@ -1,0 +1,128 @@
+// reduce.hip -- merge of split-KV partials (vllm-metal kernel walkthrough, GQA
+// decode tip 4: per-partition log2-space (max, exp-sum) statistics plus the
+// normalised partial output, merged by one shared reducer).
+//
+// One workgroup per (query token, query head).  With n partitions for the
+// token's position p (n = ceil((p+1)/P)): M = max_k m_k, w_k = l_k 2^(m_k - M),
+// out = sum_k w_k o_k / sum_k w_k.  Rows with n == 1 were finalised by the
+// attention kernel and are skipped.  Partitions are spread over lane groups of
+// the workgroup (float4 per lane along D) and combined in a fixed order, so
+// the result is deterministic.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int RT = 256;      // threads per workgroup
+constexpr int WCAP = 2048;   // partition weights kept in LDS
+
+template <typename T, int D>
+__global__ __launch_bounds__(RT) void reduce_kernel(const ReduceParams p) {
+    constexpr int LPG = D / 4;      // lanes per partition group (float4 each)
+    constexpr int KG = RT / LPG;    // partition groups
+    __shared__ float wsh[WCAP];
+    __shared__ float red[RT / 64];
+    __shared__ float4 part_acc[KG][LPG];
+
+    const int t = blockIdx.x;
+    const int h = blockIdx.y;
+    const int tid = threadIdx.x;
+
+    // owner request of token t: the r with cu[r] <= t < cu[r+1]
+    int lo = 0, hi = p.num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.cu_q[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int r = lo;
+    const int q_len = p.cu_q[r + 1] - p.cu_q[r];
+    const int pos = p.seq_lens[r] - q_len + (t - p.cu_q[r]);
+    const int n = pos / p.partition + 1;
+    if (n <= 1 || n > p.max_parts || pos < 0) return;
+
+    const size_t srow = ((size_t)t * p.hq + h) * p.max_parts;
+    const float *ml = p.max_logits + srow;
+    const float *es = p.exp_sums + srow;
+
+    // M = max_k m_k
+    float mx = NEG_INF;
+    for (int k = tid; k < n; k += RT) mx = fmaxf(mx, ml[k]);
+    mx = group_max<64>(mx);
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    float M = red[0];
+#pragma unroll
+    for (int w = 1; w < RT / 64; ++w) M = fmaxf(M, red[w]);
+    __syncthreads();
+
+    // w_k and their sum
+    float ws = 0.f;
+    for (int k = tid; k < n; k += RT) {
+        const float w = es[k] * exp2_diff(ml[k], M);
+        if (k < WCAP) wsh[k] = w;
+        ws += w;
+    }
+    ws = group_sum<64>(ws);
+    if ((tid & 63) == 0) red[tid >> 6] = ws;
+    __syncthreads();
+    float W = 0.f;
+#pragma unroll
+    for (int w = 0; w < RT / 64; ++w) W += red[w];
+
+    // sum_k w_k o_k
+    const int kg = tid / LPG;
+    const int d4 = tid % LPG;
+    const float4 *o = reinterpret_cast<const float4 *>(p.tmp_out + srow * D) + d4;
+    float4 a = {0.f, 0.f, 0.f, 0.f};
+    for (int k = kg; k < n; k += KG) {
+        const float w = k < WCAP ? wsh[k] : es[k] * exp2_diff(ml[k], M);
+        const float4 v = o[(size_t)k * LPG];
+        a.x = fmaf(w, v.x, a.x);
+        a.y = fmaf(w, v.y, a.y);
+        a.z = fmaf(w, v.z, a.z);
+        a.w = fmaf(w, v.w, a.w);
+    }
+    part_acc[kg][d4] = a;
+    __syncthreads();
+    if (tid < LPG) {
+        float4 s = part_acc[0][tid];
+#pragma unroll
+        for (int g = 1; g < KG; ++g) {
+            const float4 v = part_acc[g][tid];
+            s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+        }
+        const float inv = 1.f / W;
+        const size_t oi = ((size_t)t * p.hq + h) * D + tid * 4;
+        if constexpr (sizeof(T) == 2) {
+            uint2 pk;
+            pk.x = pack_bf16(s.x * inv, s.y * inv);
+            pk.y = pack_bf16(s.z * inv, s.w * inv);
+            *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.out) + oi) = pk;
+        } else {
+            float4 v = {s.x * inv, s.y * inv, s.z * inv, s.w * inv};
+            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.out) + oi) = v;
+        }
+    }
+}
+
+template <typename T>
+hipError_t launch_t(const ReduceParams &p, hipStream_t stream) {
+    dim3 grid(p.total_q, p.hq);
+    switch (p.head_dim) {
+        case 64: hipLaunchKernelGGL((reduce_kernel<T, 64>), grid, dim3(RT), 0, stream, p); break;
+        case 128: hipLaunchKernelGGL((reduce_kernel<T, 128>), grid, dim3(RT), 0, stream, p); break;
+        case 256: hipLaunchKernelGGL((reduce_kernel<T, 256>), grid, dim3(RT), 0, stream, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const ReduceParams &p, hipStream_t stream) {
+    if (p.total_q == 0) return hipSuccess;
+    return p.dtype == 1 ? launch_t<bf16_t>(p, stream) : launch_t<float>(p, stream);
+}
+
+}  // namespace pa

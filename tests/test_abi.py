@@ -1,0 +1,146 @@
+"""CPU tests of the C ABI: the library loads, exports every function that
+include/pa.h declares, and rejects bad arguments with the documented status
+before anything is enqueued.  Every call below carries at least one invalid
+argument, so none of them reaches a kernel launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+def _lib():
+    import paged_varlen_attention_amd as pa
+    return pa.lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ("pa_reshape_and_cache", "pa_varlen_attention", "pa_split_kv_reduce",
+              "pa_expand_block_tables", "pa_pick_partition_size", "pa_status_string"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol():
+    import paged_varlen_attention_amd as pa
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (pa_\w+)", out))
+    missing = [f for f in declared_functions() if f not in exported]
+    assert not missing, missing
+    for f in declared_functions():
+        getattr(pa.lib, f)  # resolvable through ctypes
+
+
+def test_status_strings_and_version():
+    lib = _lib()
+    for s in range(5):
+        assert lib.pa_status_string(s)
+    assert lib.pa_abi_version() == 100
+
+
+FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: every call below is rejected
+
+
+def attn_args(**over):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, cu=FAKE, sl=FAKE, bt=FAKE, num_seqs=2,
+             total_q=2, max_q_len=1, max_seq_len=50, max_blocks=4, hq=4, hkv=1, d=64, nb=8,
+             bs=16, scale=0.125, dtype=0, P=0, tmp=None, ml=None, es=None, mp=0, stream=None)
+    a.update(over)
+    return [a[k] for k in ("out", "q", "kc", "vc", "cu", "sl", "bt", "num_seqs", "total_q",
+                           "max_q_len", "max_seq_len", "max_blocks", "hq", "hkv", "d", "nb", "bs",
+                           "scale", "dtype", "P", "tmp", "ml", "es", "mp", "stream")]
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=7), 2), (dict(d=96), 2), (dict(bs=12), 2), (dict(bs=64), 2),
+    (dict(hq=5, hkv=2), 1), (dict(hq=32, hkv=2), 2), (dict(P=128), 2), (dict(num_seqs=-1), 1),
+    (dict(hq=0), 1), (dict(nb=0), 1), (dict(out=None), 1), (dict(q=None), 1), (dict(bt=None), 1),
+    (dict(cu=None), 1), (dict(max_q_len=0), 1), (dict(max_seq_len=0), 1),
+    (dict(max_blocks=3), 1), (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1),
+    (dict(q=ctypes.c_void_p(0x100004)), 1), (dict(kc=ctypes.c_void_p(0x100008)), 1),
+    (dict(P=512), 3), (dict(P=256, tmp=FAKE, ml=FAKE, es=FAKE, mp=0), 3),
+    (dict(P=256, max_seq_len=600, max_blocks=40, tmp=FAKE, ml=FAKE, es=FAKE, mp=2), 3),
+    (dict(P=256, tmp=FAKE, ml=None, es=FAKE, mp=4), 3),
+    (dict(num_seqs=70000), 2),
+])
+def test_varlen_attention_rejects(over, status):
+    assert _lib().pa_varlen_attention(*attn_args(**over)) == status
+
+
+def test_varlen_attention_empty_batch_is_ok_without_pointers():
+    args = attn_args(total_q=0, out=None, q=None)
+    assert _lib().pa_varlen_attention(*args) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=3), 2), (dict(T=-1), 1), (dict(hkv=0), 1), (dict(key=None), 1),
+    (dict(slots=None), 1), (dict(d=3), 2), (dict(bs=0), 1), (dict(nb=0), 1),
+    (dict(kc=ctypes.c_void_p(0x100002)), 1),
+])
+def test_reshape_and_cache_rejects(over, status):
+    a = dict(key=FAKE, value=FAKE, kc=FAKE, vc=FAKE, slots=FAKE, T=4, hkv=1, d=64, nb=2, bs=16,
+             dtype=1, stream=None)
+    a.update(over)
+    args = [a[k] for k in ("key", "value", "kc", "vc", "slots", "T", "hkv", "d", "nb", "bs",
+                           "dtype", "stream")]
+    assert _lib().pa_reshape_and_cache(*args) == status
+
+
+def test_reshape_and_cache_zero_tokens_ok():
+    assert _lib().pa_reshape_and_cache(None, None, None, None, None, 0, 1, 64, 2, 16, 1, None) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=9), 2), (dict(d=48), 2), (dict(P=0), 2), (dict(P=300), 2), (dict(out=None), 1),
+    (dict(tmp=None), 3), (dict(mp=0), 3), (dict(hq=0), 1), (dict(out=ctypes.c_void_p(0x100006)), 1),
+])
+def test_split_kv_reduce_rejects(over, status):
+    a = dict(out=FAKE, tmp=FAKE, ml=FAKE, es=FAKE, cu=FAKE, sl=FAKE, B=2, TQ=2, hq=4, d=64, P=256,
+             mp=2, dtype=1, stream=None)
+    a.update(over)
+    args = [a[k] for k in ("out", "tmp", "ml", "es", "cu", "sl", "B", "TQ", "hq", "d", "P", "mp",
+                           "dtype", "stream")]
+    assert _lib().pa_split_kv_reduce(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, 2, 3, 3, 26, 9), 1),   # dst_stride < src_blocks * ratio
+    ((FAKE, FAKE, 2, 3, 3, 27, 0), 1),   # ratio 0
+    ((None, FAKE, 2, 3, 3, 27, 9), 1),
+    ((FAKE, FAKE, -1, 3, 3, 27, 9), 1),
+    ((FAKE, FAKE, 2, 2, 3, 27, 9), 1),   # src_stride < src_blocks
+])
+def test_expand_block_tables_rejects(args, status):
+    assert _lib().pa_expand_block_tables(*args, None) == status
+
+
+def test_partials_bytes():
+    lib = _lib()
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.pa_partials_bytes(32, 32, 128, 8, ctypes.byref(a), ctypes.byref(b)) == 0
+    assert a.value == 32 * 32 * 8 * 128 * 4 and b.value == 32 * 32 * 8 * 4
+    assert lib.pa_partials_bytes(-1, 32, 128, 8, ctypes.byref(a), ctypes.byref(b)) == 1
+
+
+def test_partition_policy():
+    """Host-only policy with an explicit CU count (no device query)."""
+    import paged_varlen_attention_amd as pa
+    cus = 256
+    assert pa.pick_partition_size([100] * 32, 8, cus) == 0            # nothing longer than 256
+    assert pa.pick_partition_size([4000] * 32, 8, cus) == 512         # 8*32*7 >= 512 full partitions
+    assert pa.pick_partition_size([32768] * 4, 4, cus) == 512         # 4*4*64 = 1024 >= 512
+    assert pa.pick_partition_size([700] * 4, 4, cus) == 256           # few full 512s
+    assert pa.pick_partition_size([3000] * 512, 8, cus) == 0          # 4096 unsplit workgroups
+    with pytest.raises(ValueError):
+        pa.pick_partition_size([-5], 1, cus)
