@@ -1,0 +1,321 @@
+"""Benchmark of paged varlen attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--secondary/--no-secondary]
+                    [--no-cpu-baseline] [--copy-calibration]
+
+Headline workload: the GQA decode batch -- 32 requests with one query token
+each, context U[512, 4096], Hq=32 Hkv=8 D=128, 16-token pages shuffled over a
+16,384-block pool, bf16.  One step is the whole decode hot path on that batch:
+pa_reshape_and_cache of the 32 new K/V rows, pa_varlen_attention with 512-token
+split-KV partitions, and pa_split_kv_reduce.  ``value`` is the step's
+algorithmic HBM bytes (every visible KV row once per KV head, Q in, O out, the
+cache write, table ints) divided by the step's wall time.
+
+Inputs are resident in HBM before timing starts.  The step cycles over
+several identical copies of the KV pool so that no step finds the previous
+step's pages in the 256 MB last-level cache (MALL); the "warm" figure
+(one copy) is reported beside it.
+
+``roofline`` times the dominant kernel (the decode attention launch) with HIP
+events on the stream it runs on.  ``cpu_baseline`` times the fp64 oracle on
+the same workload on this host's cores.  ``secondary`` holds the other
+workloads of the metric: long-context split-KV decode and the mixed prefill
+and speculative-verify batches (MFMA TFLOP/s).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "paged-attn decode HBM GB/s (% of peak) + prefill TFLOP/s (% MFMA peak), 1 GPU"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Step:
+    """One pass of the hot path over one batch, on the current stream,
+    bracketed by events so each kernel's duration can be read back."""
+
+    def __init__(self, w, partition_size, copies, device, write_cache):
+        import torch
+        import paged_varlen_attention_amd as pa
+        self.w = w
+        self.P = partition_size
+        self.pa = pa
+        self.device = device
+        self.q = w.q.to(device)
+        self.cu = w.cu_seqlens_q.to(device)
+        self.sl = w.seq_lens.to(device)
+        bt = w.block_tables.to(device)
+        self.ratio = w.kernel_page_ratio
+        self.bt_src = bt
+        self.bt = pa.expand_block_tables(bt, self.ratio) if self.ratio > 1 else bt
+        self.pools = []
+        for _ in range(copies):
+            kc = w.key_cache.to(device)
+            vc = w.value_cache.to(device)
+            self.pools.append((kc, vc))
+        self.write_cache = write_cache and w.slot_mapping is not None
+        if self.write_cache:
+            self.new_k = w.new_key.to(device)
+            self.new_v = w.new_value.to(device)
+            self.slots = w.slot_mapping.to(device)
+        self.out = torch.empty_like(self.q)
+        self.partials = None
+        if self.P:
+            mp = pa.max_partitions(w.max_seq_len, self.P)
+            self.partials = pa.alloc_partials(w.total_q, w.num_q_heads, w.head_dim, mp, device)
+        self.i = 0
+        self.events = []
+
+    def kernel_view(self, kc, vc):
+        if self.ratio == 1:
+            return kc, vc
+        nb, bs, hkv, d = kc.shape
+        return (kc.view(nb * self.ratio, bs // self.ratio, hkv, d),
+                vc.view(nb * self.ratio, bs // self.ratio, hkv, d))
+
+    def __call__(self, record=False):
+        import torch
+        pa, w = self.pa, self.w
+        kc, vc = self.pools[self.i % len(self.pools)]
+        self.i += 1
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
+        if record:
+            ev[0].record()
+        if self.write_cache:
+            pa.reshape_and_cache(self.new_k, self.new_v, kc, vc, self.slots)
+        if record:
+            ev[1].record()
+        if self.ratio > 1:
+            pa.expand_block_tables(self.bt_src, self.ratio, out=self.bt)
+        if record:
+            ev[2].record()
+        kkc, kvc = self.kernel_view(kc, vc)
+        pa.varlen_attention(self.q, kkc, kvc, self.cu, self.sl, self.bt, max_q_len=w.max_q_len,
+                            max_seq_len=w.max_seq_len, scale=w.scale, partition_size=self.P,
+                            out=self.out, partials=self.partials, reduce=False)
+        if record:
+            ev[3].record()
+        if self.P:
+            pa.split_kv_reduce(self.out, self.partials, self.cu, self.sl, self.P)
+        if record:
+            ev[4].record()
+            self.events.append(ev)
+
+    def kernel_ms(self):
+        """Mean durations (ms) of: cache write, table view, attention, reduce."""
+        n = len(self.events)
+        if not n:
+            return {}
+        tot = [0.0] * 4
+        for ev in self.events:
+            for k in range(4):
+                tot[k] += ev[k].elapsed_time(ev[k + 1])
+        return dict(zip(("cache_write", "table_view", "attention", "reduce"),
+                        (t / n for t in tot)))
+
+
+def step_bytes(w, include_cache_write):
+    b = w.algorithmic_bytes()
+    if include_cache_write and w.slot_mapping is not None:
+        n = int((w.slot_mapping >= 0).sum())
+        b += 2 * 2 * n * w.num_kv_heads * w.head_dim * w.elt_bytes  # K and V rows, read + write
+    return b
+
+
+def time_steps(step, steps, warmup, record=True):
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    step.events.clear()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(record=record)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def measure(w, P, steps, warmup, copies, device, write_cache=True):
+    step = Step(w, P, copies, device, write_cache)
+    sec = time_steps(step, steps, warmup)
+    km = step.kernel_ms()
+    step_warm = Step(w, P, 1, device, write_cache)
+    sec_warm = time_steps(step_warm, max(5, steps // 2), 2)
+    km_warm = step_warm.kernel_ms()
+    del step, step_warm
+    return sec, km, sec_warm, km_warm
+
+
+def cpu_baseline(w, budget_s=10.0):
+    """The fp64 oracle, as it stands, on whole batches of the same workload
+    until about budget_s of wall time has passed."""
+    import oracle
+    oracle.attention  # noqa: B018  (loads / builds the oracle library)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.run_workload(w)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or el / reps * (reps + 1) > 3 * budget_s:
+            break
+    per = el / reps
+    return {"value": round(w.algorithmic_bytes() / per / 1e9, 3), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{reps} full passes of the {w.name} batch ({w.num_seqs} requests, all "
+                      f"{w.num_q_heads} heads), {per * 1e3:.1f} ms each, fp64 C oracle, OpenMP"}
+
+
+def copy_calibration(device, mib=512, reps=5):
+    """A plain device copy of known size, for scaling rocprof FETCH/WRITE counters."""
+    import torch
+    a = torch.empty(mib * 2 ** 20 // 4, dtype=torch.float32, device=device).fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} x copy of {mib} MiB (read {mib} MiB + write {mib} MiB each)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=3, help="KV pool copies cycled per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--secondary", dest="secondary", action="store_true", default=True)
+    ap.add_argument("--no-secondary", dest="secondary", action="store_false")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import paged_varlen_attention_amd  # noqa: F401  (fails loudly without libpa.so)
+
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+
+    # ---------------- headline: GQA decode batch ----------------
+    w = W.gqa_decode_bf16()
+    P = 512
+    log(f"workload {w.name}: {w.description}; P={P}")
+    sec, km, sec_warm, km_warm = measure(w, P, args.steps, args.warmup, args.copies, device)
+    nbytes = step_bytes(w, include_cache_write=True)
+    value = nbytes / sec / 1e9
+    attn_bytes = w.algorithmic_bytes()
+    achieved = attn_bytes / (km["attention"] * 1e-3) / 1e9
+    log(f"decode step {sec * 1e3:.4f} ms ({value:.1f} GB/s); kernels {km}; warm step "
+        f"{sec_warm * 1e3:.4f} ms, kernels {km_warm}")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "gqa_decode_bf16",
+            "requests": w.num_seqs,
+            "query_tokens": w.total_q,
+            "context": "U[512,4096]",
+            "heads_q_kv_dim": [w.num_q_heads, w.num_kv_heads, w.head_dim],
+            "page_size": w.block_size,
+            "pool_blocks": w.num_blocks,
+            "partition_size": P,
+            "step": "reshape_and_cache + varlen_attention + split_kv_reduce",
+            "algorithmic_bytes_per_step": nbytes,
+            "kv_pool_copies_cycled": args.copies,
+            "warm_ms_per_step": round(sec_warm * 1e3, 5),
+            "kernel_ms": {k: round(v, 5) for k, v in km.items()},
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_kernel (pa_varlen_attention, split 512)",
+            "achieved": round(achieved, 3),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": attn_bytes,
+            "avg_launch_ms": round(km["attention"], 5),
+        },
+    }
+
+    # ---------------- secondary workloads ----------------
+    if args.secondary:
+        sec_out = {}
+        steps2 = max(10, args.steps // 2)
+        w4 = W.long_decode_bf16()
+        for P4 in (256, 512):
+            s4, k4, s4w, _ = measure(w4, P4, steps2, 5, 2, device)
+            b4 = w4.algorithmic_bytes()
+            sec_out[f"long_decode_bf16_P{P4}"] = {
+                "ms_per_step": round(s4 * 1e3, 5), "GB/s": round(b4 / s4 / 1e9, 2),
+                "attention_ms": round(k4["attention"], 5), "reduce_ms": round(k4["reduce"], 5),
+                "attention_GB/s": round(b4 / (k4["attention"] * 1e-3) / 1e9, 2),
+                "frac_hbm": round(b4 / s4 / 1e9 / HBM_PEAK_GBS, 4),
+                "warm_ms_per_step": round(s4w * 1e3, 5)}
+            log(f"long decode P={P4}: {sec_out[f'long_decode_bf16_P{P4}']}")
+        del w4
+        for name, P3 in (("mixed_prefill_bf16_A", 0), ("mixed_prefill_bf16_B", 0),
+                         ("spec_verify_bf16", 0)):
+            try:
+                w3 = W.CONFIGS[name]()
+                s3, k3, s3w, _ = measure(w3, P3, steps2, 5, 2, device)
+            except Exception as e:  # report, do not hide: the line says what failed
+                sec_out[name] = {"error": str(e)[:200]}
+                log(f"{name}: {e}")
+                continue
+            f3 = w3.algorithmic_flops()
+            b3 = step_bytes(w3, True)
+            sec_out[name] = {
+                "ms_per_step": round(s3 * 1e3, 5),
+                "TFLOP/s": round(f3 / s3 / 1e12, 2),
+                "attention_ms": round(k3["attention"], 5),
+                "attention_TFLOP/s": round(f3 / (k3["attention"] * 1e-3) / 1e12, 2),
+                "frac_mfma": round(f3 / (k3["attention"] * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                "GB/s": round(b3 / s3 / 1e9, 2),
+                "algorithmic_flops": f3, "algorithmic_bytes": b3,
+                "warm_ms_per_step": round(s3w * 1e3, 5)}
+            log(f"{name}: {sec_out[name]}")
+        result["secondary"] = sec_out
+
+    if args.copy_calibration:
+        copy_calibration(device)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w)
+        log(f"cpu baseline: {result['cpu_baseline']}")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

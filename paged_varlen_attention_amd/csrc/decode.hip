@@ -10,54 +10,74 @@
 //
 // The design is our own for CDNA4:
 //  * grid = (partitions, kv_heads, requests); NW waves per workgroup take the
-//    16-token chunks of the partition round-robin, each with a private ring of
-//    NST LDS stages, so no workgroup barrier is needed until the final merge;
+//    CT-token chunks of the partition round-robin, each wave with a private ring
+//    of NST LDS stages, so no workgroup barrier is needed until the final merge;
 //  * K/V rows move HBM -> LDS with gfx950's 16-byte global_load_lds_dwordx4,
 //    fully coalesced (one wave instruction moves 1 KB), while the previous stage
 //    is being consumed; vmcnt waits are explicit;
 //  * the page-table walk is one wave-wide load of up to 64 entries per window,
-//    then v_readlane per chunk (a scalar broadcast, no shuffles);
+//    then v_readlane per chunk (a scalar broadcast, no shuffles), and the DMA
+//    base addresses are pure scalar arithmetic;
 //  * a token's row is split over L lanes (32 bytes each); QK^T uses
 //    v_dot2c_f32_bf16 on bf16 pairs and a DPP all-reduce over the L lanes;
 //  * every lane keeps its own online-softmax state for its token subset; the
-//    running max is only moved when a score exceeds it by more than 2^8
-//    (the result is exact whatever reference max is used, since the partial
-//    sum and the accumulator share it);
+//    loop over a wave's full chunks has no data-dependent branch (only its
+//    last chunk can hold the end of the range and is peeled off), so the
+//    accumulators stay in their registers;
 //  * PV pairs two tokens per lane: p is packed to bf16 pairs and V is
 //    interleaved with v_perm_b32 so one v_dot2c does two multiply-adds;
-//  * lane groups and waves are merged once at the end (bpermute, then LDS).
+//  * at the end, every lane is rescaled to the wave-wide max and the lane
+//    groups of the wave are summed in registers (DPP rotations inside each
+//    16-lane row, then v_permlane16/32_swap across rows only as far as the
+//    LDS merge area requires); the row states go to LDS and all threads of
+//    the workgroup merge them.
 #include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
 namespace {
 
-constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units: p may reach 2^8 before rescaling
+#ifndef PA_DECODE_HEAD_FASTEST
+#define PA_DECODE_HEAD_FASTEST 1
+#endif
 
-template <typename T, int D, int GT, int NW_, int NST_>
+
+template <typename T, int D, int GT, int CT_, int NW_, int NST_>
 struct DecodeCfg {
     static constexpr bool BF16 = sizeof(T) == 2;
     static constexpr int ELT = sizeof(T);
+    static constexpr int CT = CT_;               // tokens per chunk (LDS stage)
     static constexpr int R = D * ELT;            // bytes per K/V row of one head
     static constexpr int L = R / 32;             // lanes per token (32 bytes each)
     static constexpr int TPP = 64 / L;           // tokens per pass of the wave
-    static constexpr int NP = CHUNK / TPP;       // passes per 16-token chunk
+    static constexpr int NP = CT / TPP;          // passes per chunk
     static constexpr int EPW = 4 / ELT;          // elements per 32-bit word
-    static constexpr int NI = CHUNK * R / 1024;  // DMA instructions per chunk per tensor
+    static constexpr int NI = CT * R / 1024;     // DMA instructions per chunk per tensor
     static constexpr int RPI = 1024 / R;         // rows moved by one DMA instruction
-    static constexpr int SLOT = 2 * CHUNK * R;   // bytes of one LDS stage (K rows, then V rows)
+    static constexpr int SLOT = 2 * CT * R;      // bytes of one LDS stage (K rows, then V rows)
     static constexpr int NW = NW_;
     static constexpr int NST = NST_;
     static constexpr int VM_PER_CHUNK = 2 * NI;
-    // softmax unit: passes handled per online-softmax update
+    // passes paired in one v_dot2 for PV
     static constexpr int SU = (BF16 && NP >= 2) ? 2 : 1;
+    static constexpr int NE = 32 / ELT;          // elements per lane per row
+    static constexpr int STATE_FLOATS = GT * D + 2 * GT;  // acc, then m, then l
     static constexpr int STAGE_BYTES = NW * NST * SLOT;
-    static constexpr int MERGE_BYTES = NW * (GT * D + 3 * GT) * 4;
+    // Merge states per wave: as many row states as fit in the staging LDS
+    // (4 rows, or 2 halves when a token spans 32 lanes), else fewer after
+    // merging rows in registers.
+    static constexpr int SPW_MAX = L <= 16 ? 4 : 2;
+    static constexpr bool fits(int spw) { return NW * spw * STATE_FLOATS * 4 <= STAGE_BYTES; }
+    static constexpr int SPW = fits(SPW_MAX) ? SPW_MAX : (fits(SPW_MAX / 2) ? SPW_MAX / 2 : 1);
+    static constexpr int NS = NW * SPW;          // merge states of the workgroup
+    static constexpr int MERGE_BYTES = NS * STATE_FLOATS * 4;
     static constexpr int LDS_BYTES = STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES;
     static_assert(L >= 4 && L <= 32, "row split");
-    static_assert(NI >= 1 && RPI >= 1 && CHUNK * R % 1024 == 0, "dma shape");
+    static_assert(NP >= 1 && CT % TPP == 0, "chunk covers whole passes");
+    static_assert(NI >= 1 && RPI >= 1 && CT * R % 1024 == 0, "dma shape");
     static_assert((NST - 1) * VM_PER_CHUNK < 64, "vmcnt range");
     static_assert(NP % SU == 0, "pass pairing");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
 // Element index (within the head's D) of word w of lane column c.
@@ -65,6 +85,21 @@ template <class C>
 __device__ __forceinline__ int word_elem(int c, int w) {
     // two 16-byte pieces per lane: piece i at byte (i*L + c)*16 of the row
     return ((w / 4) * C::L + c) * (16 / C::ELT) + (w % 4) * C::EPW;
+}
+
+// Wait until this wave's DMA for the chunk `ahead` chunks before the newest
+// one has landed in LDS (vmcnt counts instructions and completes in order).
+template <int VM, int MAXA>
+__device__ __forceinline__ void wait_chunks_ahead(int ahead) {
+    if constexpr (MAXA > 0) {
+        if (ahead >= MAXA) {
+            wait_vmcnt<MAXA * VM>();
+            return;
+        }
+        wait_chunks_ahead<VM, MAXA - 1>(ahead);
+    } else {
+        wait_vmcnt<0>();
+    }
 }
 
 template <class C>
@@ -75,14 +110,175 @@ __device__ __forceinline__ void read_row_words(const char *lds_row, int c, uint3
     w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
 }
 
-template <typename T, int D, int GT, int NW, int NST>
+// Max over all 64 lanes of the wave.
+__device__ __forceinline__ float wave_max(float x) {
+    x = group_max<16>(x);
+    const RowPair a = row_pair16(x);
+    x = fmaxf(a.a, a.b);
+    const RowPair b = row_pair32(x);
+    return fmaxf(b.a, b.b);
+}
+
+// Sum of this lane's values with those of the lane the DPP row rotation CTRL
+// brings in (same column, another lane group of the row).
+template <int CTRL, int GT, int NE>
+__device__ __forceinline__ void sum_rot(float (&l)[GT], float (&acc)[GT][NE]) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+        l[g] += dpp<CTRL>(l[g]);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[g][e] += dpp<CTRL>(acc[g][e]);
+    }
+}
+
+// The same across the rows of the wave (rows 2i+1 onto 2i, or i+2 onto i).
+template <bool X32, int GT, int NE>
+__device__ __forceinline__ void sum_pairs(float (&l)[GT], float (&acc)[GT][NE]) {
+    auto pair = [](float x) { return X32 ? row_pair32(x) : row_pair16(x); };
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+        const RowPair pl = pair(l[g]);
+        l[g] = pl.a + pl.b;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const RowPair pa = pair(acc[g][e]);
+            acc[g][e] = pa.a + pa.b;
+        }
+    }
+}
+
+// One chunk staged in LDS: scores, online-softmax update and PV for this
+// lane's tokens (the whole chunk is one softmax step).  MASKED is the chunk
+// that holds the end of the key range: its tokens past the end get score -inf
+// and their V rows (possibly NaN page tails) are replaced by zeros.  Only a
+// wave's last chunk can be masked, so the loop over the others has no
+// data-dependent branch at all (branches around the accumulators make the
+// register allocator copy them on every iteration).
+template <class C, int GT, bool MASKED>
+__device__ __forceinline__ void chunk_step(const char *kst, const char *vst, int c, int tip,
+                                           int tok0, int tok_end, float scale_log2,
+                                           const uint32_t (&qw)[GT][8], float (&m)[GT],
+                                           float (&l)[GT], float (&accv)[GT][C::NE]) {
+    constexpr int NE = C::NE;
+    constexpr int NP = C::NP;
+    // ---- scores of every pass ----
+    float sc[NP][GT];
+    bool valid[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+        const int t = j * C::TPP + tip;
+        valid[j] = !MASKED || tok0 + t < tok_end;
+        uint32_t kw[8];
+        read_row_words<C>(kst + t * C::R, c, kw);
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            float a = 0.f;
+            if constexpr (C::BF16) {
+#pragma unroll
+                for (int w = 0; w < 8; ++w) a = dot2(qw[g][w], kw[w], a);
+            } else {
+#pragma unroll
+                for (int w = 0; w < 8; ++w)
+                    a = fmaf(__uint_as_float(qw[g][w]), __uint_as_float(kw[w]), a);
+            }
+            sc[j][g] = a;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j)
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            const float a = group_sum<C::L>(sc[j][g]) * scale_log2;
+            sc[j][g] = (!MASKED || valid[j]) ? a : NEG_INF;
+        }
+    // ---- online softmax: new running max, rescale of l and acc ----
+    // In an unmasked chunk every score is finite, so the new max is finite and
+    // exp2 needs no -inf guard; the masked chunk guards both.
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+        float mx = sc[0][g];
+#pragma unroll
+        for (int j = 1; j < NP; ++j) mx = fmaxf(mx, sc[j][g]);
+        const float mn = fmaxf(m[g], mx);
+        const float alpha = MASKED ? exp2_diff(m[g], mn) : __builtin_amdgcn_exp2f(m[g] - mn);
+        m[g] = mn;
+        l[g] *= alpha;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) accv[g][e] *= alpha;
+    }
+    float pr[NP][GT];
+#pragma unroll
+    for (int j = 0; j < NP; ++j)
+#pragma unroll
+        for (int g = 0; g < GT; ++g)
+            pr[j][g] = (MASKED && sc[j][g] == NEG_INF) ? 0.f
+                                                       : __builtin_amdgcn_exp2f(sc[j][g] - m[g]);
+
+    // ---- PV ----
+#pragma unroll
+    for (int j0 = 0; j0 < NP; j0 += C::SU) {
+        uint32_t vw[C::SU][8];
+#pragma unroll
+        for (int j = 0; j < C::SU; ++j) {
+            const int t = (j0 + j) * C::TPP + tip;
+            read_row_words<C>(vst + t * C::R, c, vw[j]);
+            if (MASKED && !valid[j0 + j]) {
+#pragma unroll
+                for (int w = 0; w < 8; ++w) vw[j][w] = 0u;
+            }
+        }
+        if constexpr (C::BF16 && C::SU == 2) {
+            constexpr uint32_t ONES = 0x3F803F80u;  // bf16 pair (1, 1)
+            uint32_t pk[GT];
+#pragma unroll
+            for (int g = 0; g < GT; ++g) {
+                pk[g] = pack_bf16(pr[j0][g], pr[j0 + 1][g]);
+                l[g] = dot2(pk[g], ONES, l[g]);  // the weights actually applied
+            }
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                const uint32_t lo = perm(vw[1][w], vw[0][w], 0x05040100u);
+                const uint32_t hi = perm(vw[1][w], vw[0][w], 0x07060302u);
+#pragma unroll
+                for (int g = 0; g < GT; ++g) {
+                    accv[g][2 * w] = dot2(pk[g], lo, accv[g][2 * w]);
+                    accv[g][2 * w + 1] = dot2(pk[g], hi, accv[g][2 * w + 1]);
+                }
+            }
+        } else if constexpr (C::BF16) {
+#pragma unroll
+            for (int g = 0; g < GT; ++g) {
+                const float pb = bf16hi(pack_bf16(0.f, pr[j0][g]));
+                l[g] += pb;
+#pragma unroll
+                for (int w = 0; w < 8; ++w) {
+                    accv[g][2 * w] = fmaf(pb, bf16lo(vw[0][w]), accv[g][2 * w]);
+                    accv[g][2 * w + 1] = fmaf(pb, bf16hi(vw[0][w]), accv[g][2 * w + 1]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int g = 0; g < GT; ++g) {
+                l[g] += pr[j0][g];
+#pragma unroll
+                for (int w = 0; w < 8; ++w)
+                    accv[g][w] = fmaf(pr[j0][g], __uint_as_float(vw[0][w]), accv[g][w]);
+            }
+        }
+    }
+}
+
+template <typename T, int D, int GT, int CT, int NW, int NST>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
-    using C = DecodeCfg<T, D, GT, NW, NST>;
+    using C = DecodeCfg<T, D, GT, CT, NW, NST>;
     __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
 
+    // The KV heads of one partition are adjacent in the grid, so the
+    // workgroups that run together read the same pages (all heads' rows of a
+    // page are contiguous) rather than 1/Hkv of many different pages.
     const int r = blockIdx.z;
-    const int kvh = blockIdx.y;
-    const int part = blockIdx.x;
+    const int kvh = PA_DECODE_HEAD_FASTEST ? blockIdx.x : blockIdx.y;
+    const int part = PA_DECODE_HEAD_FASTEST ? blockIdx.y : blockIdx.x;
     const int q0 = p.cu_q[r];
     if (p.cu_q[r + 1] - q0 <= 0) return;
     const int seq_len = p.seq_lens[r];
@@ -96,6 +292,30 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane % C::L;    // column of the row this lane holds
     const int tip = lane / C::L;  // token slot within a pass
+
+    // ---- this wave's chunks and its block-table window ----
+    const int bs = p.block_size;
+    const int lbs = p.log2_bs;
+    const int c_begin = tok_begin / CT;
+    const int c_end = (tok_end + CT - 1) / CT;
+    const int nchunks = c_end - c_begin;
+    const int nmy = nchunks > wave ? (nchunks - wave + NW - 1) / NW : 0;
+    const int seq_pages = (seq_len + bs - 1) >> lbs;
+    const int ppc = bs < CT ? CT / bs : 1;  // pages per chunk: 1, or 2 for 8-token pages
+    const int cpw = 64 / ppc;               // chunks covered by one block-table window
+    const int32_t *bt_row = p.bt + (size_t)r * p.bt_stride;
+
+    // Lane i of the window holds page (i / cpw) of this wave's chunk kw0 + i % cpw.
+    auto load_window = [&](int kw0) -> int {
+        const int k = kw0 + lane % cpw;
+        const int ch = c_begin + wave + k * NW;
+        const int lp = ((ch * CT) >> lbs) + lane / cpw;
+        int v = 0;
+        if (k < nmy && lp < seq_pages) v = bt_row[lp];
+        return v < 0 ? 0 : (v >= p.num_blocks ? p.num_blocks - 1 : v);
+    };
+    int win_base = 0;
+    int btv = load_window(0);
 
     // ---- query registers: the lane's 8 words of each head of the group ----
     uint32_t qw[GT][8];
@@ -117,30 +337,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
         }
     }
 
-    // ---- this wave's chunks ----
-    const int bs = p.block_size;
-    const int lbs = p.log2_bs;
-    const int c_begin = tok_begin / CHUNK;
-    const int c_end = (tok_end + CHUNK - 1) / CHUNK;
-    const int nchunks = c_end - c_begin;
-    const int nmy = nchunks > wave ? (nchunks - wave + NW - 1) / NW : 0;
-    const int seq_pages = (seq_len + bs - 1) >> lbs;
-    const int ppc = bs < CHUNK ? 2 : 1;  // pages per chunk (block_size 8 -> 2)
-    const int cpw = 64 / ppc;            // chunks covered by one block-table window
-    const int32_t *bt_row = p.bt + (size_t)r * p.bt_stride;
-
-    // Window of block-table entries: lane i holds the page of this wave's
-    // chunk (kw0 + i % cpw), half i / cpw of it.
-    auto load_window = [&](int kw0) -> int {
-        const int k = kw0 + lane % cpw;
-        const int ch = c_begin + wave + k * NW;
-        const int lp = ((ch * CHUNK) >> lbs) + lane / cpw;
-        int v = 0;
-        if (k < nmy && lp < seq_pages) v = bt_row[lp];
-        v = v < 0 ? 0 : (v >= p.num_blocks ? p.num_blocks - 1 : v);
-        return v;
-    };
-
     // Per-lane byte offsets of the rows this lane moves, relative to the row of
     // the chunk's first token (one per DMA instruction).
     const uint32_t row_stride = (uint32_t)p.hkv * C::R;  // bytes between tokens of a page
@@ -154,248 +350,127 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
 
     const uint32_t lds_wave = lds_addr(lds) + (uint32_t)(wave * NST * C::SLOT);
     const char *kc = reinterpret_cast<const char *>(p.kc);
-    const char *vc = reinterpret_cast<const char *>(p.vc);
-    const size_t head_off = (size_t)kvh * C::R;
+    const int64_t v_minus_k = reinterpret_cast<const char *>(p.vc) - kc;
+    const uint64_t page_bytes = (uint64_t)bs * row_stride;
+    const uint64_t head_off = (uint64_t)kvh * C::R;
 
-    int win_base = 0;
-    int btv = load_window(0);
-
-    // Issue the DMA of this wave's k-th chunk into stage s.
+    // Issue the DMA of this wave's k-th chunk into stage s.  All address
+    // arithmetic is on wave-uniform values.
     auto issue = [&](int k, int s) {
-        if (k - win_base >= cpw) {  // slide the window (only for long unsplit ranges)
+        if (k - win_base >= cpw) {  // slide the window (long unsplit ranges only)
             win_base = k;
             btv = load_window(k);
         }
-        const int ch = c_begin + wave + k * NW;
-        const int tok0 = ch * CHUNK;
+        const int tok0 = (c_begin + wave + k * NW) * CT;
         const int idx = k - win_base;
         const int phys0 = __builtin_amdgcn_readlane(btv, idx);
-        const int off0 = tok0 & (bs - 1);
-        const size_t row0 = ((size_t)phys0 * bs + off0) * p.hkv;
-        const char *kb0 = kc + row0 * C::R + head_off;
-        const char *vb0 = vc + row0 * C::R + head_off;
-        const char *kb1 = kb0;
-        const char *vb1 = vb0;
+        const uint64_t off0 = (uint64_t)phys0 * page_bytes +
+                              (uint64_t)(tok0 & (bs - 1)) * row_stride + head_off;
+        uint64_t off1 = off0;
         if (ppc == 2) {
-            // rows 8..15 of the chunk live in the next page; when that page is
-            // past the sequence its rows are masked, so re-read page 0 instead.
-            int phys1 = phys0;
-            if (tok0 + 8 < seq_len) phys1 = __builtin_amdgcn_readlane(btv, idx + cpw);
-            const size_t row1 = ((size_t)phys1 * bs) * p.hkv;
-            kb1 = kc + row1 * C::R + head_off - (size_t)8 * row_stride;
-            vb1 = vc + row1 * C::R + head_off - (size_t)8 * row_stride;
+            // rows 8..15 of the chunk live in the next page; past the sequence
+            // those rows are masked, so page 0 is re-read instead.
+            const int phys1 =
+                tok0 + 8 < seq_len ? __builtin_amdgcn_readlane(btv, idx + cpw) : phys0;
+            off1 = (uint64_t)phys1 * page_bytes + head_off - 8ull * row_stride;
         }
+        const char *kb0 = kc + off0;
+        const char *kb1 = kc + off1;
         const uint32_t ldsk = lds_wave + (uint32_t)(s * C::SLOT);
-        const uint32_t ldsv = ldsk + CHUNK * C::R;
+        const uint32_t ldsv = ldsk + CT * C::R;
 #pragma unroll
-        for (int ii = 0; ii < C::NI; ++ii) {
-            const bool hi = ii * C::RPI >= 8;
-            dma16(hi ? kb1 : kb0, voff[ii], ldsk + ii * 1024);
-        }
+        for (int ii = 0; ii < C::NI; ++ii)
+            dma16(ii * C::RPI >= 8 ? kb1 : kb0, voff[ii], ldsk + ii * 1024);
 #pragma unroll
-        for (int ii = 0; ii < C::NI; ++ii) {
-            const bool hi = ii * C::RPI >= 8;
-            dma16(hi ? vb1 : vb0, voff[ii], ldsv + ii * 1024);
-        }
+        for (int ii = 0; ii < C::NI; ++ii)
+            dma16((ii * C::RPI >= 8 ? kb1 : kb0) + v_minus_k, voff[ii], ldsv + ii * 1024);
     };
 
     // ---- online softmax state (per lane, for its token subset) ----
-    float m[GT], mt[GT], l[GT];
-    constexpr int NE = 32 / C::ELT;  // elements per lane per row
+    constexpr int NE = C::NE;
+    float m[GT], l[GT];
     float accv[GT][NE];
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
         m[g] = NEG_INF;
-        mt[g] = NEG_INF;
         l[g] = 0.f;
 #pragma unroll
         for (int e = 0; e < NE; ++e) accv[g][e] = 0.f;
     }
 
-    // prologue
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s)
         if (s < nmy) issue(s, s);
 
-    for (int k = 0; k < nmy; ++k) {
-        const int s = k % NST;
+    // Every chunk but the wave's last is full: a branch-free loop over them,
+    // then the last one, the only one that can hold the end of the range.
+    auto stage = [&](int k, const char *&kst, const char *&vst) {
         if (k + NST - 1 < nmy) issue(k + NST - 1, (k + NST - 1) % NST);
-        // chunks issued after k that may stay in flight
-        const int ahead = min(NST - 1, nmy - 1 - k);
-        if constexpr (NST >= 3) {
-            if (ahead >= 2) wait_vmcnt<2 * C::VM_PER_CHUNK>();
-            else if (ahead == 1) wait_vmcnt<C::VM_PER_CHUNK>();
-            else wait_vmcnt<0>();
-        } else {
-            if (ahead >= 1) wait_vmcnt<C::VM_PER_CHUNK>();
-            else wait_vmcnt<0>();
-        }
-
-        const int ch = c_begin + wave + k * NW;
-        const int tok0 = ch * CHUNK;
-        const bool partial = tok0 + CHUNK > tok_end;
-        const char *kst = lds + (wave * NST + s) * C::SLOT;
-        const char *vst = kst + CHUNK * C::R;
-
-#pragma unroll
-        for (int u = 0; u < C::NP; u += C::SU) {
-            float sc[C::SU][GT];
-            bool valid[C::SU];
-            // ---- scores ----
-#pragma unroll
-            for (int j = 0; j < C::SU; ++j) {
-                const int t = (u + j) * C::TPP + tip;
-                valid[j] = tok0 + t < tok_end;
-                uint32_t kw[8];
-                read_row_words<C>(kst + t * C::R, c, kw);
-#pragma unroll
-                for (int g = 0; g < GT; ++g) {
-                    float a = 0.f;
-                    if constexpr (C::BF16) {
-#pragma unroll
-                        for (int w = 0; w < 8; ++w) a = dot2(qw[g][w], kw[w], a);
-                    } else {
-#pragma unroll
-                        for (int w = 0; w < 8; ++w)
-                            a = fmaf(__uint_as_float(qw[g][w]), __uint_as_float(kw[w]), a);
-                    }
-                    sc[j][g] = a;
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < C::SU; ++j)
-#pragma unroll
-                for (int g = 0; g < GT; ++g) {
-                    const float a = group_sum<C::L>(sc[j][g]) * p.scale_log2;
-                    sc[j][g] = valid[j] ? a : NEG_INF;
-                }
-            // ---- online softmax with lazy rescale ----
-            float mx[GT];
-            bool need = false;
-#pragma unroll
-            for (int g = 0; g < GT; ++g) {
-                mx[g] = sc[0][g];
-#pragma unroll
-                for (int j = 1; j < C::SU; ++j) mx[g] = fmaxf(mx[g], sc[j][g]);
-                mt[g] = fmaxf(mt[g], mx[g]);
-                need |= mx[g] > m[g] + RESCALE_THRESHOLD;
-            }
-            if (__builtin_amdgcn_ballot_w64(need)) {
-#pragma unroll
-                for (int g = 0; g < GT; ++g) {
-                    if (mx[g] > m[g] + RESCALE_THRESHOLD) {
-                        const float alpha = exp2_diff(m[g], mx[g]);
-                        m[g] = mx[g];
-                        l[g] *= alpha;
-#pragma unroll
-                        for (int e = 0; e < NE; ++e) accv[g][e] *= alpha;
-                    }
-                }
-            }
-            float pr[C::SU][GT];
-#pragma unroll
-            for (int j = 0; j < C::SU; ++j)
-#pragma unroll
-                for (int g = 0; g < GT; ++g)
-                    pr[j][g] = sc[j][g] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(sc[j][g] - m[g]);
-
-            // ---- PV ----
-            uint32_t vw[C::SU][8];
-#pragma unroll
-            for (int j = 0; j < C::SU; ++j) {
-                const int t = (u + j) * C::TPP + tip;
-                read_row_words<C>(vst + t * C::R, c, vw[j]);
-                if (partial && !valid[j]) {
-#pragma unroll
-                    for (int w = 0; w < 8; ++w) vw[j][w] = 0u;  // page tail may hold NaN
-                }
-            }
-            if constexpr (C::BF16 && C::SU == 2) {
-                uint32_t pk[GT];
-#pragma unroll
-                for (int g = 0; g < GT; ++g) {
-                    pk[g] = pack_bf16(pr[0][g], pr[1][g]);
-                    l[g] += bf16lo(pk[g]) + bf16hi(pk[g]);  // the weights actually applied
-                }
-#pragma unroll
-                for (int w = 0; w < 8; ++w) {
-                    const uint32_t lo = perm(vw[1][w], vw[0][w], 0x05040100u);
-                    const uint32_t hi = perm(vw[1][w], vw[0][w], 0x07060302u);
-#pragma unroll
-                    for (int g = 0; g < GT; ++g) {
-                        accv[g][2 * w] = dot2(pk[g], lo, accv[g][2 * w]);
-                        accv[g][2 * w + 1] = dot2(pk[g], hi, accv[g][2 * w + 1]);
-                    }
-                }
-            } else if constexpr (C::BF16) {
-#pragma unroll
-                for (int g = 0; g < GT; ++g) {
-                    const float pb = bf16hi(pack_bf16(0.f, pr[0][g]));
-                    l[g] += pb;
-#pragma unroll
-                    for (int w = 0; w < 8; ++w) {
-                        accv[g][2 * w] = fmaf(pb, bf16lo(vw[0][w]), accv[g][2 * w]);
-                        accv[g][2 * w + 1] = fmaf(pb, bf16hi(vw[0][w]), accv[g][2 * w + 1]);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < C::SU; ++j)
-#pragma unroll
-                    for (int g = 0; g < GT; ++g) {
-                        l[g] += pr[j][g];
-#pragma unroll
-                        for (int w = 0; w < 8; ++w)
-                            accv[g][w] = fmaf(pr[j][g], __uint_as_float(vw[j][w]), accv[g][w]);
-                    }
-            }
-        }
+        wait_chunks_ahead<C::VM_PER_CHUNK, NST - 1>(min(NST - 1, nmy - 1 - k));
+        kst = lds + (wave * NST + k % NST) * C::SLOT;
+        vst = kst + CT * C::R;
+    };
+    for (int k = 0; k < nmy - 1; ++k) {
+        const char *kst, *vst;
+        stage(k, kst, vst);
+        chunk_step<C, GT, false>(kst, vst, c, tip, 0, 0, p.scale_log2, qw, m, l, accv);
+    }
+    if (nmy > 0) {
+        const char *kst, *vst;
+        stage(nmy - 1, kst, vst);
+        const int tok0 = (c_begin + wave + (nmy - 1) * NW) * CT;
+        chunk_step<C, GT, true>(kst, vst, c, tip, tok0, tok_end, p.scale_log2, qw, m, l, accv);
     }
 
-    // ---- merge the lane groups of this wave (lanes with the same column) ----
+    // ---- merge the wave's lane groups: rescale every lane to the wave-wide
+    // max, after which merging is a plain sum (DPP rotation inside each
+    // 16-lane row, then v_permlane16/32_swap across rows) ----
 #pragma unroll
-    for (int off = C::L; off < 64; off <<= 1) {
+    for (int g = 0; g < GT; ++g) {
+        const float M = wave_max(m[g]);
+        const float f = exp2_diff(m[g], M);
+        m[g] = M;
+        l[g] *= f;
 #pragma unroll
-        for (int g = 0; g < GT; ++g) {
-            const float mo = __shfl_xor(m[g], off);
-            const float lo = __shfl_xor(l[g], off);
-            mt[g] = fmaxf(mt[g], __shfl_xor(mt[g], off));
-            const float M = fmaxf(m[g], mo);
-            const float fa = exp2_diff(m[g], M);
-            const float fb = exp2_diff(mo, M);
-            l[g] = l[g] * fa + lo * fb;
-#pragma unroll
-            for (int e = 0; e < NE; ++e) {
-                const float ao = __shfl_xor(accv[g][e], off);
-                accv[g][e] = accv[g][e] * fa + ao * fb;
-            }
-            m[g] = M;
-        }
+        for (int e = 0; e < NE; ++e) accv[g][e] *= f;
     }
+    if constexpr (C::L == 8) {
+        sum_rot<0x128, GT, NE>(l, accv);  // row_ror:8
+    } else if constexpr (C::L == 4) {
+        sum_rot<0x128, GT, NE>(l, accv);  // row_ror:8
+        sum_rot<0x124, GT, NE>(l, accv);  // row_ror:4
+    }
+    // rows i and i+2 onto one state, then rows 2i and 2i+1, as LDS requires
+    if constexpr (C::SPW * 2 <= C::SPW_MAX) sum_pairs<true, GT, NE>(l, accv);
+    if constexpr (C::L <= 16 && C::SPW == 1) sum_pairs<false, GT, NE>(l, accv);
 
-    // ---- merge the waves through LDS ----
+    // ---- one state per wave to LDS, then all threads merge the waves ----
     __syncthreads();  // every wave is done with its stages
     float *mrg = reinterpret_cast<float *>(lds);
-    float *macc = mrg + wave * (GT * D + 3 * GT);
-    if (tip == 0) {
+    {
+        // state of lane group `row`: 16-lane rows (32-lane halves when L = 32)
+        const int row = C::L <= 16 ? lane / 16 : lane / 32;
+        float *st = mrg + (wave * C::SPW + row) * C::STATE_FLOATS;
+        const bool writer = row < C::SPW && (C::L <= 16 ? lane % 16 : lane % 32) < C::L;
+        if (writer) {
 #pragma unroll
-        for (int g = 0; g < GT; ++g)
+            for (int g = 0; g < GT; ++g)
 #pragma unroll
-            for (int w = 0; w < 8; ++w) {
-                const int d = word_elem<C>(c, w);
-                if constexpr (C::BF16) {
-                    macc[g * D + d] = accv[g][2 * w];
-                    macc[g * D + d + 1] = accv[g][2 * w + 1];
-                } else {
-                    macc[g * D + d] = accv[g][w];
+                for (int w = 0; w < 8; ++w) {
+                    const int d = word_elem<C>(c, w);
+                    if constexpr (C::BF16) {
+                        st[g * D + d] = accv[g][2 * w];
+                        st[g * D + d + 1] = accv[g][2 * w + 1];
+                    } else {
+                        st[g * D + d] = accv[g][w];
+                    }
                 }
-            }
-        if (c == 0) {
+        }
+        if (writer && c == 0) {
 #pragma unroll
             for (int g = 0; g < GT; ++g) {
-                macc[GT * D + g] = m[g];
-                macc[GT * D + GT + g] = mt[g];
-                macc[GT * D + 2 * GT + g] = l[g];
+                st[GT * D + g] = m[g];
+                st[GT * D + GT + g] = l[g];
             }
         }
     }
@@ -405,20 +480,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
     for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
         const int g = idx / D;
         const int d = idx - g * D;
-        float M = NEG_INF, Mt = NEG_INF;
+        // m of each wave is the exact running max of its scores (log2 units)
+        float M = NEG_INF;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float *ws = mrg + w * (GT * D + 3 * GT) + GT * D;
-            M = fmaxf(M, ws[g]);
-            Mt = fmaxf(Mt, ws[GT + g]);
-        }
+        for (int s = 0; s < C::NS; ++s) M = fmaxf(M, mrg[s * C::STATE_FLOATS + GT * D + g]);
         float num = 0.f, den = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float *wb = mrg + w * (GT * D + 3 * GT);
-            const float f = exp2_diff(wb[GT * D + g], M);
-            num += wb[g * D + d] * f;
-            den += wb[GT * D + 2 * GT + g] * f;
+        for (int s = 0; s < C::NS; ++s) {
+            const float *st = mrg + s * C::STATE_FLOATS;
+            const float f = exp2_diff(st[GT * D + g], M);
+            num += st[g * D + d] * f;
+            den += st[GT * D + GT + g] * f;
         }
         const float o = num / den;
         const int h = kvh * G + g;
@@ -432,28 +504,41 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
             const size_t si = ((size_t)q0 * p.hq + h) * p.max_parts + part;
             p.tmp_out[si * D + d] = o;
             if (d == 0) {
-                p.max_logits[si] = Mt;
-                p.exp_sums[si] = den * exp2_diff(M, Mt);
+                p.max_logits[si] = M;
+                p.exp_sums[si] = den;
             }
         }
     }
 }
 
+// Chunk tokens, waves per workgroup and LDS stages per wave, by K/V row bytes.
+#ifndef PA_DECODE_CT
+#define PA_DECODE_CT(R) ((R) >= 512 ? 8 : 16)
+#endif
+#ifndef PA_DECODE_NW
+#define PA_DECODE_NW(R) ((R) >= 1024 ? 2 : 4)
+#endif
+#ifndef PA_DECODE_NST
+#define PA_DECODE_NST(R) 2
+#endif
+
 template <typename T, int D, int GT>
 struct DecodeTuning {
-    // stages and waves per workgroup by row size
     static constexpr int R = D * (int)sizeof(T);
-    static constexpr int NW = R >= 1024 ? 2 : 4;
-    static constexpr int NST = 2;
+    static constexpr int CT = PA_DECODE_CT(R);
+    static constexpr int NW = PA_DECODE_NW(R);
+    static constexpr int NST = PA_DECODE_NST(R);
 };
 
 template <typename T, int D, int GT>
 hipError_t launch_t(const AttnParams &p, hipStream_t stream) {
     using Tn = DecodeTuning<T, D, GT>;
     const int parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
-    dim3 grid(parts, p.hkv, p.num_seqs);
+    dim3 grid = PA_DECODE_HEAD_FASTEST ? dim3(p.hkv, parts, p.num_seqs)
+                                       : dim3(parts, p.hkv, p.num_seqs);
     dim3 block(Tn::NW * 64);
-    hipLaunchKernelGGL((decode_kernel<T, D, GT, Tn::NW, Tn::NST>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<T, D, GT, Tn::CT, Tn::NW, Tn::NST>), grid, block, 0, stream,
+                       p);
     return hipGetLastError();
 }
 

@@ -176,7 +176,7 @@ int pa_varlen_attention(void *out, const void *q, const void *key_cache, const v
             if (!pa::decode_supported(dtype, head_dim, group)) return PA_EUNSUPPORTED;
             const int64_t parts =
                 partition_size ? ((int64_t)max_seq_len + partition_size - 1) / partition_size : 1;
-            if (parts > 0x7fffffff) return PA_EUNSUPPORTED;
+            if (parts > GRID_YZ_MAX) return PA_EUNSUPPORTED;
             return hip_status(pa::launch_decode(p, (hipStream_t)stream));
         }
         if (!pa::prefill_supported(dtype, head_dim, group)) return PA_EUNSUPPORTED;

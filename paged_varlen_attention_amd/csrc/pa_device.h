@@ -38,6 +38,15 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// The same with the three-operand encoding (v_dot2_f32_bf16): the result
+// register is not tied to the accumulator, which keeps the register allocator
+// from copying loop-carried accumulators around branches.
+__device__ __forceinline__ float dot2_untied(uint32_t a, uint32_t b, float c) {
+    float d;
+    asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+
 // v_perm_b32 byte select; s0 supplies bytes 4..7, s1 bytes 0..3.
 __device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) {
     return __builtin_amdgcn_perm(s0, s1, sel);
@@ -78,6 +87,24 @@ __device__ __forceinline__ float group_max(float x) {
     return x;
 }
 
+// Cross-row exchange (gfx950 v_permlane16_swap / v_permlane32_swap) of a value
+// with itself: returns the two values of the row pair this lane belongs to,
+// {row 2i, row 2i+1} for the 16-lane form and {row i, row i+2} for the 32-lane
+// form, in the same order in every lane of the pair.
+struct RowPair {
+    float a, b;
+};
+__device__ __forceinline__ RowPair row_pair16(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ RowPair row_pair32(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
 // ---- direct global -> LDS loads (gfx950 global_load_lds_dwordx4) ---------
 //
 // Each active lane copies 16 bytes from (sbase + voff) to LDS address
@@ -101,6 +128,7 @@ __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t
     lds = __builtin_amdgcn_readfirstlane(lds);
     asm volatile(
         "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"  // an LDS DMA reading M0 right after an SALU write needs a wait state
         "global_load_lds_dwordx4 %0, %1"
         :
         : "v"(voff), "s"(sbase), "s"(lds)
