@@ -66,11 +66,15 @@ class Step:
             kc = w.key_cache.to(device)
             vc = w.value_cache.to(device)
             self.pools.append((kc, vc))
-        self.write_cache = write_cache and w.slot_mapping is not None
+        self.write_cache = write_cache
         if self.write_cache:
-            self.new_k = w.new_key.to(device)
-            self.new_v = w.new_value.to(device)
-            self.slots = w.slot_mapping.to(device)
+            if w.slot_mapping is not None:
+                nk, nv, sm = w.new_key, w.new_value, w.slot_mapping
+            else:  # decode: the new tokens are already in the cache; write them again
+                import workloads as W
+                nk, nv, sm = W.last_token_rows(w)
+            self.new_k, self.new_v, self.slots = nk.to(device), nv.to(device), sm.to(device)
+            self.cache_write_rows = int(sm.numel())
         self.out = torch.empty_like(self.q)
         self.partials = None
         if self.P:
@@ -129,8 +133,8 @@ class Step:
 
 def step_bytes(w, include_cache_write):
     b = w.algorithmic_bytes()
-    if include_cache_write and w.slot_mapping is not None:
-        n = int((w.slot_mapping >= 0).sum())
+    if include_cache_write:
+        n = int((w.slot_mapping >= 0).sum()) if w.slot_mapping is not None else w.total_q
         b += 2 * 2 * n * w.num_kv_heads * w.head_dim * w.elt_bytes  # K and V rows, read + write
     return b
 

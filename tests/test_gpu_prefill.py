@@ -1,0 +1,83 @@
+"""GPU parity of the tiled MFMA path (prefill and mixed batches, bf16) against
+the fp64 oracle on the same seeded inputs: ragged batches over the GQA
+geometries and page sizes, every partition size, the chunked-prefill and
+speculative-verify workloads, and edge cases of the causal alignment."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import assert_close, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+GEOMS = [(32, 8, 128), (24, 4, 256), (16, 2, 128), (16, 2, 256), (4, 1, 64), (8, 8, 64),
+         (12, 4, 128), (14, 2, 64)]
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("hq,hkv,d", GEOMS, ids=[f"{a}-{b}-{c}" for a, b, c in GEOMS])
+def test_mixed_geometries(hq, hkv, d, bs):
+    """Ragged q_len 1..45 with cached prefixes 0..300 (spans several q-tiles
+    and key tiles with ragged tails), every partition size."""
+    w = W.random_case(hq * 7 + d + bs, num_seqs=6, max_q=45, max_ctx=300, num_q_heads=hq,
+                      num_kv_heads=hkv, head_dim=d, block_size=bs, dtype=torch.bfloat16)
+    ref = oracle.run_workload(w)
+    b = to_device(w)
+    for P in (0, 256, 512):
+        out = run_gpu(b, P)
+        torch.cuda.synchronize()
+        assert_close(out, ref, torch.bfloat16, f"P={P}")
+
+
+@pytest.mark.parametrize("variant", ["A", "B"])
+def test_mixed_chunked_prefill(variant):
+    """8 prompts packed to 6,000 tokens plus 8 decode tokens, 16/2/256; every row."""
+    w = W.mixed_prefill_bf16(variant=variant)
+    ref = oracle.run_workload(w)
+    b = to_device(w)
+    out = run_gpu(b, 0)
+    torch.cuda.synchronize()
+    assert_close(out, ref, torch.bfloat16, f"mixed {variant}")
+    out = run_gpu(b, 512)
+    torch.cuda.synchronize()
+    assert_close(out, ref, torch.bfloat16, f"mixed {variant} P=512")
+
+
+def test_spec_verify_with_cache_write():
+    """Verify windows of 1..5 tokens and two 512-token chunks over 1k..8k
+    contexts, 144-token blocks seen as 9x16-token pages, new K/V written by
+    pa_reshape_and_cache first; every row, unsplit and split."""
+    w = W.spec_verify_bf16()
+    ref = oracle.run_workload(w)  # oracle: cache write then attention on 144-token blocks
+    b = to_device(w)              # GPU: cache write, 9x16 view, expanded block table
+    for P in (0, 512):
+        out = run_gpu(b, P)
+        torch.cuda.synchronize()
+        assert_close(out, ref, torch.bfloat16, f"spec verify P={P}")
+
+
+def test_causal_edges():
+    """No prefix, prefix of exactly one key tile, q_len equal to the q-tile,
+    one decode token, a single key."""
+    q_lens = [16, 17, 1, 32, 5, 1, 64]
+    seq_lens = [16, 49, 1, 64, 5, 300, 64 + 31]
+    w = W.build("edges", seed=31, q_lens=q_lens, seq_lens=seq_lens, num_q_heads=16,
+                num_kv_heads=2, head_dim=128, block_size=16, num_blocks=40, dtype=torch.bfloat16)
+    ref = oracle.run_workload(w)
+    b = to_device(w)
+    for P in (0, 256):
+        out = run_gpu(b, P)
+        torch.cuda.synchronize()
+        assert_close(out, ref, torch.bfloat16, f"edges P={P}")
+
+
+def test_prefill_deterministic():
+    w = W.random_case(12, num_seqs=4, max_q=200, max_ctx=500, num_q_heads=16, num_kv_heads=2,
+                      head_dim=256, block_size=16, dtype=torch.bfloat16)
+    b = to_device(w)
+    a = run_gpu(b, 0).clone()
+    c = run_gpu(b, 0).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))

@@ -266,6 +266,24 @@ def spec_verify_bf16(seed: int = 5, lo: int = 1024, hi: int = 8192, num_blocks: 
                  description="16 req: 14 x 1-5 tok + 2 x 512 chunk, ctx U[1k,8k], 16/2/128, 144->9x16")
 
 
+def last_token_rows(w: Workload):
+    """(key, value, slot_mapping) of each request's newest token, read back
+    from the cache: writing them again with reshape_and_cache is the cache
+    write of a decode step that leaves the cache's content unchanged."""
+    cu = w.cu_seqlens_q.numpy()
+    sl = w.seq_lens.numpy().astype(np.int64)
+    bt = w.block_tables.numpy().astype(np.int64)
+    slots = []
+    for r in range(w.num_seqs):
+        for j in range(int(cu[r + 1] - cu[r])):
+            pos = int(sl[r]) - int(cu[r + 1] - cu[r]) + j
+            slots.append(bt[r, pos // w.block_size] * w.block_size + pos % w.block_size)
+    slots = torch.tensor(slots, dtype=torch.int64)
+    flat_k = w.key_cache.reshape(-1, w.num_kv_heads, w.head_dim)
+    flat_v = w.value_cache.reshape(-1, w.num_kv_heads, w.head_dim)
+    return flat_k[slots].clone(), flat_v[slots].clone(), slots
+
+
 CONFIGS = {
     "tiny_decode_f32": tiny_decode_f32,
     "gqa_decode_bf16": gqa_decode_bf16,
