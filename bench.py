@@ -11,10 +11,12 @@ split-KV partitions, and pa_split_kv_reduce.  ``value`` is the step's
 algorithmic HBM bytes (every visible KV row once per KV head, Q in, O out, the
 cache write, table ints) divided by the step's wall time.
 
-Inputs are resident in HBM before timing starts.  The step cycles over
-several identical copies of the KV pool so that no step finds the previous
-step's pages in the 256 MB last-level cache (MALL); the "warm" figure
-(one copy) is reported beside it.
+Inputs are resident in HBM before timing starts.  Each step is captured once
+as a HIP graph and the timed region replays the graphs back to back, so host
+launch overhead does not starve the GPU.  The steps cycle over several
+identical copies of the KV pool so that no step finds the previous step's
+pages in the 256 MB last-level cache (MALL); the "warm" figure (one copy) is
+reported beside it.
 
 ``roofline`` times the dominant kernel (the decode attention launch) with HIP
 events on the stream it runs on.  ``cpu_baseline`` times the fp64 oracle on
@@ -90,11 +92,14 @@ class Step:
         return (kc.view(nb * self.ratio, bs // self.ratio, hkv, d),
                 vc.view(nb * self.ratio, bs // self.ratio, hkv, d))
 
-    def __call__(self, record=False):
+    def __call__(self, record=False, pool=None):
+        """Enqueue one step on the current stream (pool: which KV-pool copy)."""
         import torch
         pa, w = self.pa, self.w
-        kc, vc = self.pools[self.i % len(self.pools)]
-        self.i += 1
+        if pool is None:
+            pool = self.i % len(self.pools)
+            self.i += 1
+        kc, vc = self.pools[pool]
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
         if record:
             ev[0].record()
@@ -118,6 +123,23 @@ class Step:
             ev[4].record()
             self.events.append(ev)
 
+    def capture(self):
+        """One HIP graph per KV-pool copy, each holding a whole step."""
+        import torch
+        for i in range(len(self.pools)):  # warm the path before capture
+            self(pool=i)
+        torch.cuda.synchronize()
+        self.graphs = []
+        for i in range(len(self.pools)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self(pool=i)
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    def replay(self, k):
+        self.graphs[k % len(self.graphs)].replay()
+
     def kernel_ms(self):
         """Mean durations (ms) of: cache write, table view, attention, reduce."""
         n = len(self.events)
@@ -139,28 +161,71 @@ def step_bytes(w, include_cache_write):
     return b
 
 
-def time_steps(step, steps, warmup, record=True):
+def time_graph_steps(step, steps, warmup):
+    """Wall time per step of `steps` graph replays, bracketed by synchronize."""
     import torch
-    for _ in range(warmup):
-        step()
+    for k in range(warmup):
+        step.replay(k)
     torch.cuda.synchronize()
-    step.events.clear()
     t0 = time.perf_counter()
-    for _ in range(steps):
-        step(record=record)
+    for k in range(steps):
+        step.replay(k)
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps
 
 
+def time_kernels(step, reps):
+    """Per-kernel durations from HIP events on the launch stream (eager launches)."""
+    import torch
+    step.events.clear()
+    for _ in range(reps):
+        step(record=True)
+    torch.cuda.synchronize()
+    return step.kernel_ms()
+
+
 def measure(w, P, steps, warmup, copies, device, write_cache=True):
     step = Step(w, P, copies, device, write_cache)
-    sec = time_steps(step, steps, warmup)
-    km = step.kernel_ms()
+    step.capture()
+    sec = time_graph_steps(step, steps, warmup)
+    km = time_kernels(step, max(10, steps // 2))
     step_warm = Step(w, P, 1, device, write_cache)
-    sec_warm = time_steps(step_warm, max(5, steps // 2), 2)
-    km_warm = step_warm.kernel_ms()
+    step_warm.capture()
+    sec_warm = time_graph_steps(step_warm, max(5, steps // 2), 2)
+    km_warm = time_kernels(step_warm, 5)
     del step, step_warm
     return sec, km, sec_warm, km_warm
+
+
+DECODE_SOURCES = ("paged_varlen_attention_amd/csrc/decode.hip",
+                  "paged_varlen_attention_amd/csrc/pa_device.h",
+                  "paged_varlen_attention_amd/csrc/pa_internal.h")
+PMC_SUMMARY = "profiles/decode_gqa_decode_bf16_pmc.md"
+
+
+def pmc_traffic():
+    """HBM bytes per launch of the decode kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary (each scaled by its copy-kernel
+    calibration), or None when the kernel sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, PMC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "|", " ")):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if kv.get("kernel_sources_sha256") != h.hexdigest():
+        return None
+    try:
+        return int(round((float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_factor"]) +
+                          float(kv["write_kib_per_dispatch"]) * float(kv["write_factor"])) * 1024))
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, budget_s=10.0):
@@ -266,7 +331,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": pmc_traffic(),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                            "copy-calibrated; null if the kernel changed since)",
             "algorithmic_bytes_per_launch": attn_bytes,
             "avg_launch_ms": round(km["attention"], 5),
         },

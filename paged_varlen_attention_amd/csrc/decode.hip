@@ -1,4 +1,6 @@
-// decode.hip -- paged GQA decode attention for gfx950 (one query token per request).
+// decode.hip -- paged GQA decode attention for gfx950: one workgroup per query
+// token (decode batches; and every token of fp32 batches, whose key range ends
+// at the token's own causal position).
 //
 // What it computes follows the vllm-metal kernel walkthrough ("What is Paged
 // Attention"; GQA decode tips 1-4): softmax(q.k * scale) v over the keys of one
@@ -276,12 +278,28 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
     // The KV heads of one partition are adjacent in the grid, so the
     // workgroups that run together read the same pages (all heads' rows of a
     // page are contiguous) rather than 1/Hkv of many different pages.
-    const int r = blockIdx.z;
     const int kvh = PA_DECODE_HEAD_FASTEST ? blockIdx.x : blockIdx.y;
     const int part = PA_DECODE_HEAD_FASTEST ? blockIdx.y : blockIdx.x;
-    const int q0 = p.cu_q[r];
-    if (p.cu_q[r + 1] - q0 <= 0) return;
-    const int seq_len = p.seq_lens[r];
+    // A workgroup serves one query token: request r's only token, or (per-token
+    // launches) packed token blockIdx.z, whose keys end at its own causal
+    // position ctx + j.
+    int r, q0, seq_len;
+    if (p.per_token) {
+        q0 = blockIdx.z;
+        int lo = 0, hi = p.num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.cu_q[mid] <= q0) lo = mid; else hi = mid - 1;
+        }
+        r = lo;
+        const int q_len = p.cu_q[r + 1] - p.cu_q[r];
+        seq_len = p.seq_lens[r] - q_len + (q0 - p.cu_q[r]) + 1;
+    } else {
+        r = blockIdx.z;
+        q0 = p.cu_q[r];
+        if (p.cu_q[r + 1] - q0 <= 0) return;
+        seq_len = p.seq_lens[r];
+    }
     const int tok_begin = p.partition ? part * p.partition : 0;
     if (tok_begin >= seq_len || seq_len <= 0) return;
     const int tok_end = p.partition ? min(seq_len, tok_begin + p.partition) : seq_len;
@@ -534,8 +552,8 @@ template <typename T, int D, int GT>
 hipError_t launch_t(const AttnParams &p, hipStream_t stream) {
     using Tn = DecodeTuning<T, D, GT>;
     const int parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
-    dim3 grid = PA_DECODE_HEAD_FASTEST ? dim3(p.hkv, parts, p.num_seqs)
-                                       : dim3(parts, p.hkv, p.num_seqs);
+    const int rows = p.per_token ? p.total_q : p.num_seqs;
+    dim3 grid = PA_DECODE_HEAD_FASTEST ? dim3(p.hkv, parts, rows) : dim3(parts, p.hkv, rows);
     dim3 block(Tn::NW * 64);
     hipLaunchKernelGGL((decode_kernel<T, D, GT, Tn::CT, Tn::NW, Tn::NST>), grid, block, 0, stream,
                        p);

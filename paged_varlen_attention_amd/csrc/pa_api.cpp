@@ -172,8 +172,13 @@ int pa_varlen_attention(void *out, const void *q, const void *key_cache, const v
         p.scale_log2 = scale * 1.44269504088896340736f;
         p.dtype = dtype;
 
-        if (max_q_len == 1) {
+        // One query token per request -> the VALU decode kernel.  fp32 batches
+        // with longer windows also use it, one workgroup per query token; bf16
+        // prefill and mixed batches go to the MFMA tiles.
+        if (max_q_len == 1 || dtype == PA_F32) {
             if (!pa::decode_supported(dtype, head_dim, group)) return PA_EUNSUPPORTED;
+            p.per_token = max_q_len > 1;
+            if (p.per_token && total_q > GRID_YZ_MAX) return PA_EUNSUPPORTED;
             const int64_t parts =
                 partition_size ? ((int64_t)max_seq_len + partition_size - 1) / partition_size : 1;
             if (parts > GRID_YZ_MAX) return PA_EUNSUPPORTED;

@@ -38,6 +38,7 @@ struct AttnParams {
     int32_t max_parts;
     float scale_log2;       // scale * log2(e)
     int32_t dtype;
+    int32_t per_token;      // decode kernel: grid z indexes query tokens, not requests
 };
 
 struct ReduceParams {

@@ -2,12 +2,13 @@
 // decode tip 4: per-partition log2-space (max, exp-sum) statistics plus the
 // normalised partial output, merged by one shared reducer).
 //
-// One workgroup per (query token, query head).  With n partitions for the
-// token's position p (n = ceil((p+1)/P)): M = max_k m_k, w_k = l_k 2^(m_k - M),
-// out = sum_k w_k o_k / sum_k w_k.  Rows with n == 1 were finalised by the
-// attention kernel and are skipped.  Partitions are spread over lane groups of
-// the workgroup (float4 per lane along D) and combined in a fixed order, so
-// the result is deterministic.
+// One workgroup per (query token, query head, 64-wide slice of D), so rows with
+// many partitions still spread over many workgroups.  With n partitions for
+// the token's position p (n = ceil((p+1)/P)): M = max_k m_k,
+// w_k = l_k 2^(m_k - M), out = sum_k w_k o_k / sum_k w_k.  Rows with n == 1
+// were finalised by the attention kernel and are skipped.  Partitions are
+// spread over 16 lane groups of the workgroup (float4 per lane along D) and
+// combined in a fixed order, so the result is deterministic.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -17,16 +18,23 @@ namespace {
 constexpr int RT = 256;      // threads per workgroup
 constexpr int WCAP = 2048;   // partition weights kept in LDS
 
+// Elements of D per workgroup: whole rows up to 128, 64-wide slices beyond.
+template <int D>
+constexpr int slice_of() { return D <= 128 ? D : 64; }
+
+// grid = (total_q, Hq, D / slice): one workgroup per (token, head, slice of D)
 template <typename T, int D>
 __global__ __launch_bounds__(RT) void reduce_kernel(const ReduceParams p) {
-    constexpr int LPG = D / 4;      // lanes per partition group (float4 each)
-    constexpr int KG = RT / LPG;    // partition groups
+    constexpr int DS = slice_of<D>();
+    constexpr int LPG = DS / 4;   // lanes per partition group (float4 each)
+    constexpr int KG = RT / LPG;  // partition groups
     __shared__ float wsh[WCAP];
     __shared__ float red[RT / 64];
     __shared__ float4 part_acc[KG][LPG];
 
     const int t = blockIdx.x;
     const int h = blockIdx.y;
+    const int d0 = blockIdx.z * DS;
     const int tid = threadIdx.x;
 
     // owner request of token t: the r with cu[r] <= t < cu[r+1]
@@ -70,14 +78,14 @@ __global__ __launch_bounds__(RT) void reduce_kernel(const ReduceParams p) {
 #pragma unroll
     for (int w = 0; w < RT / 64; ++w) W += red[w];
 
-    // sum_k w_k o_k
+    // sum_k w_k o_k over this slice, partitions spread over the groups
     const int kg = tid / LPG;
     const int d4 = tid % LPG;
-    const float4 *o = reinterpret_cast<const float4 *>(p.tmp_out + srow * D) + d4;
+    const float4 *o = reinterpret_cast<const float4 *>(p.tmp_out + srow * D + d0) + d4;
     float4 a = {0.f, 0.f, 0.f, 0.f};
     for (int k = kg; k < n; k += KG) {
         const float w = k < WCAP ? wsh[k] : es[k] * exp2_diff(ml[k], M);
-        const float4 v = o[(size_t)k * LPG];
+        const float4 v = o[(size_t)k * (D / 4)];
         a.x = fmaf(w, v.x, a.x);
         a.y = fmaf(w, v.y, a.y);
         a.z = fmaf(w, v.z, a.z);
@@ -93,7 +101,7 @@ __global__ __launch_bounds__(RT) void reduce_kernel(const ReduceParams p) {
             s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
         }
         const float inv = 1.f / W;
-        const size_t oi = ((size_t)t * p.hq + h) * D + tid * 4;
+        const size_t oi = ((size_t)t * p.hq + h) * D + d0 + tid * 4;
         if constexpr (sizeof(T) == 2) {
             uint2 pk;
             pk.x = pack_bf16(s.x * inv, s.y * inv);
@@ -108,11 +116,19 @@ __global__ __launch_bounds__(RT) void reduce_kernel(const ReduceParams p) {
 
 template <typename T>
 hipError_t launch_t(const ReduceParams &p, hipStream_t stream) {
-    dim3 grid(p.total_q, p.hq);
     switch (p.head_dim) {
-        case 64: hipLaunchKernelGGL((reduce_kernel<T, 64>), grid, dim3(RT), 0, stream, p); break;
-        case 128: hipLaunchKernelGGL((reduce_kernel<T, 128>), grid, dim3(RT), 0, stream, p); break;
-        case 256: hipLaunchKernelGGL((reduce_kernel<T, 256>), grid, dim3(RT), 0, stream, p); break;
+        case 64:
+            hipLaunchKernelGGL((reduce_kernel<T, 64>), dim3(p.total_q, p.hq, 1), dim3(RT), 0,
+                               stream, p);
+            break;
+        case 128:
+            hipLaunchKernelGGL((reduce_kernel<T, 128>), dim3(p.total_q, p.hq, 1), dim3(RT), 0,
+                               stream, p);
+            break;
+        case 256:
+            hipLaunchKernelGGL((reduce_kernel<T, 256>), dim3(p.total_q, p.hq, 256 / slice_of<256>()),
+                               dim3(RT), 0, stream, p);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

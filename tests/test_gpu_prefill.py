@@ -81,3 +81,17 @@ def test_prefill_deterministic():
     c = run_gpu(b, 0).clone()
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs", [(4, 1, 64, 16), (16, 2, 128, 8), (24, 4, 256, 32)])
+def test_mixed_fp32_per_token(hq, hkv, d, bs):
+    """fp32 batches with multi-token windows (one workgroup per query token on
+    the VALU path): max-abs 1e-5 against the oracle, every partition size."""
+    w = W.random_case(hq + d + bs + 5, num_seqs=5, max_q=12, max_ctx=700, num_q_heads=hq,
+                      num_kv_heads=hkv, head_dim=d, block_size=bs, dtype=torch.float32)
+    ref = oracle.run_workload(w)
+    b = to_device(w)
+    for P in (0, 256, 512):
+        out = run_gpu(b, P)
+        torch.cuda.synchronize()
+        assert_close(out, ref, torch.float32, f"fp32 mixed P={P}")
