@@ -26,12 +26,15 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-ffp-contract=fast", "-fno-gpu-rdc"]
+# Per-source extras.  The MFMA kernel rescales its accumulators with VALU
+# instructions, which cannot read AGPRs: keep MFMA operands in VGPRs.
+EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC] + COMMON + DEVICE + ["-c", path, "-o", obj]
+    cmd = [HIPCC] + COMMON + DEVICE + EXTRA.get(src, []) + ["-c", path, "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -10,6 +10,7 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr float LOG2E = 1.44269504088896340736f;
@@ -141,6 +142,14 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// gfx950 LDS transpose read (ds_read_b64_tr_b16).  Every lane passes the
+// address of 4 consecutive 16-bit elements; within each group of 16 lanes,
+// lane i receives element i%4 of the chunks of lanes i/4, i/4+4, i/4+8 and
+// i/4+12, in that order.  `p` must point into LDS.
+__device__ __forceinline__ s16x4_t lds_read_tr16(const void *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t *)(p));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {

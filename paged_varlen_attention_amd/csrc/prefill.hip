@@ -17,12 +17,13 @@
 //    B operand for the whole key loop, K tiles are the A operand read from LDS;
 //    a lane's accumulator column is one query row, so the softmax statistics
 //    are per lane plus one v_permlane32_swap;
-//  * O^T += V^T P^T: P^T comes straight from the S^T accumulator registers
-//    (the key order of V^T in LDS is chosen to match the accumulator layout);
-//  * K tiles move HBM -> LDS by global_load_lds_dwordx4 with an XOR swizzle of
-//    the 16-byte pieces (conflict-free A-operand reads); V is transposed in
-//    registers (v_perm_b32) into a padded V^T tile; two stages, one barrier per
-//    32-key tile;
+//  * O^T += V^T P^T: P^T comes straight from the S^T accumulator registers and
+//    the V^T A-operand fragments come from the row-major V tile through
+//    ds_read_b64_tr_b16 (gfx950's LDS transpose read), so V needs no transpose
+//    pass;
+//  * K and V tiles move HBM -> LDS by global_load_lds_dwordx4 with an XOR
+//    swizzle of the 16-byte pieces of each row (conflict-free fragment reads);
+//    NST stages, one barrier per N-key tile;
 //  * requests are mapped to workgroups without a host pass: virtual tile x
 //    belongs to the last request r with cu[r]/BQ + r <= x (surplus tiles exit).
 #include "pa_device.h"
@@ -33,39 +34,69 @@ namespace {
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
-template <int D>
+constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units
+
+template <int D, int N_, int NST_>
 struct PrefillCfg {
     static constexpr int NWV = 4;                 // waves per workgroup
-    static constexpr int N = 32;                  // keys per tile
+    static constexpr int N = N_;                  // keys per tile
+    static constexpr int NST = NST_;              // LDS stages
+    static constexpr int NB = N / 32;             // 32-key blocks of S^T per tile
     static constexpr int R = D * 2;               // bytes of a K/V row of one head
     static constexpr int KS = D / 16;             // MFMA k-steps of QK^T
     static constexpr int DB = D / 32;             // 32-row blocks of O^T
-    static constexpr int K_BYTES = N * R;
-    static constexpr int VT_STRIDE = N * 2 + 16;  // bytes per V^T row (padded)
-    static constexpr int VT_BYTES = D * VT_STRIDE;
-    static constexpr int STAGE = K_BYTES + VT_BYTES;
-    static constexpr int NI_K = K_BYTES / 1024;   // DMA instructions per K tile
-    static constexpr int NI_W = NI_K / NWV;       // per wave
-    static constexpr int RPI = 1024 / R;          // K rows per DMA instruction
+    static constexpr int T_BYTES = N * R;         // one K (or V) tile
+    static constexpr int STAGE = 2 * T_BYTES;     // K tile, then V tile
+    static constexpr int NI = T_BYTES / 1024;     // DMA instructions per tile
+    static constexpr int NI_W = NI / NWV;         // per wave, per tensor
+    static constexpr int RPI = 1024 / R;          // rows per DMA instruction
     static constexpr int PPR = R / 16;            // 16-byte pieces per row
-    static constexpr int SWZ = PPR >= 16 ? 15 : PPR - 1;
-    static constexpr int LDS_BYTES = 2 * STAGE;
-    static_assert(NI_K % NWV == 0, "K tile split over the waves");
+    // piece swizzles: K rows are read 32 rows x one piece (ds_read_b128),
+    // V rows 4 consecutive keys x two adjacent pieces (transpose reads)
+    static constexpr int SWZ_K = PPR >= 16 ? 15 : PPR - 1;
+    static constexpr int SWZ_V = PPR >= 16 ? 7 : PPR / 2 - 1;
+    static constexpr int LDS_BYTES = NST * STAGE;
+    static_assert(NI % NWV == 0, "tile split over the waves");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    static_assert(2 * NI_W * (NST - 1) < 64, "vmcnt range");
 };
 
-// Position of tile key kk (0..31) in a V^T row: the 8 keys that one lane's
-// B-operand slots of P^T hold (the S^T accumulator rows of k-step kk/16 and
-// lane half h) are made contiguous.
-__device__ __forceinline__ int vt_pos(int kk) {
-    const int ks = kk >> 4, rem = kk & 15;
-    const int a = rem >> 3, h = (rem >> 2) & 1, b = rem & 3;
-    return 16 * ks + 8 * h + 4 * a + b;
+// Slot of 16-byte piece `piece` of row `row`: K tiles XOR it with row & 15,
+// V tiles with 2*(row & 7), which keeps the 4 keys x 2 pieces that one
+// 16-lane transpose read touches on distinct banks.
+template <class C, bool V>
+__device__ __forceinline__ int swz_slot(int row, int piece) {
+    return V ? piece ^ ((row & C::SWZ_V) << 1) : piece ^ (row & C::SWZ_K);
+}
+// Byte offset of element d (a multiple of 4) of row `row` in a swizzled tile.
+template <class C, bool V>
+__device__ __forceinline__ int swz_off(int row, int d) {
+    return row * C::R + (swz_slot<C, V>(row, d >> 3) << 4) + ((d & 7) << 1);
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void prefill_kernel(const AttnParams p) {
-    using C = PrefillCfg<D>;
+// Wait until the DMA of the tile `ahead` tiles before the newest one landed.
+template <int VM, int MAXA>
+__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
+    if constexpr (MAXA > 0) {
+        if (ahead >= MAXA) {
+            wait_vmcnt<MAXA * VM>();
+            return;
+        }
+        wait_tiles_ahead<VM, MAXA - 1>(ahead);
+    } else {
+        wait_vmcnt<0>();
+    }
+}
+
+// Workgroups per CU the register budget is sized for: D = 256 keeps O^T and
+// Q^T (192 registers) resident and runs one wave per SIMD.
+#ifndef PA_PREFILL_MINW
+#define PA_PREFILL_MINW(D) ((D) >= 256 ? 1 : 2)
+#endif
+
+template <int D, int N, int NST>
+__global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const AttnParams p) {
+    using C = PrefillCfg<D, N, NST>;
     __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
@@ -74,7 +105,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const AttnParams p) {
     const int TPW = 32 / G;       // tokens per wave
     const int BQ = C::NWV * TPW;  // tokens per workgroup
 
-    // ---- which request and which q-tile (heaviest virtual tiles first) ----
+    // ---- which request and which q-tile (later virtual tiles first) ----
     const int x = gridDim.x - 1 - blockIdx.x;
     int r;
     {
@@ -107,19 +138,26 @@ __global__ __launch_bounds__(256) void prefill_kernel(const AttnParams p) {
     const int tl = min(wave * TPW + q / G, j_last - j0);  // padding rows repeat the last token
     const int hg = q % G;
     const bool row_valid = q < TPW * G && j0 + wave * TPW + q / G <= j_last;
-    const int jq = j0 + tl;          // token index within the request
-    const int pos = ctx + jq;        // absolute position: sees keys 0..pos
+    const int jq = j0 + tl;    // token index within the request
+    const int pos = ctx + jq;  // absolute position: sees keys 0..pos
     const int t_glob = q_begin + jq;
     const int head = kvh * G + hg;
 
     // Q^T B operand: 8 bf16 of d = 16*ks + 8*h .. +8 of this row, per k-step
+    // A negative scale is folded into Q (flipping bf16 sign bits is exact), so
+    // the running max can be taken on the raw scores and the scale applied
+    // inside the exponent; a zero scale becomes the smallest normal float,
+    // which leaves every visible weight exactly 1 and masked ones 0.
+    const float sl2 = fmaxf(fabsf(p.scale_log2), 1.17549435e-38f);
     bf16x8_t qb[C::KS];
     {
+        const uint32_t flip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
         const uint4 *qrow = reinterpret_cast<const uint4 *>(
             reinterpret_cast<const uint16_t *>(p.q) + ((size_t)t_glob * p.hq + head) * D);
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-            const uint4 v = qrow[2 * ks + h];
+            uint4 v = qrow[2 * ks + h];
+            v.x ^= flip; v.y ^= flip; v.z ^= flip; v.w ^= flip;
             qb[ks] = __builtin_bit_cast(bf16x8_t, v);
         }
     }
@@ -135,89 +173,43 @@ __global__ __launch_bounds__(256) void prefill_kernel(const AttnParams p) {
     };
     int win_page = k_lo >> lbs;
     int btv = load_window(win_page);
-    // physical page of logical page lp (clamped to the last page of the request)
-    auto phys_of = [&](int lp) -> int {
-        lp = min(lp, seq_pages - 1);
-        return __builtin_amdgcn_readlane(btv, lp - win_page);
-    };
 
     const uint32_t row_stride = (uint32_t)p.hkv * C::R;
     const uint64_t page_bytes = (uint64_t)bs * row_stride;
     const uint64_t head_off = (uint64_t)kvh * C::R;
     const char *kc = reinterpret_cast<const char *>(p.kc);
-    const char *vc = reinterpret_cast<const char *>(p.vc);
+    const int64_t v_minus_k = reinterpret_cast<const char *>(p.vc) - kc;
 
-    // K DMA: this wave's instructions ii = wave*NI_W + i; lane offsets with the
-    // piece swizzle (LDS slot s of row kk holds global piece s ^ (kk & SWZ))
-    uint32_t kvoff[C::NI_W];
+    // DMA: this wave moves instructions ii = wave*NI_W + i of each tile; lane
+    // offsets carry the piece swizzle (LDS slot s of row kk <- global piece
+    // s ^ (kk & SWZ)).
+    uint32_t dkoff[C::NI_W], dvoff[C::NI_W];
 #pragma unroll
     for (int i = 0; i < C::NI_W; ++i) {
         const int ii = wave * C::NI_W + i;
         const int row = ii * C::RPI + lane / C::PPR;
-        const int slot = lane % C::PPR;
-        const int piece = slot ^ (row & C::SWZ);
-        kvoff[i] = (uint32_t)(row & (bs - 1)) * row_stride + (uint32_t)piece * 16u;
+        const int slot = lane % C::PPR;  // slot s holds piece swz(s): the map is an involution
+        const uint32_t rb = (uint32_t)(row & (bs - 1)) * row_stride;
+        dkoff[i] = rb + (uint32_t)swz_slot<C, false>(row, slot) * 16u;
+        dvoff[i] = rb + (uint32_t)swz_slot<C, true>(row, slot) * 16u;
     }
     const uint32_t lds0 = lds_addr(lds);
 
-    // V load assignment: key quad kq (keys 4kq..4kq+3), 8-element d chunk dblk
-    const int vt_id = threadIdx.x;
-    const bool v_active = vt_id < D;  // (N/4) * (D/8) = D work units
-    const int kq = vt_id & 7;
-    const int dblk = vt_id >> 3;
-
-    auto issue_k = [&](int kt, int stage) {
+    auto issue = [&](int kt, int stage) {
         const int lp0 = kt >> lbs;
-        if (lp0 + ((C::N - 1) >> lbs) - win_page >= 64) {
+        if (lp0 + ((C::N - 1) >> lbs) - win_page >= 64) {  // long ranges: slide the window
             win_page = lp0;
             btv = load_window(win_page);
         }
 #pragma unroll
         for (int i = 0; i < C::NI_W; ++i) {
             const int ii = wave * C::NI_W + i;
-            const int phys = phys_of(lp0 + ((ii * C::RPI) >> lbs));
+            const int lp = min(lp0 + ((ii * C::RPI) >> lbs), seq_pages - 1);
+            const int phys = __builtin_amdgcn_readlane(btv, lp - win_page);
             const char *base = kc + (uint64_t)phys * page_bytes + head_off;
-            dma16(base, kvoff[i], lds0 + stage * C::STAGE + ii * 1024);
-        }
-    };
-    auto load_v = [&](int kt, uint4 (&vr)[4]) {
-        if (!v_active) return;
-        const int key0 = kt + 4 * kq;
-        const int lp = key0 >> lbs;
-        // the 4 keys of a quad share a page (pages hold a multiple of 4 keys)
-        const int lpc = min(lp, seq_pages - 1);
-        const int phys = __shfl(btv, lpc - win_page);
-        const char *base = vc + (uint64_t)phys * page_bytes + head_off + dblk * 16;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int off = (key0 + b) & (bs - 1);
-            vr[b] = *reinterpret_cast<const uint4 *>(base + (uint64_t)off * row_stride);
-        }
-    };
-    auto store_vt = [&](int kt, int stage, uint4 (&vr)[4]) {
-        if (!v_active) return;
-        // keys past the sequence may hold anything (NaN): zeros, since p = 0
-        // does not cancel a NaN in the MFMA
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-            if (kt + 4 * kq + b >= seq_len) vr[b] = make_uint4(0, 0, 0, 0);
-        char *vt = lds + stage * C::STAGE + C::K_BYTES;
-        const int col = vt_pos(4 * kq) * 2;
-        const uint32_t w0[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
-        const uint32_t w1[4] = {vr[1].x, vr[1].y, vr[1].z, vr[1].w};
-        const uint32_t w2[4] = {vr[2].x, vr[2].y, vr[2].z, vr[2].w};
-        const uint32_t w3[4] = {vr[3].x, vr[3].y, vr[3].z, vr[3].w};
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            // d = 8*dblk + 2w (low halves) and 2w+1 (high halves), 4 keys each
-            uint2 lo, hi;
-            lo.x = perm(w1[w], w0[w], 0x05040100u);
-            lo.y = perm(w3[w], w2[w], 0x05040100u);
-            hi.x = perm(w1[w], w0[w], 0x07060302u);
-            hi.y = perm(w3[w], w2[w], 0x07060302u);
-            const int d = 8 * dblk + 2 * w;
-            *reinterpret_cast<uint2 *>(vt + d * C::VT_STRIDE + col) = lo;
-            *reinterpret_cast<uint2 *>(vt + (d + 1) * C::VT_STRIDE + col) = hi;
+            const uint32_t l = lds0 + stage * C::STAGE + ii * 1024;
+            dma16(base, dkoff[i], l);
+            dma16(base + v_minus_k, dvoff[i], l + C::T_BYTES);
         }
     };
 
@@ -227,96 +219,123 @@ __global__ __launch_bounds__(256) void prefill_kernel(const AttnParams p) {
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int j = 0; j < 16; ++j) o[db][j] = 0.f;
-    float m = NEG_INF;  // running max of this row's scores (log2 units), shared by the lane pair
-    float l = 0.f;      // this lane's half of the exp-sum
-    const float sl2 = p.scale_log2;
+    // m: reference max of the row's scaled scores (log2 units), shared by the
+    // lane pair; it is only raised when a tile's max exceeds it by more than
+    // RESCALE_THRESHOLD, so weights stay below 2^RESCALE_THRESHOLD.
+    float m = NEG_INF;
+    float mtrue = NEG_INF;  // the true running max (split-KV statistics)
+    float l = 0.f;          // this lane's half of the exp-sum
     const int k_vis_end = min(k_hi, seq_len);  // keys past this are never visible
+    // register j of block b holds key kt + 32*b + 8*(j/4) + 4*h + (j%4); it is
+    // visible when that offset from kt + 4*h is <= lim0 - kt
+    const int lim0 = min(pos, k_vis_end - 1) - 4 * h;
+
+    // transpose-read source address pieces for the V^T fragments: within each
+    // 16-lane group, lane s points at key (s/4) of the 4-key slice and at d
+    // column 4*(s%4) of the group's 16 d values
+    const int tg = lane >> 4;               // 16-lane group
+    const int ts = lane & 15;
+    const int tr_key = 4 * h + (ts >> 2);  // + 16*k-step (+8 for the second read)
+    const int tr_d = 16 * (tg & 1) + 4 * (ts & 3);  // + 32*db
 
     const int ntiles = (k_hi - k_lo + C::N - 1) / C::N;
-    uint4 vr[4];
-    issue_k(k_lo, 0);
-    load_v(k_lo, vr);
-    wait_vmcnt<0>();
-    store_vt(k_lo, 0, vr);
-    __syncthreads();
+    constexpr int VM = 2 * C::NI_W;
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+        if (s < ntiles) issue(k_lo + s * C::N, s);
 
     for (int it = 0; it < ntiles; ++it) {
         const int kt = k_lo + it * C::N;
-        const int stage = it & 1;
-        const bool more = it + 1 < ntiles;
-        if (more) {
-            issue_k(kt + C::N, stage ^ 1);
-            load_v(kt + C::N, vr);
+        const int stage = it % NST;
+        if (it + NST - 1 < ntiles) issue(kt + (NST - 1) * C::N, (it + NST - 1) % NST);
+        wait_tiles_ahead<VM, NST - 1>(min(NST - 1, ntiles - 1 - it));
+        const char *kst = lds + stage * C::STAGE;
+        char *vst = const_cast<char *>(kst) + C::T_BYTES;
+        if (kt + C::N > seq_len) {
+            // V rows past the sequence may hold anything (NaN): zero them, since
+            // p = 0 does not cancel a NaN inside the MFMA
+            __syncthreads();
+            for (int i = threadIdx.x; i < C::N * C::PPR; i += 256) {
+                const int row = i / C::PPR;
+                if (kt + row >= seq_len)
+                    *reinterpret_cast<uint4 *>(vst + row * C::R + (i % C::PPR) * 16) =
+                        make_uint4(0, 0, 0, 0);
+            }
         }
-        const char *ks_base = lds + stage * C::STAGE;
-        const char *vt_base = ks_base + C::K_BYTES;
+        __syncthreads();  // every wave's DMA share of this tile is in
 
-        // ---- S^T = K Q^T (32 keys x 32 rows) ----
-        f32x16_t s = {};
-        {
-            const int kk = lane & 31;
-            const char *krow = ks_base + kk * C::R;
+        // ---- S^T = K Q^T, 32-key blocks ----
+        f32x16_t s[C::NB];
+#pragma unroll
+        for (int b = 0; b < C::NB; ++b) {
+            s[b] = f32x16_t{};
+            const int kk = b * 32 + (lane & 31);
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
-                const int piece = (2 * ks + h) ^ (kk & C::SWZ);
-                const uint4 a = *reinterpret_cast<const uint4 *>(krow + piece * 16);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                            qb[ks], s, 0, 0, 0);
+                const uint4 a =
+                    *reinterpret_cast<const uint4 *>(kst + swz_off<C, false>(kk, 16 * ks + 8 * h));
+                s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                               qb[ks], s[b], 0, 0, 0);
             }
         }
-        // ---- mask, online softmax ----
-        // key of accumulator register j: kt + 8*(j/4) + 4*h + (j%4)
-        const bool need_mask = kt + C::N - 1 > ctx + j0 || kt + C::N > k_vis_end;
+        // ---- mask (boundary tiles only), online softmax on raw scores ----
+        if (kt + C::N - 1 > ctx + j0 || kt + C::N > k_vis_end) {
+            const int lim = lim0 - kt;
+#pragma unroll
+            for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    if (32 * b + 8 * (j >> 2) + (j & 3) > lim) s[b][j] = NEG_INF;
+        }
         float mx = NEG_INF;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            float v = s[j] * sl2;
-            if (need_mask) {
-                const int key = kt + 8 * (j >> 2) + 4 * h + (j & 3);
-                v = (key <= pos && key < k_vis_end) ? v : NEG_INF;
-            }
-            s[j] = v;
-            mx = fmaxf(mx, v);
-        }
+        for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[b][j]);
         {
             const RowPair pm = row_pair32(mx);
-            mx = fmaxf(pm.a, pm.b);
+            mx = fmaxf(pm.a, pm.b) * sl2;
         }
-        const float mn = fmaxf(m, mx);
-        const float alpha = exp2_diff(m, mn);
-        m = mn;
-        l *= alpha;
+        mtrue = fmaxf(mtrue, mx);
+        if (__builtin_amdgcn_ballot_w64(mx > m + RESCALE_THRESHOLD)) {
+            const bool up = mx > m + RESCALE_THRESHOLD;
+            const float alpha = up ? __builtin_amdgcn_exp2f(m - mx) : 1.f;
+            m = up ? mx : m;
+            l *= alpha;
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
+            for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
-        uint32_t pk[8];
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) {
-            const float p0 = exp2_diff(s[j], m);
-            const float p1 = exp2_diff(s[j + 1], m);
-            pk[j / 2] = pack_bf16(p0, p1);
-            l += bf16lo(pk[j / 2]) + bf16hi(pk[j / 2]);  // the weights actually applied
+                for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
         }
-        // ---- O^T += V^T P^T ----
+        const float msub = m == NEG_INF ? 0.f : m;  // rows with no visible key yet
+        // ---- per 32-key block: P (bf16), then O^T += V^T P^T over its two k-steps ----
 #pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2) {
-            u32x4_t pb = {pk[4 * ks2], pk[4 * ks2 + 1], pk[4 * ks2 + 2], pk[4 * ks2 + 3]};
-            const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, pb);
+        for (int b = 0; b < C::NB; ++b) {
+            uint32_t pk[8];
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
-                const int d = db * 32 + (lane & 31);
-                const uint4 a = *reinterpret_cast<const uint4 *>(vt_base + d * C::VT_STRIDE +
-                                                                 (16 * ks2 + 8 * h) * 2);
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                                bop, o[db], 0, 0, 0);
+            for (int j = 0; j < 16; j += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[b][j], sl2, -msub));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[b][j + 1], sl2, -msub));
+                pk[j / 2] = pack_bf16(p0, p1);
+                l = dot2(pk[j / 2], 0x3F803F80u, l);  // sums the bf16 weights actually applied
+            }
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2) {
+                u32x4_t pb = {pk[4 * ks2], pk[4 * ks2 + 1], pk[4 * ks2 + 2], pk[4 * ks2 + 3]};
+                const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, pb);
+                const int key1 = 32 * b + 16 * ks2 + tr_key;  // keys of slots 0..3
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db) {
+                    const int d = 32 * db + tr_d;
+                    const s16x4_t lo = lds_read_tr16(vst + swz_off<C, true>(key1, d));
+                    const s16x4_t hi = lds_read_tr16(vst + swz_off<C, true>(key1 + 8, d));
+                    const s16x4_t av[2] = {lo, hi};
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8_t, av), bop, o[db], 0, 0, 0);
+                }
             }
         }
-        if (more) {
-            wait_vmcnt<0>();          // the next K tile's DMA and V rows are in
-            store_vt(kt + C::N, stage ^ 1, vr);
-        }
-        __syncthreads();
+        __syncthreads();  // everyone is done with this stage before it is refilled
     }
 
     // ---- finish: full exp-sum of the row, normalise, store ----
@@ -353,19 +372,29 @@ __global__ __launch_bounds__(256) void prefill_kernel(const AttnParams p) {
                 *reinterpret_cast<float4 *>(orow + d) = w;
             }
         if (h == 0) {
-            p.max_logits[si] = m;
-            p.exp_sums[si] = l;
+            p.max_logits[si] = mtrue;
+            p.exp_sums[si] = l * __builtin_amdgcn_exp2f(m - mtrue);
         }
     }
 }
 
+// Keys per tile and LDS stages by head size.
+#ifndef PA_PREFILL_N
+#define PA_PREFILL_N(D) ((D) >= 256 ? 32 : 64)
+#endif
+#ifndef PA_PREFILL_NST
+#define PA_PREFILL_NST(D) 2
+#endif
+
 template <int D>
 hipError_t launch_d(const AttnParams &p, hipStream_t stream) {
+    constexpr int N = PA_PREFILL_N(D), NST = PA_PREFILL_NST(D);
     const int TPW = 32 / p.group;
-    const int BQ = PrefillCfg<D>::NWV * TPW;
+    const int BQ = PrefillCfg<D, N, NST>::NWV * TPW;
     const int tiles = p.total_q / BQ + p.num_seqs;
     const int parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
-    hipLaunchKernelGGL((prefill_kernel<D>), dim3(tiles, p.hkv, parts), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<D, N, NST>), dim3(tiles, p.hkv, parts), dim3(256), 0,
+                       stream, p);
     return hipGetLastError();
 }
 

@@ -2,6 +2,8 @@
 the fp64 oracle on the same seeded inputs: ragged batches over the GQA
 geometries and page sizes, every partition size, the chunked-prefill and
 speculative-verify workloads, and edge cases of the causal alignment."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -95,3 +97,21 @@ def test_mixed_fp32_per_token(hq, hkv, d, bs):
         out = run_gpu(b, P)
         torch.cuda.synchronize()
         assert_close(out, ref, torch.float32, f"fp32 mixed P={P}")
+
+
+@pytest.mark.parametrize("scale", [-0.11, 0.0, 0.9])
+def test_scale_values(scale):
+    """A negative scale, a zero scale (uniform weights over the visible keys)
+    and a large one (scores spread over tens of log2 units, so the running max
+    jumps far between tiles), on the MFMA path (multi-token windows) and the
+    VALU decode path, unsplit and split."""
+    for max_q, seed in ((40, 51), (1, 52)):
+        w = W.random_case(seed, num_seqs=5, max_q=max_q, max_ctx=700, num_q_heads=16,
+                          num_kv_heads=2, head_dim=128, block_size=16, dtype=torch.bfloat16)
+        w = dataclasses.replace(w, scale=scale)
+        ref = oracle.run_workload(w)
+        b = to_device(w)
+        for P in (0, 256):
+            out = run_gpu(b, P)
+            torch.cuda.synchronize()
+            assert_close(out, ref, torch.bfloat16, f"scale={scale} max_q={max_q} P={P}")
