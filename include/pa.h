@@ -10,7 +10,8 @@
  *     (kernel walkthrough, "What is Paged Attention"), grouped-query heads
  *     (kernel walkthrough, GQA decode section), causal masking of each
  *     request's new tokens against its cached prefix;
- *   - split-KV: long key ranges cut into 256- or 512-token partitions whose
+ *   - split-KV: long key ranges cut into partitions (256 or 512 tokens in the
+ *     pages, any multiple of 256 here) whose
  *     log2-space (max, exp-sum) statistics and normalised partial outputs are
  *     merged by a separate reduce (kernel walkthrough, GQA decode tip 4);
  *   - the block-size view: a large cache block seen as several kernel pages
@@ -74,6 +75,7 @@ enum {
 /* Limits of this build. */
 #define PA_MAX_GROUP 8          /* num_q_heads / num_kv_heads */
 #define PA_MAX_SEQS 65535       /* requests per call */
+#define PA_MAX_PARTITION 8192  /* largest partition_size accepted */
 #define PA_SPLIT_WG_PER_CU 2    /* workgroups per CU the partition policy aims for */
 
 /*
@@ -120,7 +122,9 @@ int pa_expand_block_tables(int32_t *dst, const int32_t *src, int32_t num_seqs, i
  * of any mix of requests.
  *
  * partition_size = 0: no split; `out` receives every row.
- * partition_size = P in {256, 512}: the keys of a row at position p are cut
+ * partition_size = P, a multiple of 256 up to PA_MAX_PARTITION (the pages use
+ *   256 and 512; larger ones bound the work of one workgroup on long prefill
+ *   rows): the keys of a row at position p are cut
  *   into n = ceil((p + 1) / P) partitions [kP, min((k+1)P, p+1)).
  *   Rows with n == 1 are written straight to `out`.  For rows with n >= 2,
  *   partition k < n writes

@@ -29,10 +29,13 @@ int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_EHIP; }
 // Grid dimensions y and z are limited to 65535 workgroups.
 constexpr int32_t GRID_YZ_MAX = 65535;
 
+// Partition sizes: multiples of 256 keys up to PA_MAX_PARTITION.
+bool partition_ok(int32_t P) { return P > 0 && P % 256 == 0 && P <= PA_MAX_PARTITION; }
+
 int check_partitions(int32_t partition_size, int32_t max_seq_len, const float *tmp_out,
                      const float *max_logits, const float *exp_sums, int32_t max_partitions) {
     if (partition_size == 0) return PA_OK;
-    if (partition_size != 256 && partition_size != 512) return PA_EUNSUPPORTED;
+    if (!partition_ok(partition_size)) return PA_EUNSUPPORTED;
     if (!tmp_out || !max_logits || !exp_sums) return PA_EWORKSPACE;
     if (!aligned16(tmp_out)) return PA_EINVAL;
     const int64_t need = ((int64_t)max_seq_len + partition_size - 1) / partition_size;
@@ -44,7 +47,7 @@ int check_partitions(int32_t partition_size, int32_t max_seq_len, const float *t
 
 extern "C" {
 
-int pa_abi_version(void) { return 100; }
+int pa_abi_version(void) { return 101; }
 
 const char *pa_status_string(int status) {
     switch (status) {
@@ -129,8 +132,7 @@ int pa_varlen_attention(void *out, const void *q, const void *key_cache, const v
         if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PA_EUNSUPPORTED;
         const int lbs = log2_exact(block_size);
         if (block_size < 8 || block_size > 32 || lbs < 0) return PA_EUNSUPPORTED;
-        if (partition_size != 0 && partition_size != 256 && partition_size != 512)
-            return PA_EUNSUPPORTED;
+        if (partition_size != 0 && !partition_ok(partition_size)) return PA_EUNSUPPORTED;
         if (total_q == 0 || num_seqs == 0) return PA_OK;
         if (num_seqs > GRID_YZ_MAX || num_kv_heads > GRID_YZ_MAX) return PA_EUNSUPPORTED;
         if (max_q_len < 1 || max_seq_len < max_q_len) return PA_EINVAL;
@@ -200,7 +202,7 @@ int pa_split_kv_reduce(void *out, const float *tmp_out, const float *max_logits,
         if (!elt_bytes(dtype)) return PA_EUNSUPPORTED;
         if (num_seqs < 0 || total_q < 0 || num_q_heads <= 0 || head_dim <= 0) return PA_EINVAL;
         if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PA_EUNSUPPORTED;
-        if (partition_size != 256 && partition_size != 512) return PA_EUNSUPPORTED;
+        if (!partition_ok(partition_size)) return PA_EUNSUPPORTED;
         if (total_q == 0 || num_seqs == 0) return PA_OK;
         if (num_q_heads > GRID_YZ_MAX) return PA_EUNSUPPORTED;
         if (!out || !cu_seqlens_q || !seq_lens) return PA_EINVAL;

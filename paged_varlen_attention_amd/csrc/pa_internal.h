@@ -39,6 +39,8 @@ struct AttnParams {
     float scale_log2;       // scale * log2(e)
     int32_t dtype;
     int32_t per_token;      // decode kernel: grid z indexes query tokens, not requests
+    int32_t grid_tiles;     // tiled kernel: virtual q-tiles (set by its launcher)
+    int32_t grid_parts;     // tiled kernel: partitions in the grid (set by its launcher)
 };
 
 struct ReduceParams {

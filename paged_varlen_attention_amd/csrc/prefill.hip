@@ -47,31 +47,34 @@ struct PrefillCfg {
     static constexpr int DB = D / 32;             // 32-row blocks of O^T
     static constexpr int T_BYTES = N * R;         // one K (or V) tile
     static constexpr int STAGE = 2 * T_BYTES;     // K tile, then V tile
+    static constexpr int PPR = R / 16;            // 16-byte pieces per row
+    static constexpr int KG = 8;                  // keys per group in the tile layout
+    static constexpr int GROUP_BYTES = KG * R;    // one key group: PPR pieces x KG keys
+    static constexpr int IPG = GROUP_BYTES / 1024;  // DMA instructions per key group
     static constexpr int NI = T_BYTES / 1024;     // DMA instructions per tile
     static constexpr int NI_W = NI / NWV;         // per wave, per tensor
-    static constexpr int RPI = 1024 / R;          // rows per DMA instruction
-    static constexpr int PPR = R / 16;            // 16-byte pieces per row
-    // piece swizzles: K rows are read 32 rows x one piece (ds_read_b128),
-    // V rows 4 consecutive keys x two adjacent pieces (transpose reads)
-    static constexpr int SWZ_K = PPR >= 16 ? 15 : PPR - 1;
-    static constexpr int SWZ_V = PPR >= 16 ? 7 : PPR / 2 - 1;
     static constexpr int LDS_BYTES = NST * STAGE;
     static_assert(NI % NWV == 0, "tile split over the waves");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
     static_assert(2 * NI_W * (NST - 1) < 64, "vmcnt range");
 };
 
-// Slot of 16-byte piece `piece` of row `row`: K tiles XOR it with row & 15,
-// V tiles with 2*(row & 7), which keeps the 4 keys x 2 pieces that one
-// 16-lane transpose read touches on distinct banks.
-template <class C, bool V>
-__device__ __forceinline__ int swz_slot(int row, int piece) {
-    return V ? piece ^ ((row & C::SWZ_V) << 1) : piece ^ (row & C::SWZ_K);
-}
-// Byte offset of element d (a multiple of 4) of row `row` in a swizzled tile.
-template <class C, bool V>
-__device__ __forceinline__ int swz_off(int row, int d) {
-    return row * C::R + (swz_slot<C, V>(row, d >> 3) << 4) + ((d & 7) << 1);
+// Tile layout in LDS (K and V alike).  Keys come in groups of KG = 8; a
+// group stores piece-major: piece p (16 bytes: elements 8p..8p+7) of its 8
+// keys is one 128-byte line, and on odd pieces the key slot is XORed with 4:
+//   off(key, p) = (key / 8) * 8R + p * 128 + ((key % 8) ^ 4 (p & 1)) * 16.
+// * S^T A operand (ds_read_b128): 8 consecutive lanes read 8 keys of one
+//   piece -- one line, all banks -- and a lane's address changes with the
+//   k-step only by an immediate.
+// * V^T A operand (ds_read_b64_tr_b16): a 16-lane group reads 4 keys x 2
+//   adjacent pieces; the XOR puts the two pieces on opposite 64-byte halves.
+// * DMA: one global_load_lds_dwordx4 fills 1 KB = 8 pieces of one key group
+//   with 128 contiguous bytes of each key row (one 8-key group never spans
+//   two pages since pages hold a multiple of 8 keys), and a lane's source
+//   offset inside the page is the same for every instruction.
+template <class C>
+__device__ __forceinline__ int tile_off(int key, int piece) {
+    return (key >> 3) * C::GROUP_BYTES + piece * 128 + (((key & 7) ^ ((piece & 1) << 2)) << 4);
 }
 
 // Wait until the DMA of the tile `ahead` tiles before the newest one landed.
@@ -88,15 +91,32 @@ __device__ __forceinline__ void wait_tiles_ahead(int ahead) {
     }
 }
 
-// Workgroups per CU the register budget is sized for: D = 256 keeps O^T and
-// Q^T (192 registers) resident and runs one wave per SIMD.
+// Workgroups per CU the register budget is sized for (2: at most 256
+// registers a lane; D = 256 keeps 192 of them for O^T and Q^T).
 #ifndef PA_PREFILL_MINW
-#define PA_PREFILL_MINW(D) ((D) >= 256 ? 1 : 2)
+#define PA_PREFILL_MINW(D) 2
 #endif
+
+// LDS fragment reads in flight ahead of their MFMA (K for S^T, V^T for O^T).
+#ifndef PA_PREFILL_PF_K
+#define PA_PREFILL_PF_K(D) ((D) >= 256 ? 2 : 4)
+#endif
+#ifndef PA_PREFILL_PF_V
+#define PA_PREFILL_PF_V(D) ((D) >= 256 ? 2 : 4)
+#endif
+#ifndef PA_PREFILL_XCD_CHUNK
+#define PA_PREFILL_XCD_CHUNK 8
+#endif
+constexpr int XCD_CHUNK = PA_PREFILL_XCD_CHUNK;
+#ifndef PA_PREFILL_SCHED
+#define PA_PREFILL_SCHED 1
+#endif
+constexpr bool PF_SCHED = PA_PREFILL_SCHED;
 
 template <int D, int N, int NST>
 __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const AttnParams p) {
     using C = PrefillCfg<D, N, NST>;
+    constexpr int PF_K = PA_PREFILL_PF_K(D), PF_V = PA_PREFILL_PF_V(D);
     __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
@@ -106,7 +126,20 @@ __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const 
     const int BQ = C::NWV * TPW;  // tokens per workgroup
 
     // ---- which request and which q-tile (later virtual tiles first) ----
-    const int x = gridDim.x - 1 - blockIdx.x;
+    // ---- XCD-aware order.  Workgroups go to the 8 XCDs round-robin by launch
+    // index L; groups of XCD_CHUNK consecutive work items (q-tiles of one
+    // request and KV head, which read the same keys) are kept on one XCD so
+    // its L2 serves the repeats.  Work items are taken last-first: later
+    // q-tiles of a request see more keys.
+    const int n_items = p.grid_tiles * p.hkv * p.grid_parts;
+    int lam = blockIdx.x;
+    if (XCD_CHUNK > 0) {
+        const int xcd = lam & 7, slot = lam >> 3;
+        lam = ((slot / XCD_CHUNK) * 8 + xcd) * XCD_CHUNK + slot % XCD_CHUNK;
+    }
+    if (lam >= n_items) return;
+    lam = n_items - 1 - lam;
+    const int x = lam % p.grid_tiles;
     int r;
     {
         int lo = 0, hi = p.num_seqs - 1;
@@ -123,8 +156,8 @@ __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const 
     if (tile < 0 || j0 >= q_len) return;
     const int seq_len = p.seq_lens[r];
     const int ctx = seq_len - q_len;
-    const int kvh = blockIdx.y;
-    const int part = blockIdx.z;
+    const int kvh = (lam / p.grid_tiles) % p.hkv;
+    const int part = lam / (p.grid_tiles * p.hkv);
     const int j_last = min(q_len, j0 + BQ) - 1;
     // keys of this workgroup: the partition, cut at the last token's position
     const int k_lo = p.partition ? part * p.partition : 0;
@@ -180,19 +213,12 @@ __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const 
     const char *kc = reinterpret_cast<const char *>(p.kc);
     const int64_t v_minus_k = reinterpret_cast<const char *>(p.vc) - kc;
 
-    // DMA: this wave moves instructions ii = wave*NI_W + i of each tile; lane
-    // offsets carry the piece swizzle (LDS slot s of row kk <- global piece
-    // s ^ (kk & SWZ)).
-    uint32_t dkoff[C::NI_W], dvoff[C::NI_W];
-#pragma unroll
-    for (int i = 0; i < C::NI_W; ++i) {
-        const int ii = wave * C::NI_W + i;
-        const int row = ii * C::RPI + lane / C::PPR;
-        const int slot = lane % C::PPR;  // slot s holds piece swz(s): the map is an involution
-        const uint32_t rb = (uint32_t)(row & (bs - 1)) * row_stride;
-        dkoff[i] = rb + (uint32_t)swz_slot<C, false>(row, slot) * 16u;
-        dvoff[i] = rb + (uint32_t)swz_slot<C, true>(row, slot) * 16u;
-    }
+    // DMA: this wave moves instructions c = wave*NI_W + i of each tile.
+    // Instruction c covers key group c / IPG, pieces 8*(c % IPG) .. +7; lane l
+    // brings piece 8*(c % IPG) + l/8 of key slot l%8 (its key is the slot
+    // XORed back, which is the same involution).
+    const uint32_t dma_voff =
+        (uint32_t)((lane & 7) ^ (((lane >> 3) & 1) << 2)) * row_stride + (uint32_t)(lane >> 3) * 16u;
     const uint32_t lds0 = lds_addr(lds);
 
     auto issue = [&](int kt, int stage) {
@@ -203,13 +229,15 @@ __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const 
         }
 #pragma unroll
         for (int i = 0; i < C::NI_W; ++i) {
-            const int ii = wave * C::NI_W + i;
-            const int lp = min(lp0 + ((ii * C::RPI) >> lbs), seq_pages - 1);
+            const int c = wave * C::NI_W + i;
+            const int k8 = kt + C::KG * (c / C::IPG);  // first key of the group
+            const int lp = min(k8 >> lbs, seq_pages - 1);
             const int phys = __builtin_amdgcn_readlane(btv, lp - win_page);
-            const char *base = kc + (uint64_t)phys * page_bytes + head_off;
-            const uint32_t l = lds0 + stage * C::STAGE + ii * 1024;
-            dma16(base, dkoff[i], l);
-            dma16(base + v_minus_k, dvoff[i], l + C::T_BYTES);
+            const char *base = kc + (uint64_t)phys * page_bytes + head_off +
+                               (uint32_t)(k8 & (bs - 1)) * row_stride + 128 * (c % C::IPG);
+            const uint32_t l = lds0 + stage * C::STAGE + c * 1024;
+            dma16(base, dma_voff, l);
+            dma16(base + v_minus_k, dma_voff, l + C::T_BYTES);
         }
     };
 
@@ -230,13 +258,17 @@ __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const 
     // visible when that offset from kt + 4*h is <= lim0 - kt
     const int lim0 = min(pos, k_vis_end - 1) - 4 * h;
 
-    // transpose-read source address pieces for the V^T fragments: within each
-    // 16-lane group, lane s points at key (s/4) of the 4-key slice and at d
-    // column 4*(s%4) of the group's 16 d values
-    const int tg = lane >> 4;               // 16-lane group
+    // Per-lane LDS bases; everything else in a fragment address is an
+    // immediate.  K: lane reads key 32b + (lane&31), piece 2ks + h.  V^T: in
+    // each 16-lane group, lane s points at key 4h + s/4 (+ 8 for the second
+    // read, + 16 per k-step, + 32 per block) and at d = 32db + 16*(group&1)
+    // + 4*(s%4), i.e. piece 4db + 2*(group&1) + (s/2)%2, byte 8*(s%2).
+    const int tg = lane >> 4;
     const int ts = lane & 15;
-    const int tr_key = 4 * h + (ts >> 2);  // + 16*k-step (+8 for the second read)
-    const int tr_d = 16 * (tg & 1) + 4 * (ts & 3);  // + 32*db
+    const int k_base = ((lane & 31) >> 3) * C::GROUP_BYTES + h * 128 + (((lane & 7) ^ (h << 2)) << 4);
+    const int v_pb = (ts >> 1) & 1;
+    const int v_base = (2 * (tg & 1) + v_pb) * 128 + (((4 * h + (ts >> 2)) ^ (v_pb << 2)) << 4) +
+                       8 * (ts & 1);
 
     const int ntiles = (k_hi - k_lo + C::N - 1) / C::N;
     constexpr int VM = 2 * C::NI_W;
@@ -258,24 +290,34 @@ __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const 
             for (int i = threadIdx.x; i < C::N * C::PPR; i += 256) {
                 const int row = i / C::PPR;
                 if (kt + row >= seq_len)
-                    *reinterpret_cast<uint4 *>(vst + row * C::R + (i % C::PPR) * 16) =
+                    *reinterpret_cast<uint4 *>(vst + tile_off<C>(row, i % C::PPR)) =
                         make_uint4(0, 0, 0, 0);
             }
         }
         __syncthreads();  // every wave's DMA share of this tile is in
 
         // ---- S^T = K Q^T, 32-key blocks ----
+        // K fragments are streamed PF_K reads ahead of their MFMA (the
+        // scheduling barriers keep the compiler from hoisting all of them,
+        // which would cost registers the occupancy target does not have)
         f32x16_t s[C::NB];
 #pragma unroll
         for (int b = 0; b < C::NB; ++b) {
             s[b] = f32x16_t{};
-            const int kk = b * 32 + (lane & 31);
+            auto kread = [&](int ks) {
+                return *reinterpret_cast<const uint4 *>(kst + k_base + b * 4 * C::GROUP_BYTES +
+                                                        ks * 256);
+            };
+            uint4 ka[PF_K];
+#pragma unroll
+            for (int ks = 0; ks < PF_K; ++ks) ka[ks] = kread(ks);
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
-                const uint4 a =
-                    *reinterpret_cast<const uint4 *>(kst + swz_off<C, false>(kk, 16 * ks + 8 * h));
+                const uint4 a = ka[ks % PF_K];
+                if (ks + PF_K < C::KS) ka[ks % PF_K] = kread(ks + PF_K);
                 s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                                qb[ks], s[b], 0, 0, 0);
+                if (PF_SCHED) __builtin_amdgcn_sched_barrier(0);
             }
         }
         // ---- mask (boundary tiles only), online softmax on raw scores ----
@@ -319,20 +361,27 @@ __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const 
                 pk[j / 2] = pack_bf16(p0, p1);
                 l = dot2(pk[j / 2], 0x3F803F80u, l);  // sums the bf16 weights actually applied
             }
+            // V^T fragments, streamed PF_V MFMAs ahead; MFMA i = (ks2, db)
+            auto vread = [&](int i) {
+                const char *a = vst + v_base + (4 * b + 2 * (i / C::DB)) * C::GROUP_BYTES +
+                                (i % C::DB) * 512;
+                const s16x4_t lo = lds_read_tr16(a);
+                const s16x4_t hi = lds_read_tr16(a + C::GROUP_BYTES);
+                const s16x4_t av[2] = {lo, hi};
+                return __builtin_bit_cast(bf16x8_t, av);
+            };
+            bf16x8_t va[PF_V];
 #pragma unroll
-            for (int ks2 = 0; ks2 < 2; ++ks2) {
+            for (int i = 0; i < PF_V; ++i) va[i] = vread(i);
+#pragma unroll
+            for (int i = 0; i < 2 * C::DB; ++i) {
+                const int ks2 = i / C::DB, db = i % C::DB;
                 u32x4_t pb = {pk[4 * ks2], pk[4 * ks2 + 1], pk[4 * ks2 + 2], pk[4 * ks2 + 3]};
-                const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, pb);
-                const int key1 = 32 * b + 16 * ks2 + tr_key;  // keys of slots 0..3
-#pragma unroll
-                for (int db = 0; db < C::DB; ++db) {
-                    const int d = 32 * db + tr_d;
-                    const s16x4_t lo = lds_read_tr16(vst + swz_off<C, true>(key1, d));
-                    const s16x4_t hi = lds_read_tr16(vst + swz_off<C, true>(key1 + 8, d));
-                    const s16x4_t av[2] = {lo, hi};
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8_t, av), bop, o[db], 0, 0, 0);
-                }
+                const bf16x8_t a = va[i % PF_V];
+                if (i + PF_V < 2 * C::DB) va[i % PF_V] = vread(i + PF_V);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, pb),
+                                                                o[db], 0, 0, 0);
+                if (PF_SCHED) __builtin_amdgcn_sched_barrier(0);
             }
         }
         __syncthreads();  // everyone is done with this stage before it is refilled
@@ -391,10 +440,14 @@ hipError_t launch_d(const AttnParams &p, hipStream_t stream) {
     constexpr int N = PA_PREFILL_N(D), NST = PA_PREFILL_NST(D);
     const int TPW = 32 / p.group;
     const int BQ = PrefillCfg<D, N, NST>::NWV * TPW;
-    const int tiles = p.total_q / BQ + p.num_seqs;
-    const int parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
-    hipLaunchKernelGGL((prefill_kernel<D, N, NST>), dim3(tiles, p.hkv, parts), dim3(256), 0,
-                       stream, p);
+    AttnParams q = p;
+    q.grid_tiles = p.total_q / BQ + p.num_seqs;
+    q.grid_parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
+    const int64_t items = (int64_t)q.grid_tiles * p.hkv * q.grid_parts;
+    if (items > INT32_MAX - 4096) return hipErrorInvalidConfiguration;
+    const int64_t unit = XCD_CHUNK > 0 ? 8 * XCD_CHUNK : 1;
+    const int blocks = (int)((items + unit - 1) / unit * unit);
+    hipLaunchKernelGGL((prefill_kernel<D, N, NST>), dim3(blocks), dim3(256), 0, stream, q);
     return hipGetLastError();
 }
 

@@ -2,13 +2,15 @@
 // decode tip 4: per-partition log2-space (max, exp-sum) statistics plus the
 // normalised partial output, merged by one shared reducer).
 //
-// One workgroup per (query token, query head, 64-wide slice of D), so rows with
-// many partitions still spread over many workgroups.  With n partitions for
-// the token's position p (n = ceil((p+1)/P)): M = max_k m_k,
-// w_k = l_k 2^(m_k - M), out = sum_k w_k o_k / sum_k w_k.  Rows with n == 1
-// were finalised by the attention kernel and are skipped.  Partitions are
-// spread over 16 lane groups of the workgroup (float4 per lane along D) and
-// combined in a fixed order, so the result is deterministic.
+// With n partitions for the token's position p (n = ceil((p+1)/P)):
+// M = max_k m_k, w_k = l_k 2^(m_k - M), out = sum_k w_k o_k / sum_k w_k.
+// Rows with n == 1 were finalised by the attention kernel and are skipped.
+// Two launch shapes, both summing in a fixed order (deterministic):
+//  * up to 64 partitions (every prefill or mixed batch, decode up to 64*P
+//    keys): one wave per (token, head) row, four rows per workgroup;
+//  * more partitions (long decode): one workgroup per (token, head, 64-wide
+//    slice of D), partitions spread over 16 lane groups (float4 per lane along
+//    D), so a few very long rows still spread over many workgroups.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -114,8 +116,93 @@ __global__ __launch_bounds__(RT) void reduce_kernel(const ReduceParams p) {
     }
 }
 
+// One wave per (token, head) row, four rows per workgroup: for batches with
+// many rows and at most 64 partitions per row (prefill and mixed batches),
+// where a workgroup per row would be mostly launch overhead.  Lane k holds
+// partition k's statistics; the partials are then accumulated in partition
+// order, each lane owning D/64 consecutive elements of the row.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void reduce_rows_kernel(const ReduceParams p) {
+    constexpr int E = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // t * Hq + h
+    if (row >= p.total_q * p.hq) return;
+    const int t = row / p.hq;
+    int lo = 0, hi = p.num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.cu_q[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int q_len = p.cu_q[lo + 1] - p.cu_q[lo];
+    const int pos = p.seq_lens[lo] - q_len + (t - p.cu_q[lo]);
+    const int n = pos / p.partition + 1;
+    if (n <= 1 || n > p.max_parts || pos < 0) return;
+
+    const size_t srow = (size_t)row * p.max_parts;
+    const float m = lane < n ? p.max_logits[srow + lane] : NEG_INF;
+    const float M = group_max<64>(m);
+    const float w = lane < n ? p.exp_sums[srow + lane] * exp2_diff(m, M) : 0.f;
+    const float W = group_sum<64>(w);
+
+    const float *o = p.tmp_out + srow * D + lane * E;
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    for (int k = 0; k < n; ++k) {
+        const float wk =
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
+        float v[E];
+        if constexpr (E == 4) {
+            const float4 x = *reinterpret_cast<const float4 *>(o + (size_t)k * D);
+            v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        } else if constexpr (E == 2) {
+            const float2 x = *reinterpret_cast<const float2 *>(o + (size_t)k * D);
+            v[0] = x.x; v[1] = x.y;
+        } else {
+            v[0] = o[(size_t)k * D];
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = fmaf(wk, v[e], acc[e]);
+    }
+    const float inv = 1.f / W;
+    const size_t oi = (size_t)row * D + lane * E;
+    if constexpr (sizeof(T) == 2) {
+        uint16_t *out = reinterpret_cast<uint16_t *>(p.out) + oi;
+        if constexpr (E == 4) {
+            uint2 pk;
+            pk.x = pack_bf16(acc[0] * inv, acc[1] * inv);
+            pk.y = pack_bf16(acc[2] * inv, acc[3] * inv);
+            *reinterpret_cast<uint2 *>(out) = pk;
+        } else if constexpr (E == 2) {
+            *reinterpret_cast<uint32_t *>(out) = pack_bf16(acc[0] * inv, acc[1] * inv);
+        } else {
+            *out = (uint16_t)(pack_bf16(acc[0] * inv, 0.f) & 0xFFFFu);
+        }
+    } else {
+        float *out = reinterpret_cast<float *>(p.out) + oi;
+#pragma unroll
+        for (int e = 0; e < E; ++e) out[e] = acc[e] * inv;
+    }
+}
+
 template <typename T>
 hipError_t launch_t(const ReduceParams &p, hipStream_t stream) {
+    if (p.max_parts <= 64) {
+        const int blocks = (int)(((int64_t)p.total_q * p.hq + 3) / 4);
+        switch (p.head_dim) {
+            case 64:
+                hipLaunchKernelGGL((reduce_rows_kernel<T, 64>), dim3(blocks), dim3(256), 0, stream, p);
+                break;
+            case 128:
+                hipLaunchKernelGGL((reduce_rows_kernel<T, 128>), dim3(blocks), dim3(256), 0, stream, p);
+                break;
+            case 256:
+                hipLaunchKernelGGL((reduce_rows_kernel<T, 256>), dim3(blocks), dim3(256), 0, stream, p);
+                break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (p.head_dim) {
         case 64:
             hipLaunchKernelGGL((reduce_kernel<T, 64>), dim3(p.total_q, p.hq, 1), dim3(RT), 0,

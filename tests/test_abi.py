@@ -46,7 +46,7 @@ def test_status_strings_and_version():
     lib = _lib()
     for s in range(5):
         assert lib.pa_status_string(s)
-    assert lib.pa_abi_version() == 100
+    assert lib.pa_abi_version() == 101
 
 
 FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: every call below is rejected
@@ -64,7 +64,8 @@ def attn_args(**over):
 
 @pytest.mark.parametrize("over,status", [
     (dict(dtype=7), 2), (dict(d=96), 2), (dict(bs=12), 2), (dict(bs=64), 2),
-    (dict(hq=5, hkv=2), 1), (dict(hq=32, hkv=2), 2), (dict(P=128), 2), (dict(num_seqs=-1), 1),
+    (dict(hq=5, hkv=2), 1), (dict(hq=32, hkv=2), 2), (dict(P=128), 2), (dict(P=384), 2),
+    (dict(P=8192 + 256), 2), (dict(num_seqs=-1), 1),
     (dict(hq=0), 1), (dict(nb=0), 1), (dict(out=None), 1), (dict(q=None), 1), (dict(bt=None), 1),
     (dict(cu=None), 1), (dict(max_q_len=0), 1), (dict(max_seq_len=0), 1),
     (dict(max_blocks=3), 1), (dict(scale=float("nan")), 1), (dict(scale=float("inf")), 1),
@@ -102,7 +103,8 @@ def test_reshape_and_cache_zero_tokens_ok():
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(dtype=9), 2), (dict(d=48), 2), (dict(P=0), 2), (dict(P=300), 2), (dict(out=None), 1),
+    (dict(dtype=9), 2), (dict(d=48), 2), (dict(P=0), 2), (dict(P=300), 2), (dict(P=8448), 2),
+    (dict(out=None), 1),
     (dict(tmp=None), 3), (dict(mp=0), 3), (dict(hq=0), 1), (dict(out=ctypes.c_void_p(0x100006)), 1),
 ])
 def test_split_kv_reduce_rejects(over, status):

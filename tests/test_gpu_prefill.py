@@ -115,3 +115,17 @@ def test_scale_values(scale):
             out = run_gpu(b, P)
             torch.cuda.synchronize()
             assert_close(out, ref, torch.bfloat16, f"scale={scale} max_q={max_q} P={P}")
+
+
+@pytest.mark.parametrize("max_q", [1, 60])
+def test_large_partitions(max_q):
+    """Partition sizes beyond the pages' 256/512 (any multiple of 256): rows
+    cut into 1..4 partitions, on the decode path (max_q 1) and the MFMA path."""
+    w = W.random_case(61 + max_q, num_seqs=6, max_q=max_q, max_ctx=2900, num_q_heads=16,
+                      num_kv_heads=2, head_dim=128, block_size=16, dtype=torch.bfloat16)
+    ref = oracle.run_workload(w)
+    b = to_device(w)
+    for P in (768, 1024, 2048):
+        out = run_gpu(b, P)
+        torch.cuda.synchronize()
+        assert_close(out, ref, torch.bfloat16, f"max_q={max_q} P={P}")
