@@ -42,6 +42,15 @@ namespace {
 #ifndef PA_DECODE_HEAD_FASTEST
 #define PA_DECODE_HEAD_FASTEST 1
 #endif
+#ifndef PA_DECODE_ORDER
+#define PA_DECODE_ORDER 2
+#endif
+#ifndef PA_DECODE_LAZY
+#define PA_DECODE_LAZY 1
+#endif
+// A lane's reference max m is only raised when a chunk's max exceeds it by
+// more than this (log2 units); weights then stay below 2^RESCALE_THRESHOLD.
+constexpr float RESCALE_THRESHOLD = 8.0f;
 
 
 template <typename T, int D, int GT, int CT_, int NW_, int NST_>
@@ -160,7 +169,8 @@ template <class C, int GT, bool MASKED>
 __device__ __forceinline__ void chunk_step(const char *kst, const char *vst, int c, int tip,
                                            int tok0, int tok_end, float scale_log2,
                                            const uint32_t (&qw)[GT][8], float (&m)[GT],
-                                           float (&l)[GT], float (&accv)[GT][C::NE]) {
+                                           float (&mtrue)[GT], float (&l)[GT],
+                                           float (&accv)[GT][C::NE]) {
     constexpr int NE = C::NE;
     constexpr int NP = C::NP;
     // ---- scores of every pass ----
@@ -196,17 +206,44 @@ __device__ __forceinline__ void chunk_step(const char *kst, const char *vst, int
     // ---- online softmax: new running max, rescale of l and acc ----
     // In an unmasked chunk every score is finite, so the new max is finite and
     // exp2 needs no -inf guard; the masked chunk guards both.
+    if constexpr (PA_DECODE_LAZY && !MASKED) {
+        // Lazy: rescale (all lanes, uniformly) only when some lane's max grew
+        // past its reference by more than the threshold.
+        float mx[GT];
+        bool up = false;
 #pragma unroll
-    for (int g = 0; g < GT; ++g) {
-        float mx = sc[0][g];
+        for (int g = 0; g < GT; ++g) {
+            mx[g] = sc[0][g];
 #pragma unroll
-        for (int j = 1; j < NP; ++j) mx = fmaxf(mx, sc[j][g]);
-        const float mn = fmaxf(m[g], mx);
-        const float alpha = MASKED ? exp2_diff(m[g], mn) : __builtin_amdgcn_exp2f(m[g] - mn);
-        m[g] = mn;
-        l[g] *= alpha;
+            for (int j = 1; j < NP; ++j) mx[g] = fmaxf(mx[g], sc[j][g]);
+            up = up || mx[g] > m[g] + RESCALE_THRESHOLD;
+            mtrue[g] = fmaxf(mtrue[g], mx[g]);
+        }
+        if (__builtin_amdgcn_ballot_w64(up)) {
 #pragma unroll
-        for (int e = 0; e < NE; ++e) accv[g][e] *= alpha;
+            for (int g = 0; g < GT; ++g) {
+                const float mn = mx[g] > m[g] + RESCALE_THRESHOLD ? mx[g] : m[g];
+                const float alpha = exp2_diff(m[g], mn);  // m = -inf before the first key
+                m[g] = mn;
+                l[g] *= alpha;
+#pragma unroll
+                for (int e = 0; e < NE; ++e) accv[g][e] *= alpha;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            float mx = sc[0][g];
+#pragma unroll
+            for (int j = 1; j < NP; ++j) mx = fmaxf(mx, sc[j][g]);
+            const float mn = fmaxf(m[g], mx);
+            const float alpha = MASKED ? exp2_diff(m[g], mn) : __builtin_amdgcn_exp2f(m[g] - mn);
+            m[g] = mn;
+            mtrue[g] = fmaxf(mtrue[g], mx);
+            l[g] *= alpha;
+#pragma unroll
+            for (int e = 0; e < NE; ++e) accv[g][e] *= alpha;
+        }
     }
     float pr[NP][GT];
 #pragma unroll
@@ -278,14 +315,25 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
     // The KV heads of one partition are adjacent in the grid, so the
     // workgroups that run together read the same pages (all heads' rows of a
     // page are contiguous) rather than 1/Hkv of many different pages.
+#if PA_DECODE_ORDER == 0
     const int kvh = PA_DECODE_HEAD_FASTEST ? blockIdx.x : blockIdx.y;
     const int part = PA_DECODE_HEAD_FASTEST ? blockIdx.y : blockIdx.x;
+    const int zrow = blockIdx.z;
+#elif PA_DECODE_ORDER == 1   // partition-major: grid (hkv, rows, parts)
+    const int kvh = blockIdx.x;
+    const int part = blockIdx.z;
+    const int zrow = blockIdx.y;
+#else                        // partition-major, last partitions first
+    const int kvh = blockIdx.x;
+    const int part = gridDim.z - 1 - blockIdx.z;
+    const int zrow = blockIdx.y;
+#endif
     // A workgroup serves one query token: request r's only token, or (per-token
     // launches) packed token blockIdx.z, whose keys end at its own causal
     // position ctx + j.
     int r, q0, seq_len;
     if (p.per_token) {
-        q0 = blockIdx.z;
+        q0 = zrow;
         int lo = 0, hi = p.num_seqs - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
@@ -295,7 +343,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
         const int q_len = p.cu_q[r + 1] - p.cu_q[r];
         seq_len = p.seq_lens[r] - q_len + (q0 - p.cu_q[r]) + 1;
     } else {
-        r = blockIdx.z;
+        r = zrow;
         q0 = p.cu_q[r];
         if (p.cu_q[r + 1] - q0 <= 0) return;
         seq_len = p.seq_lens[r];
@@ -406,11 +454,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
 
     // ---- online softmax state (per lane, for its token subset) ----
     constexpr int NE = C::NE;
-    float m[GT], l[GT];
+    float m[GT], mtrue[GT], l[GT];  // reference max, true max, exp-sum
     float accv[GT][NE];
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
         m[g] = NEG_INF;
+        mtrue[g] = NEG_INF;
         l[g] = 0.f;
 #pragma unroll
         for (int e = 0; e < NE; ++e) accv[g][e] = 0.f;
@@ -431,21 +480,22 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
     for (int k = 0; k < nmy - 1; ++k) {
         const char *kst, *vst;
         stage(k, kst, vst);
-        chunk_step<C, GT, false>(kst, vst, c, tip, 0, 0, p.scale_log2, qw, m, l, accv);
+        chunk_step<C, GT, false>(kst, vst, c, tip, 0, 0, p.scale_log2, qw, m, mtrue, l, accv);
     }
     if (nmy > 0) {
         const char *kst, *vst;
         stage(nmy - 1, kst, vst);
         const int tok0 = (c_begin + wave + (nmy - 1) * NW) * CT;
-        chunk_step<C, GT, true>(kst, vst, c, tip, tok0, tok_end, p.scale_log2, qw, m, l, accv);
+        chunk_step<C, GT, true>(kst, vst, c, tip, tok0, tok_end, p.scale_log2, qw, m, mtrue, l,
+                                 accv);
     }
 
     // ---- merge the wave's lane groups: rescale every lane to the wave-wide
-    // max, after which merging is a plain sum (DPP rotation inside each
+    // true max, after which merging is a plain sum (DPP rotation inside each
     // 16-lane row, then v_permlane16/32_swap across rows) ----
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
-        const float M = wave_max(m[g]);
+        const float M = wave_max(mtrue[g]);
         const float f = exp2_diff(m[g], M);
         m[g] = M;
         l[g] *= f;
@@ -553,7 +603,11 @@ hipError_t launch_t(const AttnParams &p, hipStream_t stream) {
     using Tn = DecodeTuning<T, D, GT>;
     const int parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
     const int rows = p.per_token ? p.total_q : p.num_seqs;
+#if PA_DECODE_ORDER == 0
     dim3 grid = PA_DECODE_HEAD_FASTEST ? dim3(p.hkv, parts, rows) : dim3(parts, p.hkv, rows);
+#else
+    dim3 grid = dim3(p.hkv, rows, parts);
+#endif
     dim3 block(Tn::NW * 64);
     hipLaunchKernelGGL((decode_kernel<T, D, GT, Tn::CT, Tn::NW, Tn::NST>), grid, block, 0, stream,
                        p);
