@@ -22,7 +22,9 @@ reported beside it.
 events on the stream it runs on.  ``cpu_baseline`` times the fp64 oracle on
 the same workload on this host's cores.  ``secondary`` holds the other
 workloads of the metric: long-context split-KV decode and the mixed prefill
-and speculative-verify batches (MFMA TFLOP/s).
+and speculative-verify batches (MFMA TFLOP/s), plus a uniform long-prompt
+prefill batch of the mixed batches' head shape that shows the tiled kernel's
+steady state apart from the load imbalance of short ragged batches.
 """
 from __future__ import annotations
 
@@ -355,10 +357,18 @@ def main():
                 "warm_ms_per_step": round(s4w * 1e3, 5)}
             log(f"long decode P={P4}: {sec_out[f'long_decode_bf16_P{P4}']}")
         del w4
+        # partition sizes: the mixed batches run unsplit (their rows are at
+        # most 3,000 keys); the verify batch splits its long contexts so its
+        # 164 q-tiles do not leave most of the GPU idle
+        uniform = lambda: W.build(  # noqa: E731
+            "prefill_uniform_bf16", seed=7, q_lens=[4096] * 8, seq_lens=[8192] * 8,
+            num_q_heads=16, num_kv_heads=2, head_dim=256, block_size=16,
+            num_blocks=8 * 8192 // 16 + 8, dtype=torch.bfloat16,
+            description="8 x 4096-token prompt chunks over 4096 cached tokens, 16/2/256")
         for name, P3 in (("mixed_prefill_bf16_A", 0), ("mixed_prefill_bf16_B", 0),
-                         ("spec_verify_bf16", 0)):
+                         ("spec_verify_bf16", 1024), ("prefill_uniform_bf16", 0)):
             try:
-                w3 = W.CONFIGS[name]()
+                w3 = uniform() if name == "prefill_uniform_bf16" else W.CONFIGS[name]()
                 s3, k3, s3w, _ = measure(w3, P3, steps2, 5, 2, device)
             except Exception as e:  # report, do not hide: the line says what failed
                 sec_out[name] = {"error": str(e)[:200]}
@@ -367,6 +377,7 @@ def main():
             f3 = w3.algorithmic_flops()
             b3 = step_bytes(w3, True)
             sec_out[name] = {
+                "partition_size": P3,
                 "ms_per_step": round(s3 * 1e3, 5),
                 "TFLOP/s": round(f3 / s3 / 1e12, 2),
                 "attention_ms": round(k3["attention"], 5),

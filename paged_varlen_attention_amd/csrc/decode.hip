@@ -328,60 +328,63 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
     const int part = gridDim.z - 1 - blockIdx.z;
     const int zrow = blockIdx.y;
 #endif
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane % C::L;    // column of the row this lane holds
+    const int tip = lane / C::L;  // token slot within a pass
+    const int tok_begin = p.partition ? part * p.partition : 0;
+    const int bs = p.block_size;
+    const int lbs = p.log2_bs;
+    const int c_begin = tok_begin / CT;
+    const int ppc = bs < CT ? CT / bs : 1;  // pages per chunk: 1, or 2 for 8-token pages
+    const int cpw = 64 / ppc;               // chunks covered by one block-table window
+
     // A workgroup serves one query token: request r's only token, or (per-token
-    // launches) packed token blockIdx.z, whose keys end at its own causal
-    // position ctx + j.
-    int r, q0, seq_len;
+    // launches) packed token `zrow`, whose keys end at its own causal position
+    // ctx + j.
+    int r = zrow, q0 = zrow;
     if (p.per_token) {
-        q0 = zrow;
         int lo = 0, hi = p.num_seqs - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (p.cu_q[mid] <= q0) lo = mid; else hi = mid - 1;
         }
         r = lo;
+    }
+
+    // ---- this wave's block-table window: lane i holds page (i / cpw) of the
+    // wave's chunk kw0 + i % cpw.  The load needs the request but not its
+    // length (it is bounded by the table row), so it is in flight while the
+    // lengths arrive. ----
+    const int32_t *bt_row = p.bt + (size_t)r * p.bt_stride;
+    auto load_window = [&](int kw0) -> int {
+        const int k = kw0 + lane % cpw;
+        const int ch = c_begin + wave + k * NW;
+        const int lp = ((ch * CT) >> lbs) + lane / cpw;
+        const int v = lp < p.bt_stride ? bt_row[lp] : 0;
+        return v < 0 ? 0 : (v >= p.num_blocks ? p.num_blocks - 1 : v);
+    };
+    int win_base = 0;
+    int btv = load_window(0);
+
+    int seq_len;
+    if (p.per_token) {
         const int q_len = p.cu_q[r + 1] - p.cu_q[r];
         seq_len = p.seq_lens[r] - q_len + (q0 - p.cu_q[r]) + 1;
     } else {
-        r = zrow;
         q0 = p.cu_q[r];
         if (p.cu_q[r + 1] - q0 <= 0) return;
         seq_len = p.seq_lens[r];
     }
-    const int tok_begin = p.partition ? part * p.partition : 0;
     if (tok_begin >= seq_len || seq_len <= 0) return;
     const int tok_end = p.partition ? min(seq_len, tok_begin + p.partition) : seq_len;
     const int nparts = p.partition ? (seq_len + p.partition - 1) / p.partition : 1;
     const int G = p.group;
 
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c = lane % C::L;    // column of the row this lane holds
-    const int tip = lane / C::L;  // token slot within a pass
-
-    // ---- this wave's chunks and its block-table window ----
-    const int bs = p.block_size;
-    const int lbs = p.log2_bs;
-    const int c_begin = tok_begin / CT;
+    // ---- this wave's chunks ----
     const int c_end = (tok_end + CT - 1) / CT;
     const int nchunks = c_end - c_begin;
     const int nmy = nchunks > wave ? (nchunks - wave + NW - 1) / NW : 0;
-    const int seq_pages = (seq_len + bs - 1) >> lbs;
-    const int ppc = bs < CT ? CT / bs : 1;  // pages per chunk: 1, or 2 for 8-token pages
-    const int cpw = 64 / ppc;               // chunks covered by one block-table window
-    const int32_t *bt_row = p.bt + (size_t)r * p.bt_stride;
-
-    // Lane i of the window holds page (i / cpw) of this wave's chunk kw0 + i % cpw.
-    auto load_window = [&](int kw0) -> int {
-        const int k = kw0 + lane % cpw;
-        const int ch = c_begin + wave + k * NW;
-        const int lp = ((ch * CT) >> lbs) + lane / cpw;
-        int v = 0;
-        if (k < nmy && lp < seq_pages) v = bt_row[lp];
-        return v < 0 ? 0 : (v >= p.num_blocks ? p.num_blocks - 1 : v);
-    };
-    int win_base = 0;
-    int btv = load_window(0);
 
     // ---- query registers: the lane's 8 words of each head of the group ----
     uint32_t qw[GT][8];
