@@ -176,6 +176,23 @@ def time_graph_steps(step, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
+def step_percentiles(step, reps):
+    """p10 / p50 / p90 (ms) of single graph replays, each bracketed by its own
+    events on the current stream."""
+    import torch
+    ts = []
+    for k in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step.replay(k)
+        e1.record()
+        ts.append((e0, e1))
+    torch.cuda.synchronize()
+    v = sorted(a.elapsed_time(b) for a, b in ts)
+    pick = lambda q: v[min(len(v) - 1, int(q * (len(v) - 1) + 0.5))]  # noqa: E731
+    return {"p10": round(pick(0.1), 5), "p50": round(pick(0.5), 5), "p90": round(pick(0.9), 5)}
+
+
 def time_kernels(step, reps):
     """Per-kernel durations from HIP events on the launch stream (eager launches)."""
     import torch
@@ -190,7 +207,9 @@ def measure(w, P, steps, warmup, copies, device, write_cache=True):
     step = Step(w, P, copies, device, write_cache)
     step.capture()
     sec = time_graph_steps(step, steps, warmup)
+    pct = step_percentiles(step, max(10, steps))
     km = time_kernels(step, max(10, steps // 2))
+    km["step_ms_percentiles"] = pct
     step_warm = Step(w, P, 1, device, write_cache)
     step_warm.capture()
     sec_warm = time_graph_steps(step_warm, max(5, steps // 2), 2)
@@ -323,7 +342,8 @@ def main():
             "algorithmic_bytes_per_step": nbytes,
             "kv_pool_copies_cycled": args.copies,
             "warm_ms_per_step": round(sec_warm * 1e3, 5),
-            "kernel_ms": {k: round(v, 5) for k, v in km.items()},
+            "kernel_ms": {k: round(v, 5) for k, v in km.items() if k != "step_ms_percentiles"},
+            "step_ms_percentiles": km["step_ms_percentiles"],
             "parallelism": "single GPU",
         },
         "roofline": {
@@ -354,6 +374,7 @@ def main():
                 "attention_ms": round(k4["attention"], 5), "reduce_ms": round(k4["reduce"], 5),
                 "attention_GB/s": round(b4 / (k4["attention"] * 1e-3) / 1e9, 2),
                 "frac_hbm": round(b4 / s4 / 1e9 / HBM_PEAK_GBS, 4),
+                "step_ms_percentiles": k4["step_ms_percentiles"],
                 "warm_ms_per_step": round(s4w * 1e3, 5)}
             log(f"long decode P={P4}: {sec_out[f'long_decode_bf16_P{P4}']}")
         del w4
@@ -385,6 +406,7 @@ def main():
                 "frac_mfma": round(f3 / (k3["attention"] * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                 "GB/s": round(b3 / s3 / 1e9, 2),
                 "algorithmic_flops": f3, "algorithmic_bytes": b3,
+                "step_ms_percentiles": k3["step_ms_percentiles"],
                 "warm_ms_per_step": round(s3w * 1e3, 5)}
             log(f"{name}: {sec_out[name]}")
         result["secondary"] = sec_out

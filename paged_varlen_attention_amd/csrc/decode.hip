@@ -45,6 +45,10 @@ namespace {
 #ifndef PA_DECODE_ORDER
 #define PA_DECODE_ORDER 2
 #endif
+// Merge states a wave leaves in LDS: 1 = rows merged in registers first.
+#ifndef PA_DECODE_SPW_MAX
+#define PA_DECODE_SPW_MAX(L) 4
+#endif
 #ifndef PA_DECODE_LAZY
 #define PA_DECODE_LAZY 1
 #endif
@@ -77,7 +81,8 @@ struct DecodeCfg {
     // Merge states per wave: as many row states as fit in the staging LDS
     // (4 rows, or 2 halves when a token spans 32 lanes), else fewer after
     // merging rows in registers.
-    static constexpr int SPW_MAX = L <= 16 ? 4 : 2;
+    static constexpr int ROWS = L <= 16 ? 4 : 2;  // lane groups of a wave (16- or 32-lane rows)
+    static constexpr int SPW_MAX = PA_DECODE_SPW_MAX(L) < ROWS ? PA_DECODE_SPW_MAX(L) : ROWS;
     static constexpr bool fits(int spw) { return NW * spw * STATE_FLOATS * 4 <= STAGE_BYTES; }
     static constexpr int SPW = fits(SPW_MAX) ? SPW_MAX : (fits(SPW_MAX / 2) ? SPW_MAX / 2 : 1);
     static constexpr int NS = NW * SPW;          // merge states of the workgroup
@@ -512,8 +517,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
         sum_rot<0x124, GT, NE>(l, accv);  // row_ror:4
     }
     // rows i and i+2 onto one state, then rows 2i and 2i+1, as LDS requires
-    if constexpr (C::SPW * 2 <= C::SPW_MAX) sum_pairs<true, GT, NE>(l, accv);
-    if constexpr (C::L <= 16 && C::SPW == 1) sum_pairs<false, GT, NE>(l, accv);
+    if constexpr (C::SPW * 2 <= C::ROWS) sum_pairs<true, GT, NE>(l, accv);
+    if constexpr (C::ROWS == 4 && C::SPW == 1) sum_pairs<false, GT, NE>(l, accv);
 
     // ---- one state per wave to LDS, then all threads merge the waves ----
     __syncthreads();  // every wave is done with its stages

@@ -6,7 +6,7 @@
 // M = max_k m_k, w_k = l_k 2^(m_k - M), out = sum_k w_k o_k / sum_k w_k.
 // Rows with n == 1 were finalised by the attention kernel and are skipped.
 // Two launch shapes, both summing in a fixed order (deterministic):
-//  * up to 64 partitions (every prefill or mixed batch, decode up to 64*P
+//  * up to 16 partitions (prefill and mixed batches, decode up to 16*P
 //    keys): one wave per (token, head) row, four rows per workgroup;
 //  * more partitions (long decode): one workgroup per (token, head, 64-wide
 //    slice of D), partitions spread over 16 lane groups (float4 per lane along
@@ -19,6 +19,7 @@ namespace {
 
 constexpr int RT = 256;      // threads per workgroup
 constexpr int WCAP = 2048;   // partition weights kept in LDS
+constexpr int ROWS_MAX_PARTS = 16;  // partitions per row up to which the row form is used
 
 // Elements of D per workgroup: whole rows up to 128, 64-wide slices beyond.
 template <int D>
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(RT) void reduce_kernel(const ReduceParams p) {
 }
 
 // One wave per (token, head) row, four rows per workgroup: for batches with
-// many rows and at most 64 partitions per row (prefill and mixed batches),
+// many rows and at most 16 partitions per row (prefill and mixed batches),
 // where a workgroup per row would be mostly launch overhead.  Lane k holds
 // partition k's statistics; the partials are then accumulated in partition
 // order, each lane owning D/64 consecutive elements of the row.
@@ -187,7 +188,9 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(const ReduceParams p) 
 
 template <typename T>
 hipError_t launch_t(const ReduceParams &p, hipStream_t stream) {
-    if (p.max_parts <= 64) {
+    // The row form serialises a row's partitions in one wave: right for many
+    // rows with few partitions; a few long rows keep the slice form.
+    if (p.max_parts <= ROWS_MAX_PARTS) {
         const int blocks = (int)(((int64_t)p.total_q * p.hq + 3) / 4);
         switch (p.head_dim) {
             case 64:
