@@ -54,10 +54,10 @@ def _declare(lib):
     lib.pa_ref_num_threads.restype = ctypes.c_int
     lib.pa_ref_reshape_and_cache.argtypes = [P, P, P, P, P, I, I, I, I, I, I]
     lib.pa_ref_expand_block_tables.argtypes = [P, P, I, I, I, I, I]
-    lib.pa_ref_attention.argtypes = [P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, I, I, I, D, I]
+    lib.pa_ref_attention.argtypes = [P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, I, I, I, D, I, P]
     lib.pa_ref_attention_partials.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
                                               D, I, I, I]
-    lib.pa_ref_split_reduce.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I]
+    lib.pa_ref_split_reduce.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P]
     for f in ("pa_ref_reshape_and_cache", "pa_ref_expand_block_tables", "pa_ref_attention",
               "pa_ref_attention_partials", "pa_ref_split_reduce"):
         getattr(lib, f).restype = ctypes.c_int
@@ -113,10 +113,20 @@ def _common(w_q, key_cache, cu, seq_lens, block_tables):
     return TQ, hq, d, nb, bs, hkv, int(seq_lens.numel()), int(block_tables.shape[1])
 
 
+def _sinks(sinks, hq):
+    if sinks is None:
+        return None
+    sinks = torch.as_tensor(sinks, dtype=torch.float32).contiguous()
+    if sinks.shape != (hq,):
+        raise ValueError("sinks must be float32 [num_q_heads]")
+    return sinks
+
+
 def attention(q, key_cache, value_cache, cu_seqlens_q, seq_lens, block_tables, scale: float,
-              rows: Optional[Sequence[Sequence[int]]] = None, lib=None) -> torch.Tensor:
+              rows: Optional[Sequence[Sequence[int]]] = None, sinks=None, lib=None) -> torch.Tensor:
     """fp64 masked softmax(QK^T*scale)V through the block tables.
-    rows=None -> [total_q, Hq, D]; rows=[(t, h), ...] -> [n, D]."""
+    rows=None -> [total_q, Hq, D]; rows=[(t, h), ...] -> [n, D].
+    sinks: optional float32 [Hq] sink logits (one more softmax term, no value)."""
     lib = lib or _load()
     TQ, hq, d, nb, bs, hkv, B, mb = _common(q, key_cache, cu_seqlens_q, seq_lens, block_tables)
     if rows is None:
@@ -129,10 +139,11 @@ def attention(q, key_cache, value_cache, cu_seqlens_q, seq_lens, block_tables, s
         head = np.ascontiguousarray(rows[:, 1])
         n = len(rows)
         out = torch.empty((n, d), dtype=torch.float64)
+    sk = _sinks(sinks, hq)  # kept alive across the call
     rc = lib.pa_ref_attention(_ptr(out), _ptr(tok), _ptr(head), n, _ptr(q), _ptr(key_cache),
                               _ptr(value_cache), _ptr(cu_seqlens_q), _ptr(seq_lens),
                               _ptr(block_tables), B, TQ, mb, hq, hkv, d, nb, bs, float(scale),
-                              _dtype_code(q.dtype))
+                              _dtype_code(q.dtype), _ptr(sk))
     if rc:
         raise ValueError("oracle attention: bad arguments")
     return out
@@ -160,12 +171,15 @@ def attention_partials(q, key_cache, value_cache, cu_seqlens_q, seq_lens, block_
     return o, m, l
 
 
-def split_reduce(o, m, l, cu_seqlens_q, seq_lens, partition_size: int, lib=None) -> torch.Tensor:
+def split_reduce(o, m, l, cu_seqlens_q, seq_lens, partition_size: int, sinks=None,
+                 lib=None) -> torch.Tensor:
     lib = lib or _load()
     TQ, hq, mp, d = o.shape
     out = torch.empty((TQ, hq, d), dtype=torch.float64)
+    sk = _sinks(sinks, hq)  # kept alive across the call
     rc = lib.pa_ref_split_reduce(_ptr(out), _ptr(o), _ptr(m), _ptr(l), _ptr(cu_seqlens_q),
-                                 _ptr(seq_lens), int(seq_lens.numel()), TQ, hq, d, partition_size, mp)
+                                 _ptr(seq_lens), int(seq_lens.numel()), TQ, hq, d, partition_size, mp,
+                                 _ptr(sk))
     if rc:
         raise ValueError("oracle split_reduce: bad arguments")
     return out
@@ -180,4 +194,4 @@ def run_workload(w, rows=None, lib=None) -> torch.Tensor:
         kc, vc = kc.clone(), vc.clone()
         reshape_and_cache(w.new_key, w.new_value, kc, vc, w.slot_mapping, lib=lib)
     return attention(w.q, kc, vc, w.cu_seqlens_q, w.seq_lens, w.block_tables, w.scale, rows=rows,
-                     lib=lib)
+                     sinks=getattr(w, "sinks", None), lib=lib)

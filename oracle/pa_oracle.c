@@ -88,6 +88,7 @@ typedef struct {
     const int32_t *cu, *seq_lens, *bt;
     int32_t num_seqs, total_q, max_blocks, hq, hkv, d, num_blocks, bs, dtype;
     double scale;
+    const float *sinks; /* NULL, or one logit per query head */
 } args_t;
 
 /* Where logical key i of request r lives: index of element 0 of that key's
@@ -128,7 +129,9 @@ static int64_t query_pos(const args_t *a, int32_t r, int32_t t) {
     return (int64_t)ctx + (t - a->cu[r]);
 }
 
-/* One output row: softmax over keys 0..p (natural exponent), weighted sum of V. */
+/* One output row: softmax over keys 0..p (natural exponent), weighted sum of V.
+ * With a sink logit for head h, the sink is one more term of the softmax
+ * denominator that carries no value: out = sum_i e^(s_i) v_i / (e^sink + sum_i e^(s_i)). */
 static int attention_row(const args_t *a, int32_t t, int32_t h, double *out_row, double *scores) {
     int32_t r = owner_of(t, a->cu, a->num_seqs);
     if (r < 0) return -1;
@@ -138,7 +141,9 @@ static int attention_row(const args_t *a, int32_t t, int32_t h, double *out_row,
     if (scores_for(a, r, t, h, 0, nk, scores)) return -1;
     double m = -INFINITY;
     for (int32_t i = 0; i < nk; ++i) m = scores[i] > m ? scores[i] : m;
-    double z = 0.0;
+    double sink = a->sinks ? (double)a->sinks[h] : -INFINITY;
+    if (sink > m) m = sink;
+    double z = a->sinks ? exp(sink - m) : 0.0;
     for (int32_t i = 0; i < nk; ++i) {
         scores[i] = exp(scores[i] - m);
         z += scores[i];
@@ -175,10 +180,10 @@ int pa_ref_attention(double *out, const int32_t *tok, const int32_t *head, int32
                      const int32_t *block_tables, int32_t num_seqs, int32_t total_q,
                      int32_t max_blocks_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
                      int32_t head_dim, int32_t num_blocks, int32_t block_size, double scale,
-                     int32_t dtype) {
+                     int32_t dtype, const float *sinks) {
     args_t a = {q, key_cache, value_cache, cu_seqlens_q, seq_lens, block_tables, num_seqs,
                 total_q, max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, num_blocks,
-                block_size, dtype, scale};
+                block_size, dtype, scale, sinks};
     if (check_args(&a)) return -1;
     int64_t rows = (tok == NULL) ? (int64_t)total_q * num_q_heads : n_rows;
     int32_t maxk = longest_seq(&a);
@@ -211,7 +216,7 @@ int pa_ref_attention_partials(double *o, double *m, double *l, const void *q,
                               int32_t partition_size, int32_t max_parts) {
     args_t a = {q, key_cache, value_cache, cu_seqlens_q, seq_lens, block_tables, num_seqs,
                 total_q, max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, num_blocks,
-                block_size, dtype, scale};
+                block_size, dtype, scale, NULL};
     if (check_args(&a) || partition_size <= 0 || max_parts <= 0) return -1;
     int64_t rows = (int64_t)total_q * num_q_heads;
     int err = 0;
@@ -271,7 +276,7 @@ int pa_ref_attention_partials(double *o, double *m, double *l, const void *q,
 int pa_ref_split_reduce(double *out, const double *o, const double *m, const double *l,
                         const int32_t *cu_seqlens_q, const int32_t *seq_lens, int32_t num_seqs,
                         int32_t total_q, int32_t num_q_heads, int32_t head_dim,
-                        int32_t partition_size, int32_t max_parts) {
+                        int32_t partition_size, int32_t max_parts, const float *sinks) {
     if (partition_size <= 0 || max_parts <= 0 || num_q_heads <= 0 || head_dim <= 0) return -1;
     for (int32_t t = 0; t < total_q; ++t) {
         int32_t r = owner_of(t, cu_seqlens_q, num_seqs);
@@ -285,7 +290,10 @@ int pa_ref_split_reduce(double *out, const double *o, const double *m, const dou
             size_t n = (size_t)t * num_q_heads + h;
             double M = -INFINITY;
             for (int32_t k = 0; k < parts; ++k) M = m[n * max_parts + k] > M ? m[n * max_parts + k] : M;
-            double wsum = 0.0;
+            /* the sink (natural-log logit) joins once, in log2 units like the statistics */
+            double sink2 = sinks ? (double)sinks[h] * LOG2E : -INFINITY;
+            if (sink2 > M) M = sink2;
+            double wsum = sinks ? exp2(sink2 - M) : 0.0;
             double *orow = out + n * head_dim;
             for (int32_t d = 0; d < head_dim; ++d) orow[d] = 0.0;
             for (int32_t k = 0; k < parts; ++k) {

@@ -23,7 +23,12 @@
  *   - query head h reads KV head h / (Hq / Hkv);
  *   - caches are [num_blocks, block_size, Hkv, D]; logical key i of request r
  *     lives in block block_tables[r][i / block_size], slot i % block_size;
- *   - slot_mapping < 0 means "skip this token".
+ *   - slot_mapping < 0 means "skip this token";
+ *   - an attention sink (the kernel walkthrough's decode kernel lists sink
+ *     support; the pages give no formula) is a per-query-head logit in the
+ *     same units as scale * q.k that joins the softmax denominator and
+ *     carries no value: out = sum_i e^(s_i) v_i / (e^sink + sum_i e^(s_i)).
+ *     Split partials leave it out; the merge adds it once.
  *
  * Element types: PA_REF_F32 = IEEE float32, PA_REF_BF16 = bfloat16 (the upper
  * 16 bits of a float32).  Every input value is widened exactly to double and
@@ -62,14 +67,15 @@ int pa_ref_expand_block_tables(int32_t *dst, const int32_t *src, int32_t num_seq
 
 /* Attention for selected (token, head) pairs: out[n][D] (double) for
  * n in [0, n_rows), row n = (tok[n], head[n]).  Pass tok = head = NULL to
- * compute every (t, h) in the natural order t*Hq + h (out = [total_q][Hq][D]). */
+ * compute every (t, h) in the natural order t*Hq + h (out = [total_q][Hq][D]).
+ * sinks: NULL, or float32 [num_q_heads] sink logits (see above). */
 int pa_ref_attention(double *out, const int32_t *tok, const int32_t *head, int32_t n_rows,
                      const void *q, const void *key_cache, const void *value_cache,
                      const int32_t *cu_seqlens_q, const int32_t *seq_lens,
                      const int32_t *block_tables, int32_t num_seqs, int32_t total_q,
                      int32_t max_blocks_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
                      int32_t head_dim, int32_t num_blocks, int32_t block_size, double scale,
-                     int32_t dtype);
+                     int32_t dtype, const float *sinks);
 
 /* Split-KV partials for every (t, h): partition k of the query at absolute
  * position p covers keys [k*P, min((k+1)*P, p+1)), k < ceil((p+1)/P).
@@ -88,11 +94,13 @@ int pa_ref_attention_partials(double *o, double *m, double *l, const void *q,
                               int32_t partition_size, int32_t max_parts);
 
 /* Merge of the partials above: with n = ceil((p+1)/P), M = max_k m_k,
- * w_k = l_k * 2^(m_k - M):  out[t][h][:] = sum_k w_k o_k / sum_k w_k. */
+ * w_k = l_k * 2^(m_k - M):  out[t][h][:] = sum_k w_k o_k / sum_k w_k.
+ * With sinks (float32 [num_q_heads], natural-log logits), sigma = sink * log2(e)
+ * joins the max and adds 2^(sigma - M) to the denominator once. */
 int pa_ref_split_reduce(double *out, const double *o, const double *m, const double *l,
                         const int32_t *cu_seqlens_q, const int32_t *seq_lens, int32_t num_seqs,
                         int32_t total_q, int32_t num_q_heads, int32_t head_dim,
-                        int32_t partition_size, int32_t max_parts);
+                        int32_t partition_size, int32_t max_parts, const float *sinks);
 
 #ifdef __cplusplus
 }

@@ -56,6 +56,15 @@ def cases():
         expected_m=[[[1.0, 2.0]]], expected_l=[[[1.5, 1.0]]],
         expected_o=[[[[1.0, 2.0 / 3.0], [1.0, 2.0]]]],
         expected_out=[[[1.0, 10.0 / 7.0]]])
+    c["attention_sink"] = dict(
+        source="vllm-metal kernel walkthrough, 'three Metal kernels': the decode kernel carries online softmax with attention-sink support (read as one more softmax term per query head that carries no value)",
+        derivation="paged_walk's keys (e^s = 1, 2, 4; v_i = [1, i]) plus a sink logit ln 8 (e^sink = 8): out = (1*v0 + 2*v1 + 4*v2) / (7 + 8) = [7/15, 10/15]. Split at 2 keys: partials as in split_partials_log2; merge with sigma = log2(8) = 3: M = 3, w = (1.5/4, 1/2), sink weight 1 -> (0.375*[1,2/3] + 0.5*[1,2]) / 1.875 = [7/15, 2/3]",
+        dtype="f32", num_q_heads=1, num_kv_heads=1, head_dim=2, block_size=2, num_blocks=3,
+        cu_seqlens_q=[0, 1], seq_lens=[3], block_tables=[[2, 0]], scale=math.log(2.0), partition_size=2,
+        sinks=[math.log(8.0)],
+        q=[[[1, 0]]],
+        cache_rows={str(i): {"k": [[[i, 0]]], "v": [[[1, i]]]} for i in range(3)},
+        expected_out=[[[7.0 / 15.0, 10.0 / 15.0]]])
     c["reshape_and_cache_scatter"] = dict(
         source="vllm-metal kernel walkthrough, 'three Metal kernels': reshape_and_cache scatters projected K/V into the paged cache; a slot is block*block_size + offset",
         derivation="bs 2, 3 blocks, slots [5,-1,0]: token 0 -> block 2 offset 1, token 1 skipped, token 2 -> block 0 offset 0; every other slot keeps its previous content (0 here)",

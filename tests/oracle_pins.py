@@ -17,6 +17,7 @@ against a deliberately broken build of the oracle (see
 from __future__ import annotations
 
 import json
+import math
 import os
 
 import numpy as np
@@ -353,6 +354,82 @@ def pin_closed_forms(lib):
     assert (out - ref).abs().max() <= 1e-12
 
 
+def _with_sinks(w, seed, scale=2.0):
+    import dataclasses
+    g = torch.Generator().manual_seed(seed)
+    return dataclasses.replace(w, sinks=(torch.randn(w.num_q_heads, generator=g) * scale).float())
+
+
+def dense_numpy_sinks(w):
+    """The dense numpy reference with each head's sink as one more key whose
+    logit is the sink and whose value is zero."""
+    q = w.q.double().numpy()
+    out = np.zeros(q.shape)
+    G = w.num_q_heads // w.num_kv_heads
+    cu = w.cu_seqlens_q.numpy()
+    sk = w.sinks.double().numpy()
+    for r in range(w.num_seqs):
+        K, V = gather_request(w, r)
+        L, ql = K.shape[0], cu[r + 1] - cu[r]
+        if ql == 0:
+            continue
+        ctx = L - ql
+        Kx, Vx = np.repeat(K, G, axis=1), np.repeat(V, G, axis=1)
+        Q = q[cu[r]:cu[r + 1]]
+        S = np.einsum("jhd,ihd->hji", Q, Kx) * w.scale
+        mask = np.arange(L)[None, :] <= (ctx + np.arange(ql))[:, None]
+        S = np.where(mask[None], S, -np.inf)
+        S = np.concatenate([S, np.broadcast_to(sk[:, None, None], S.shape[:2] + (1,))], axis=-1)
+        Vz = np.concatenate([Vx, np.zeros((1,) + Vx.shape[1:])], axis=0)
+        S = S - S.max(axis=-1, keepdims=True)
+        P = np.exp(S)
+        P /= P.sum(axis=-1, keepdims=True)
+        out[cu[r]:cu[r + 1]] = np.einsum("hji,ihd->jhd", P, Vz)
+    return torch.from_numpy(out)
+
+
+def pin_golden_sink(lib):
+    c = golden("attention_sink")
+    q, kc, vc, cu, sl, bt, scale = golden_inputs(c)
+    sinks = torch.tensor(c["sinks"], dtype=torch.float32)
+    exp = torch.tensor(c["expected_out"], dtype=torch.float64)
+    out = oracle.attention(q, kc, vc, cu, sl, bt, scale, sinks=sinks, lib=lib)
+    assert torch.allclose(out, exp, rtol=1e-7, atol=1e-7), out  # the sink is stored as float32
+    o, m, l = oracle.attention_partials(q, kc, vc, cu, sl, bt, scale, c["partition_size"], lib=lib)
+    out = oracle.split_reduce(o, m, l, cu, sl, c["partition_size"], sinks=sinks, lib=lib)
+    assert torch.allclose(out, exp, rtol=1e-7, atol=1e-7), out
+
+
+def pin_sinks(lib):
+    """Sinks against the dense reference with a zero-value key, against the
+    closed form of one key, -inf against no sink, and split invariance."""
+    import dataclasses
+    for i, w in enumerate(micro_cases()[:6]):
+        ws = _with_sinks(w, 7 + i)
+        out = run(ws, lib)
+        ref = dense_numpy_sinks(ws)
+        assert (out - ref).abs().max() <= 1e-12, (w.name, (out - ref).abs().max())
+        none = dataclasses.replace(w, sinks=torch.full((w.num_q_heads,), float("-inf")))
+        assert bitwise_equal(run(none, lib), run(w, lib)), w.name
+        for P in (8, 32):
+            o, m, l = oracle.attention_partials(w.q, w.key_cache, w.value_cache, w.cu_seqlens_q,
+                                                w.seq_lens, w.block_tables, w.scale, P, lib=lib)
+            red = oracle.split_reduce(o, m, l, w.cu_seqlens_q, w.seq_lens, P, sinks=ws.sinks, lib=lib)
+            err = ((red - out).abs() / out.abs().clamp_min(1e-3)).max()
+            assert err <= 1e-12, (w.name, P, err)
+    # one key of logit x and a sink sigma: out = v * e^x / (e^x + e^sigma)
+    w = _single(1, 1, 2, 1, 64, seed=41)
+    x = (w.q.double()[0] @ w.key_cache.double()[int(w.block_tables[0, 0]), 0, 0]) * w.scale
+    for sig in (-3.0, 0.0, 2.5):
+        ws = dataclasses.replace(w, sinks=torch.tensor([sig, -sig], dtype=torch.float32))
+        out = run(ws, lib)
+        v = w.value_cache.double()[int(w.block_tables[0, 0]), 0, 0]
+        for h in range(2):
+            s = float(ws.sinks[h])
+            expect = v / (1.0 + math.exp(s - float(x[h])))
+            assert (out[0, h] - expect).abs().max() <= 1e-13, (sig, h)
+
+
 ALL_PINS = [pin_golden_attention, pin_golden_split, pin_golden_cache_write, pin_dense,
             pin_cache_write_vs_index_copy, pin_page_permutation, pin_page_size,
-            pin_split_invariance, pin_single_request, pin_closed_forms]
+            pin_split_invariance, pin_single_request, pin_closed_forms, pin_golden_sink, pin_sinks]

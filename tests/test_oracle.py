@@ -35,6 +35,9 @@ MUTATIONS = [
     ("cache write: block offset dropped", "size_t dst = ((size_t)blk * block_size + (size_t)off) * row;", "size_t dst = ((size_t)blk * block_size) * row;"),
     ("block-table view: wrong page order", "v * ratio + j", "v + j * ratio"),
     ("V read through the K cache", "out_row[d] += scores[i] * load_elem(a->vc,", "out_row[d] += scores[i] * load_elem(a->kc,"),
+    ("sink left out of the denominator", "double z = a->sinks ? exp(sink - m) : 0.0;", "double z = 0.0;"),
+    ("sink merged in natural units", "double sink2 = sinks ? (double)sinks[h] * LOG2E : -INFINITY;",
+     "double sink2 = sinks ? (double)sinks[h] : -INFINITY;"),
 ]
 
 

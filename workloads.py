@@ -64,6 +64,7 @@ class Workload:
     # page size the attention kernel walks (block_size / kernel_page_ratio)
     kernel_page_ratio: int = 1
     description: str = ""
+    sinks: Optional[torch.Tensor] = None  # float32 [Hq] attention-sink logits, or None
 
     @property
     def num_seqs(self) -> int:
