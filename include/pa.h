@@ -135,6 +135,15 @@ int pa_expand_block_tables(int32_t *dst, const int32_t *src, int32_t num_seqs, i
  *   Entries for k >= n are not written.
  *   max_partitions >= ceil(max_seq_len / P) is the capacity of the partials.
  *
+ * sinks: NULL, or device float32 [num_q_heads]: one attention-sink logit per
+ *   query head (kernel walkthrough, "three Metal kernels": the decode kernel's
+ *   sink support), in the units of scale * q.k.  The sink is one more term of
+ *   the softmax denominator and carries no value:
+ *     out[t][h][:] = sum_i e^(x_i) v_i / (e^(sinks[h]) + sum_i e^(x_i)),
+ *   x_i = scale * q.k_i.  Partials never include it (pass the same sinks to
+ *   pa_split_kv_reduce, which adds it once).  Values must be finite or -inf
+ *   (-inf is the same as no sink).
+ *
  * Host scalars: max_q_len = max over requests of q_len (>= 1 unless
  * total_q == 0), max_seq_len = max of seq_lens; both must be upper bounds.
  * Supported: dtype PA_F32 / PA_BF16; head_dim 64, 128, 256; block_size 8, 16,
@@ -147,23 +156,27 @@ int pa_varlen_attention(void *out, const void *q, const void *key_cache, const v
                         const int32_t *block_tables, int32_t num_seqs, int32_t total_q,
                         int32_t max_q_len, int32_t max_seq_len, int32_t max_blocks_per_seq,
                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                        int32_t num_blocks, int32_t block_size, float scale, int32_t dtype,
-                        int32_t partition_size, float *tmp_out, float *max_logits,
-                        float *exp_sums, int32_t max_partitions, void *stream);
+                        int32_t num_blocks, int32_t block_size, float scale,
+                        const float *sinks, int32_t dtype, int32_t partition_size,
+                        float *tmp_out, float *max_logits, float *exp_sums,
+                        int32_t max_partitions, void *stream);
 
 /*
  * pa_split_kv_reduce -- merge split-KV partials (kernel walkthrough, GQA decode
  * tip 4: the shared reducer).  For every row (t, h) with n >= 2 partitions
  * (n as above): M = max_k max_logits[k], w_k = exp_sums[k] * 2^(max_logits[k] - M),
  * out[t][h][:] = sum_k w_k tmp_out[k][:] / sum_k w_k, cast to dtype with
- * round-to-nearest-even.  Rows with n == 1 are left untouched.
+ * round-to-nearest-even.  With sinks (NULL or float32 [num_q_heads], as in
+ * pa_varlen_attention), sigma = sinks[h] * log2(e) joins the max M and
+ * 2^(sigma - M) the denominator.  Rows with n == 1 are left untouched.
  * Arguments mean what they mean in pa_varlen_attention.
  * Errors: PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP.
  */
 int pa_split_kv_reduce(void *out, const float *tmp_out, const float *max_logits,
                        const float *exp_sums, const int32_t *cu_seqlens_q, const int32_t *seq_lens,
                        int32_t num_seqs, int32_t total_q, int32_t num_q_heads, int32_t head_dim,
-                       int32_t partition_size, int32_t max_partitions, int32_t dtype, void *stream);
+                       const float *sinks, int32_t partition_size, int32_t max_partitions,
+                       int32_t dtype, void *stream);
 
 /*
  * pa_pick_partition_size -- host-only partition policy for decode batches

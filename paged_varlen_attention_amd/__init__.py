@@ -40,9 +40,9 @@ def _load() -> ctypes.CDLL:
     P, I, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
     lib.pa_reshape_and_cache.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
     lib.pa_expand_block_tables.argtypes = [P, P, I, I, I, I, I, P]
-    lib.pa_varlen_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I,
-                                        I, P, P, P, I, P]
-    lib.pa_split_kv_reduce.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+    lib.pa_varlen_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, P,
+                                        I, I, P, P, P, I, P]
+    lib.pa_split_kv_reduce.argtypes = [P, P, P, P, P, P, I, I, I, I, P, I, I, I, P]
     lib.pa_pick_partition_size.argtypes = [P, I, I, I]
     lib.pa_pick_partition_size.restype = ctypes.c_int32
     lib.pa_partials_bytes.argtypes = [I, I, I, I, ctypes.POINTER(ctypes.c_size_t),
@@ -149,9 +149,10 @@ def varlen_attention(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torc
                      cu_seqlens_q: torch.Tensor, seq_lens: torch.Tensor, block_tables: torch.Tensor,
                      *, max_q_len: int, max_seq_len: int, scale: float, partition_size: int = 0,
                      out: Optional[torch.Tensor] = None, partials: Optional[Partials] = None,
-                     reduce: bool = True) -> torch.Tensor:
+                     reduce: bool = True, sinks: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Paged varlen attention; with partition_size > 0 and reduce=True the split
-    partials are merged by pa_split_kv_reduce on the same stream."""
+    partials are merged by pa_split_kv_reduce on the same stream.  sinks:
+    optional float32 [Hq] attention-sink logits on the same device."""
     TQ, hq, d = q.shape
     nb, bs, hkv, cd = key_cache.shape
     if cd != d or value_cache.shape != key_cache.shape:
@@ -169,6 +170,8 @@ def varlen_attention(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torc
     if partials is not None and partition_size:
         tmp, ml, es = partials
         mp = partials.max_parts
+    if sinks is not None and sinks.shape != (hq,):
+        raise ValueError("sinks must be [num_q_heads]")
     s = _stream(dev)
     st = lib.pa_varlen_attention(
         _dev(out, "out", q.dtype, dev), _dev(q, "q", device=dev),
@@ -176,26 +179,31 @@ def varlen_attention(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torc
         _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev), _dev(seq_lens, "seq_lens", torch.int32, dev),
         _dev(block_tables, "block_tables", torch.int32, dev), B, TQ, int(max_q_len),
         int(max_seq_len), block_tables.shape[1], hq, hkv, d, nb, bs, float(scale),
+        _dev(sinks, "sinks", torch.float32, dev),
         _dtype_code(q.dtype), int(partition_size), _dev(tmp, "tmp_out", torch.float32, dev),
         _dev(ml, "max_logits", torch.float32, dev), _dev(es, "exp_sums", torch.float32, dev), mp, s)
     _check("pa_varlen_attention", st)
     if partition_size and reduce:
-        split_kv_reduce(out, partials, cu_seqlens_q, seq_lens, partition_size)
+        split_kv_reduce(out, partials, cu_seqlens_q, seq_lens, partition_size, sinks=sinks)
     return out
 
 
 def split_kv_reduce(out: torch.Tensor, partials: Partials, cu_seqlens_q: torch.Tensor,
-                    seq_lens: torch.Tensor, partition_size: int) -> torch.Tensor:
+                    seq_lens: torch.Tensor, partition_size: int,
+                    sinks: Optional[torch.Tensor] = None) -> torch.Tensor:
     TQ, hq, d = out.shape
     dev = out.device
     tmp, ml, es = partials
     if tmp.shape[:2] != (TQ, hq) or tmp.shape[3] != d:
         raise ValueError("partials shape mismatch")
+    if sinks is not None and sinks.shape != (hq,):
+        raise ValueError("sinks must be [num_q_heads]")
     st = lib.pa_split_kv_reduce(
         _dev(out, "out", device=dev), _dev(tmp, "tmp_out", torch.float32, dev),
         _dev(ml, "max_logits", torch.float32, dev), _dev(es, "exp_sums", torch.float32, dev),
         _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev), _dev(seq_lens, "seq_lens", torch.int32, dev),
-        seq_lens.shape[0], TQ, hq, d, int(partition_size), partials.max_parts,
+        seq_lens.shape[0], TQ, hq, d, _dev(sinks, "sinks", torch.float32, dev),
+        int(partition_size), partials.max_parts,
         _dtype_code(out.dtype), _stream(dev))
     _check("pa_split_kv_reduce", st)
     return out

@@ -568,8 +568,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
             num += st[g * D + d] * f;
             den += st[GT * D + GT + g] * f;
         }
-        const float o = num / den;
         const int h = kvh * G + g;
+        float o = num / den;
+        if (direct && p.sinks) {
+            // the head's sink: one more denominator term, no value (log2 units)
+            const float s2 = p.sinks[h] * LOG2E_F;
+            const float Mx = fmaxf(M, s2);
+            const float a = exp2_diff(M, Mx);
+            o = num * a / (den * a + exp2_diff(s2, Mx));
+        }
         if (direct) {
             const size_t oi = ((size_t)q0 * p.hq + h) * D + d;
             if constexpr (C::BF16)

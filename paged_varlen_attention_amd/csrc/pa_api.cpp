@@ -47,7 +47,7 @@ int check_partitions(int32_t partition_size, int32_t max_seq_len, const float *t
 
 extern "C" {
 
-int pa_abi_version(void) { return 101; }
+int pa_abi_version(void) { return 200; }
 
 const char *pa_status_string(int status) {
     switch (status) {
@@ -117,9 +117,10 @@ int pa_varlen_attention(void *out, const void *q, const void *key_cache, const v
                         const int32_t *block_tables, int32_t num_seqs, int32_t total_q,
                         int32_t max_q_len, int32_t max_seq_len, int32_t max_blocks_per_seq,
                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                        int32_t num_blocks, int32_t block_size, float scale, int32_t dtype,
-                        int32_t partition_size, float *tmp_out, float *max_logits,
-                        float *exp_sums, int32_t max_partitions, void *stream) {
+                        int32_t num_blocks, int32_t block_size, float scale,
+                        const float *sinks, int32_t dtype, int32_t partition_size,
+                        float *tmp_out, float *max_logits, float *exp_sums,
+                        int32_t max_partitions, void *stream) {
     try {
         if (!elt_bytes(dtype)) return PA_EUNSUPPORTED;
         if (num_seqs < 0 || total_q < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
@@ -142,6 +143,7 @@ int pa_varlen_attention(void *out, const void *q, const void *key_cache, const v
             return PA_EINVAL;
         if (!aligned16(out) || !aligned16(q) || !aligned16(key_cache) || !aligned16(value_cache))
             return PA_EINVAL;
+        if (reinterpret_cast<uintptr_t>(sinks) % alignof(float) != 0) return PA_EINVAL;
         const int st = check_partitions(partition_size, max_seq_len, tmp_out, max_logits,
                                         exp_sums, max_partitions);
         if (st != PA_OK) return st;
@@ -172,6 +174,7 @@ int pa_varlen_attention(void *out, const void *q, const void *key_cache, const v
         p.partition = partition_size;
         p.max_parts = partition_size ? max_partitions : 1;
         p.scale_log2 = scale * 1.44269504088896340736f;
+        p.sinks = sinks;
         p.dtype = dtype;
 
         // One query token per request -> the VALU decode kernel.  fp32 batches
@@ -196,8 +199,8 @@ int pa_varlen_attention(void *out, const void *q, const void *key_cache, const v
 int pa_split_kv_reduce(void *out, const float *tmp_out, const float *max_logits,
                        const float *exp_sums, const int32_t *cu_seqlens_q, const int32_t *seq_lens,
                        int32_t num_seqs, int32_t total_q, int32_t num_q_heads, int32_t head_dim,
-                       int32_t partition_size, int32_t max_partitions, int32_t dtype,
-                       void *stream) {
+                       const float *sinks, int32_t partition_size, int32_t max_partitions,
+                       int32_t dtype, void *stream) {
     try {
         if (!elt_bytes(dtype)) return PA_EUNSUPPORTED;
         if (num_seqs < 0 || total_q < 0 || num_q_heads <= 0 || head_dim <= 0) return PA_EINVAL;
@@ -208,6 +211,7 @@ int pa_split_kv_reduce(void *out, const float *tmp_out, const float *max_logits,
         if (!out || !cu_seqlens_q || !seq_lens) return PA_EINVAL;
         if (!tmp_out || !max_logits || !exp_sums || max_partitions <= 0) return PA_EWORKSPACE;
         if (!aligned16(out) || !aligned16(tmp_out)) return PA_EINVAL;
+        if (reinterpret_cast<uintptr_t>(sinks) % alignof(float) != 0) return PA_EINVAL;
         pa::ReduceParams p{};
         p.out = out;
         p.tmp_out = tmp_out;
@@ -221,6 +225,7 @@ int pa_split_kv_reduce(void *out, const float *tmp_out, const float *max_logits,
         p.head_dim = head_dim;
         p.partition = partition_size;
         p.max_parts = max_partitions;
+        p.sinks = sinks;
         p.dtype = dtype;
         return hip_status(pa::launch_reduce(p, (hipStream_t)stream));
     } catch (...) {

@@ -54,6 +54,8 @@ __device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel)
 }
 
 // exp2 of (a - m) that is 0 when a is -inf (also when m is -inf).
+constexpr float LOG2E_F = 1.44269504088896341f;
+
 __device__ __forceinline__ float exp2_diff(float a, float m) {
     return a == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(a - m);
 }

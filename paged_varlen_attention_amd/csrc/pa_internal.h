@@ -37,6 +37,7 @@ struct AttnParams {
     int32_t partition;      // 0 = no split
     int32_t max_parts;
     float scale_log2;       // scale * log2(e)
+    const float *sinks;     // NULL or [hq] sink logits (natural-log units)
     int32_t dtype;
     int32_t per_token;      // decode kernel: grid z indexes query tokens, not requests
     int32_t grid_tiles;     // tiled kernel: virtual q-tiles (set by its launcher)
@@ -56,6 +57,7 @@ struct ReduceParams {
     int32_t head_dim;
     int32_t partition;
     int32_t max_parts;
+    const float *sinks;     // NULL or [hq] sink logits (natural-log units)
     int32_t dtype;
 };
 

@@ -395,7 +395,14 @@ __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const 
     if (!row_valid) return;
     const int n_parts = p.partition ? pos / p.partition + 1 : 1;
     if (p.partition && part >= n_parts) return;  // no keys of this row here
-    const float inv = 1.f / l;
+    float inv = 1.f / l;
+    if (n_parts == 1 && p.sinks) {
+        // the head's sink: one more denominator term, no value (log2 units)
+        const float s2 = p.sinks[head] * LOG2E_F;
+        const float Mx = fmaxf(m, s2);
+        const float a = exp2_diff(m, Mx);
+        inv = a / (l * a + exp2_diff(s2, Mx));
+    }
     if (n_parts == 1) {
         uint16_t *orow = reinterpret_cast<uint16_t *>(p.out) + ((size_t)t_glob * p.hq + head) * D;
 #pragma unroll

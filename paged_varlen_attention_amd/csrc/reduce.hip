@@ -65,6 +65,9 @@ __global__ __launch_bounds__(RT) void reduce_kernel(const ReduceParams p) {
     float M = red[0];
 #pragma unroll
     for (int w = 1; w < RT / 64; ++w) M = fmaxf(M, red[w]);
+    // the head's sink joins the max and, once, the denominator (log2 units)
+    const float s2 = p.sinks ? p.sinks[h] * LOG2E_F : NEG_INF;
+    M = fmaxf(M, s2);
     __syncthreads();
 
     // w_k and their sum
@@ -77,7 +80,7 @@ __global__ __launch_bounds__(RT) void reduce_kernel(const ReduceParams p) {
     ws = group_sum<64>(ws);
     if ((tid & 63) == 0) red[tid >> 6] = ws;
     __syncthreads();
-    float W = 0.f;
+    float W = exp2_diff(s2, M);
 #pragma unroll
     for (int w = 0; w < RT / 64; ++w) W += red[w];
 
@@ -141,9 +144,11 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(const ReduceParams p) 
 
     const size_t srow = (size_t)row * p.max_parts;
     const float m = lane < n ? p.max_logits[srow + lane] : NEG_INF;
-    const float M = group_max<64>(m);
+    // the head's sink joins the max and, once, the denominator (log2 units)
+    const float s2 = p.sinks ? p.sinks[row % p.hq] * LOG2E_F : NEG_INF;
+    const float M = fmaxf(group_max<64>(m), s2);
     const float w = lane < n ? p.exp_sums[srow + lane] * exp2_diff(m, M) : 0.f;
-    const float W = group_sum<64>(w);
+    const float W = group_sum<64>(w) + exp2_diff(s2, M);
 
     const float *o = p.tmp_out + srow * D + lane * E;
     float acc[E];

@@ -3,6 +3,7 @@ HIP path through the C ABI binding, and compare with the fp64 oracle."""
 from __future__ import annotations
 
 import dataclasses
+from typing import Optional
 
 import numpy as np
 import torch
@@ -26,6 +27,7 @@ class DeviceBatch:
     max_q_len: int
     max_seq_len: int
     scale: float
+    sinks: Optional[torch.Tensor] = None   # float32 [Hq] on the device, or None
 
 
 def to_device(w, device="cuda", write_cache=True) -> DeviceBatch:
@@ -48,7 +50,8 @@ def to_device(w, device="cuda", write_cache=True) -> DeviceBatch:
     return DeviceBatch(q=w.q.to(device), key_cache=kc, value_cache=vc,
                        cu_seqlens_q=w.cu_seqlens_q.to(device), seq_lens=w.seq_lens.to(device),
                        block_tables=bt, max_q_len=w.max_q_len, max_seq_len=w.max_seq_len,
-                       scale=w.scale)
+                       scale=w.scale,
+                       sinks=None if w.sinks is None else w.sinks.to(device).float().contiguous())
 
 
 def run_gpu(b: DeviceBatch, partition_size=0, out=None, partials=None, reduce=True):
@@ -56,7 +59,7 @@ def run_gpu(b: DeviceBatch, partition_size=0, out=None, partials=None, reduce=Tr
     return pa.varlen_attention(b.q, b.key_cache, b.value_cache, b.cu_seqlens_q, b.seq_lens,
                                b.block_tables, max_q_len=b.max_q_len, max_seq_len=b.max_seq_len,
                                scale=b.scale, partition_size=partition_size, out=out,
-                               partials=partials, reduce=reduce)
+                               partials=partials, reduce=reduce, sinks=b.sinks)
 
 
 def errors(gpu: torch.Tensor, ref: torch.Tensor):

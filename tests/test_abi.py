@@ -46,7 +46,7 @@ def test_status_strings_and_version():
     lib = _lib()
     for s in range(5):
         assert lib.pa_status_string(s)
-    assert lib.pa_abi_version() == 101
+    assert lib.pa_abi_version() == 200
 
 
 FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: every call below is rejected
@@ -55,11 +55,12 @@ FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: every call belo
 def attn_args(**over):
     a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, cu=FAKE, sl=FAKE, bt=FAKE, num_seqs=2,
              total_q=2, max_q_len=1, max_seq_len=50, max_blocks=4, hq=4, hkv=1, d=64, nb=8,
-             bs=16, scale=0.125, dtype=0, P=0, tmp=None, ml=None, es=None, mp=0, stream=None)
+             bs=16, scale=0.125, sinks=None, dtype=0, P=0, tmp=None, ml=None, es=None, mp=0,
+             stream=None)
     a.update(over)
     return [a[k] for k in ("out", "q", "kc", "vc", "cu", "sl", "bt", "num_seqs", "total_q",
                            "max_q_len", "max_seq_len", "max_blocks", "hq", "hkv", "d", "nb", "bs",
-                           "scale", "dtype", "P", "tmp", "ml", "es", "mp", "stream")]
+                           "scale", "sinks", "dtype", "P", "tmp", "ml", "es", "mp", "stream")]
 
 
 @pytest.mark.parametrize("over,status", [
@@ -73,7 +74,7 @@ def attn_args(**over):
     (dict(P=512), 3), (dict(P=256, tmp=FAKE, ml=FAKE, es=FAKE, mp=0), 3),
     (dict(P=256, max_seq_len=600, max_blocks=40, tmp=FAKE, ml=FAKE, es=FAKE, mp=2), 3),
     (dict(P=256, tmp=FAKE, ml=None, es=FAKE, mp=4), 3),
-    (dict(num_seqs=70000), 2),
+    (dict(num_seqs=70000), 2), (dict(sinks=ctypes.c_void_p(0x100002)), 1),
 ])
 def test_varlen_attention_rejects(over, status):
     assert _lib().pa_varlen_attention(*attn_args(**over)) == status
@@ -106,13 +107,14 @@ def test_reshape_and_cache_zero_tokens_ok():
     (dict(dtype=9), 2), (dict(d=48), 2), (dict(P=0), 2), (dict(P=300), 2), (dict(P=8448), 2),
     (dict(out=None), 1),
     (dict(tmp=None), 3), (dict(mp=0), 3), (dict(hq=0), 1), (dict(out=ctypes.c_void_p(0x100006)), 1),
+    (dict(sinks=ctypes.c_void_p(0x100001)), 1),
 ])
 def test_split_kv_reduce_rejects(over, status):
-    a = dict(out=FAKE, tmp=FAKE, ml=FAKE, es=FAKE, cu=FAKE, sl=FAKE, B=2, TQ=2, hq=4, d=64, P=256,
-             mp=2, dtype=1, stream=None)
+    a = dict(out=FAKE, tmp=FAKE, ml=FAKE, es=FAKE, cu=FAKE, sl=FAKE, B=2, TQ=2, hq=4, d=64,
+             sinks=None, P=256, mp=2, dtype=1, stream=None)
     a.update(over)
-    args = [a[k] for k in ("out", "tmp", "ml", "es", "cu", "sl", "B", "TQ", "hq", "d", "P", "mp",
-                           "dtype", "stream")]
+    args = [a[k] for k in ("out", "tmp", "ml", "es", "cu", "sl", "B", "TQ", "hq", "d", "sinks", "P",
+                           "mp", "dtype", "stream")]
     assert _lib().pa_split_kv_reduce(*args) == status
 
 
