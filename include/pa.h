@@ -76,7 +76,8 @@ enum {
 #define PA_MAX_GROUP 8          /* num_q_heads / num_kv_heads */
 #define PA_MAX_SEQS 65535       /* requests per call */
 #define PA_MAX_PARTITION 8192  /* largest partition_size accepted */
-#define PA_SPLIT_WG_PER_CU 2    /* workgroups per CU the partition policy aims for */
+#define PA_SPLIT_FILL_NUM 7     /* the partition policy aims for 7/8 of a workgroup per CU */
+#define PA_SPLIT_FILL_DEN 8
 
 /*
  * pa_reshape_and_cache -- write new K/V rows into the paged cache
@@ -179,20 +180,56 @@ int pa_split_kv_reduce(void *out, const float *tmp_out, const float *max_logits,
                        int32_t dtype, void *stream);
 
 /*
- * pa_pick_partition_size -- host-only partition policy for decode batches
- * (kernel walkthrough, "dispatch layer": a work budget proportional to the
- * number of GPU cores, 512-token partitions tried first, then 256, and only
- * full partitions counted toward the budget).  With
- *   budget = PA_SPLIT_WG_PER_CU * num_cus,
- *   unsplit = num_kv_heads * num_seqs   (workgroups without a split),
- *   W(P)    = num_kv_heads * sum_r floor(seq_lens[r] / P):
- * returns 0 if no sequence is longer than 256 or unsplit >= 2 * budget,
- * else 512 if W(512) >= budget, else 256.
+ * pa_pick_partition_size -- host-only partition policy for decode batches.
+ * The pages' rule (kernel walkthrough, "dispatch layer") is a work budget
+ * proportional to the number of GPU cores with 512-token partitions tried
+ * before 256.  Calibrated on MI355X (decode batches of 1..256 requests,
+ * 1K..64K keys, two head shapes), the best partition is the LARGEST one that
+ * still gives about one workgroup per CU, because every partition pays a
+ * fixed start-up and merge cost.  With
+ *   budget  = num_cus * PA_SPLIT_FILL_NUM / PA_SPLIT_FILL_DEN,
+ *   unsplit = num_kv_heads * num_seqs    (workgroups without a split),
+ *   W(P)    = num_kv_heads * sum_r ceil(seq_lens[r] / P):
+ * returns 0 if no sequence is longer than 256 or unsplit >= budget, else the
+ * largest P in {256, 512, ..., PA_MAX_PARTITION} (powers of two) with
+ * W(P) >= budget, else 256.
  * host_seq_lens is a HOST array.  num_cus <= 0 asks the current device.
  * Returns -1 on bad arguments.  Enqueues nothing.
  */
 int32_t pa_pick_partition_size(const int32_t *host_seq_lens, int32_t num_seqs,
                                int32_t num_kv_heads, int32_t num_cus);
+
+/*
+ * Dispatch record: what the calling thread's last pa_varlen_attention or
+ * pa_split_kv_reduce call decided (the kernel walkthrough's dispatch layer,
+ * made inspectable).  Environment switch, read at every call:
+ *   PA_NO_SPLIT=1  pa_varlen_attention ignores partition_size (every row is
+ *                  finished in place, partial buffers untouched) and
+ *                  pa_split_kv_reduce does nothing.
+ */
+enum {
+    PA_PATH_NONE = 0,        /* rejected, or nothing to do (empty batch) */
+    PA_PATH_DECODE = 1,      /* VALU decode kernel, one workgroup per request */
+    PA_PATH_DECODE_TOKEN = 2,/* VALU decode kernel, one workgroup per query token */
+    PA_PATH_TILED = 3,       /* bf16 MFMA tile kernel */
+    PA_PATH_REDUCE_ROWS = 4, /* split-KV reduce, one wave per row */
+    PA_PATH_REDUCE_SLICES = 5,/* split-KV reduce, one workgroup per row slice */
+    PA_PATH_REDUCE_SKIP = 6  /* reduce disabled by PA_NO_SPLIT */
+};
+typedef struct {
+    int32_t path;            /* PA_PATH_* */
+    int32_t status;          /* the call's return value */
+    int32_t partition_size;  /* partition actually used (0 = none) */
+    int32_t split_disabled;  /* 1 if PA_NO_SPLIT overrode the caller's partition */
+    int32_t grid[3];         /* launch grid in workgroups (0 if nothing launched) */
+    int32_t block;           /* threads per workgroup */
+    int32_t tile[3];         /* decode: chunk tokens, waves, LDS stages; tiled: keys per
+                                tile, LDS stages, q tokens per tile; reduce: 0 */
+} pa_dispatch_info;
+
+/* Copy the calling thread's last record into *info.  Returns PA_EINVAL if
+ * info is NULL. */
+int pa_last_dispatch(pa_dispatch_info *info);
 
 /* Bytes needed for the partials of a split call (tmp_out; max_logits and
  * exp_sums each).  Returns PA_EINVAL on bad sizes. */

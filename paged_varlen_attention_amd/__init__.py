@@ -47,10 +47,11 @@ def _load() -> ctypes.CDLL:
     lib.pa_pick_partition_size.restype = ctypes.c_int32
     lib.pa_partials_bytes.argtypes = [I, I, I, I, ctypes.POINTER(ctypes.c_size_t),
                                       ctypes.POINTER(ctypes.c_size_t)]
+    lib.pa_last_dispatch.argtypes = [P]
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     for f in ("pa_reshape_and_cache", "pa_expand_block_tables", "pa_varlen_attention",
-              "pa_split_kv_reduce", "pa_partials_bytes", "pa_abi_version"):
+              "pa_split_kv_reduce", "pa_partials_bytes", "pa_abi_version", "pa_last_dispatch"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -209,8 +210,29 @@ def split_kv_reduce(out: torch.Tensor, partials: Partials, cu_seqlens_q: torch.T
     return out
 
 
+class _DispatchInfo(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("status", ctypes.c_int32),
+                ("partition_size", ctypes.c_int32), ("split_disabled", ctypes.c_int32),
+                ("grid", ctypes.c_int32 * 3), ("block", ctypes.c_int32),
+                ("tile", ctypes.c_int32 * 3)]
+
+
+PATHS = {0: "none", 1: "decode", 2: "decode_per_token", 3: "tiled", 4: "reduce_rows",
+         5: "reduce_slices", 6: "reduce_skipped"}
+
+
+def last_dispatch() -> dict:
+    """The calling thread's last pa_varlen_attention / pa_split_kv_reduce decision."""
+    info = _DispatchInfo()
+    _check("pa_last_dispatch", lib.pa_last_dispatch(ctypes.byref(info)))
+    return {"path": PATHS.get(info.path, str(info.path)), "status": info.status,
+            "partition_size": info.partition_size, "split_disabled": bool(info.split_disabled),
+            "grid": tuple(info.grid), "block": info.block, "tile": tuple(info.tile)}
+
+
 def pick_partition_size(seq_lens: Sequence[int], num_kv_heads: int, num_cus: int = 0) -> int:
-    """Host-side partition policy (0, 256 or 512); seq_lens is a host sequence."""
+    """Host-side partition policy (0 or a power of two from 256 to 8192);
+    seq_lens is a host sequence."""
     arr = (ctypes.c_int32 * len(seq_lens))(*[int(s) for s in seq_lens])
     r = lib.pa_pick_partition_size(ctypes.cast(arr, ctypes.c_void_p), len(seq_lens), num_kv_heads,
                                    num_cus)

@@ -614,7 +614,7 @@ struct DecodeTuning {
 };
 
 template <typename T, int D, int GT>
-hipError_t launch_t(const AttnParams &p, hipStream_t stream) {
+hipError_t launch_t(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
     using Tn = DecodeTuning<T, D, GT>;
     const int parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
     const int rows = p.per_token ? p.total_q : p.num_seqs;
@@ -624,32 +624,34 @@ hipError_t launch_t(const AttnParams &p, hipStream_t stream) {
     dim3 grid = dim3(p.hkv, rows, parts);
 #endif
     dim3 block(Tn::NW * 64);
+    if (li) *li = LaunchInfo{{(int)grid.x, (int)grid.y, (int)grid.z}, (int)block.x,
+                             {Tn::CT, Tn::NW, Tn::NST}, 0};
     hipLaunchKernelGGL((decode_kernel<T, D, GT, Tn::CT, Tn::NW, Tn::NST>), grid, block, 0, stream,
                        p);
     return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t launch_d(const AttnParams &p, hipStream_t stream) {
+hipError_t launch_d(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
     switch (p.group) {
-        case 1: return launch_t<T, D, 1>(p, stream);
-        case 2: return launch_t<T, D, 2>(p, stream);
+        case 1: return launch_t<T, D, 1>(p, stream, li);
+        case 2: return launch_t<T, D, 2>(p, stream, li);
         case 3:
-        case 4: return launch_t<T, D, 4>(p, stream);
+        case 4: return launch_t<T, D, 4>(p, stream, li);
         case 5:
-        case 6: return launch_t<T, D, 6>(p, stream);
+        case 6: return launch_t<T, D, 6>(p, stream, li);
         case 7:
-        case 8: return launch_t<T, D, 8>(p, stream);
+        case 8: return launch_t<T, D, 8>(p, stream, li);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename T>
-hipError_t launch_dt(const AttnParams &p, hipStream_t stream) {
+hipError_t launch_dt(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
     switch (p.head_dim) {
-        case 64: return launch_d<T, 64>(p, stream);
-        case 128: return launch_d<T, 128>(p, stream);
-        case 256: return launch_d<T, 256>(p, stream);
+        case 64: return launch_d<T, 64>(p, stream, li);
+        case 128: return launch_d<T, 128>(p, stream, li);
+        case 256: return launch_d<T, 256>(p, stream, li);
         default: return hipErrorInvalidValue;
     }
 }
@@ -661,9 +663,9 @@ bool decode_supported(int dtype, int head_dim, int group) {
            group >= 1 && group <= 8;
 }
 
-hipError_t launch_decode(const AttnParams &p, hipStream_t stream) {
-    if (p.dtype == 1) return launch_dt<bf16_t>(p, stream);
-    return launch_dt<float>(p, stream);
+hipError_t launch_decode(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
+    if (p.dtype == 1) return launch_dt<bf16_t>(p, stream, li);
+    return launch_dt<float>(p, stream, li);
 }
 
 }  // namespace pa

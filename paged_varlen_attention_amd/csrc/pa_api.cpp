@@ -29,6 +29,25 @@ int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_EHIP; }
 // Grid dimensions y and z are limited to 65535 workgroups.
 constexpr int32_t GRID_YZ_MAX = 65535;
 
+// The calling thread's last dispatch decision (pa_last_dispatch).
+thread_local pa_dispatch_info g_last{};
+
+void record_launch(pa_dispatch_info &rec, int32_t path, const pa::LaunchInfo &li) {
+    rec.path = path;
+    for (int i = 0; i < 3; ++i) {
+        rec.grid[i] = li.grid[i];
+        rec.tile[i] = li.tile[i];
+    }
+    rec.block = li.block;
+}
+
+// PA_NO_SPLIT=1 (read at every call) disables split-KV: attention finishes
+// every row in place and the reduce does nothing.
+bool split_disabled_by_env() {
+    const char *v = std::getenv("PA_NO_SPLIT");
+    return v && v[0] && !(v[0] == '0' && v[1] == 0);
+}
+
 // Partition sizes: multiples of 256 keys up to PA_MAX_PARTITION.
 bool partition_ok(int32_t P) { return P > 0 && P % 256 == 0 && P <= PA_MAX_PARTITION; }
 
@@ -112,15 +131,19 @@ int pa_expand_block_tables(int32_t *dst, const int32_t *src, int32_t num_seqs, i
     }
 }
 
-int pa_varlen_attention(void *out, const void *q, const void *key_cache, const void *value_cache,
-                        const int32_t *cu_seqlens_q, const int32_t *seq_lens,
-                        const int32_t *block_tables, int32_t num_seqs, int32_t total_q,
-                        int32_t max_q_len, int32_t max_seq_len, int32_t max_blocks_per_seq,
-                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                        int32_t num_blocks, int32_t block_size, float scale,
-                        const float *sinks, int32_t dtype, int32_t partition_size,
-                        float *tmp_out, float *max_logits, float *exp_sums,
-                        int32_t max_partitions, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int varlen_attention_impl(pa_dispatch_info &rec, void *out, const void *q, const void *key_cache,
+                          const void *value_cache, const int32_t *cu_seqlens_q,
+                          const int32_t *seq_lens, const int32_t *block_tables, int32_t num_seqs,
+                          int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                          int32_t max_blocks_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t num_blocks, int32_t block_size, float scale,
+                          const float *sinks, int32_t dtype, int32_t partition_size,
+                          float *tmp_out, float *max_logits, float *exp_sums,
+                          int32_t max_partitions, void *stream) {
     try {
         if (!elt_bytes(dtype)) return PA_EUNSUPPORTED;
         if (num_seqs < 0 || total_q < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
@@ -134,6 +157,11 @@ int pa_varlen_attention(void *out, const void *q, const void *key_cache, const v
         const int lbs = log2_exact(block_size);
         if (block_size < 8 || block_size > 32 || lbs < 0) return PA_EUNSUPPORTED;
         if (partition_size != 0 && !partition_ok(partition_size)) return PA_EUNSUPPORTED;
+        if (partition_size != 0 && split_disabled_by_env()) {
+            partition_size = 0;
+            rec.split_disabled = 1;
+        }
+        rec.partition_size = partition_size;
         if (total_q == 0 || num_seqs == 0) return PA_OK;
         if (num_seqs > GRID_YZ_MAX || num_kv_heads > GRID_YZ_MAX) return PA_EUNSUPPORTED;
         if (max_q_len < 1 || max_seq_len < max_q_len) return PA_EINVAL;
@@ -187,25 +215,38 @@ int pa_varlen_attention(void *out, const void *q, const void *key_cache, const v
             const int64_t parts =
                 partition_size ? ((int64_t)max_seq_len + partition_size - 1) / partition_size : 1;
             if (parts > GRID_YZ_MAX) return PA_EUNSUPPORTED;
-            return hip_status(pa::launch_decode(p, (hipStream_t)stream));
+            pa::LaunchInfo li{};
+            const int lst = hip_status(pa::launch_decode(p, (hipStream_t)stream, &li));
+            record_launch(rec, p.per_token ? PA_PATH_DECODE_TOKEN : PA_PATH_DECODE, li);
+            return lst;
         }
         if (!pa::prefill_supported(dtype, head_dim, group)) return PA_EUNSUPPORTED;
-        return hip_status(pa::launch_prefill(p, (hipStream_t)stream));
+        pa::LaunchInfo li{};
+        const int lst = hip_status(pa::launch_prefill(p, (hipStream_t)stream, &li));
+        record_launch(rec, PA_PATH_TILED, li);
+        return lst;
     } catch (...) {
         return PA_EHIP;
     }
 }
 
-int pa_split_kv_reduce(void *out, const float *tmp_out, const float *max_logits,
-                       const float *exp_sums, const int32_t *cu_seqlens_q, const int32_t *seq_lens,
-                       int32_t num_seqs, int32_t total_q, int32_t num_q_heads, int32_t head_dim,
-                       const float *sinks, int32_t partition_size, int32_t max_partitions,
-                       int32_t dtype, void *stream) {
+int split_kv_reduce_impl(pa_dispatch_info &rec, void *out, const float *tmp_out,
+                         const float *max_logits, const float *exp_sums,
+                         const int32_t *cu_seqlens_q, const int32_t *seq_lens, int32_t num_seqs,
+                         int32_t total_q, int32_t num_q_heads, int32_t head_dim,
+                         const float *sinks, int32_t partition_size, int32_t max_partitions,
+                         int32_t dtype, void *stream) {
     try {
         if (!elt_bytes(dtype)) return PA_EUNSUPPORTED;
         if (num_seqs < 0 || total_q < 0 || num_q_heads <= 0 || head_dim <= 0) return PA_EINVAL;
         if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PA_EUNSUPPORTED;
         if (!partition_ok(partition_size)) return PA_EUNSUPPORTED;
+        if (split_disabled_by_env()) {  // attention finished every row in place
+            rec.path = PA_PATH_REDUCE_SKIP;
+            rec.split_disabled = 1;
+            return PA_OK;
+        }
+        rec.partition_size = partition_size;
         if (total_q == 0 || num_seqs == 0) return PA_OK;
         if (num_q_heads > GRID_YZ_MAX) return PA_EUNSUPPORTED;
         if (!out || !cu_seqlens_q || !seq_lens) return PA_EINVAL;
@@ -227,10 +268,55 @@ int pa_split_kv_reduce(void *out, const float *tmp_out, const float *max_logits,
         p.max_parts = max_partitions;
         p.sinks = sinks;
         p.dtype = dtype;
-        return hip_status(pa::launch_reduce(p, (hipStream_t)stream));
+        pa::LaunchInfo li{};
+        const int st = hip_status(pa::launch_reduce(p, (hipStream_t)stream, &li));
+        record_launch(rec, li.form ? PA_PATH_REDUCE_SLICES : PA_PATH_REDUCE_ROWS, li);
+        return st;
     } catch (...) {
         return PA_EHIP;
     }
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_varlen_attention(void *out, const void *q, const void *key_cache, const void *value_cache,
+                        const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                        const int32_t *block_tables, int32_t num_seqs, int32_t total_q,
+                        int32_t max_q_len, int32_t max_seq_len, int32_t max_blocks_per_seq,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t num_blocks, int32_t block_size, float scale,
+                        const float *sinks, int32_t dtype, int32_t partition_size,
+                        float *tmp_out, float *max_logits, float *exp_sums,
+                        int32_t max_partitions, void *stream) {
+    pa_dispatch_info rec{};
+    rec.status = varlen_attention_impl(
+        rec, out, q, key_cache, value_cache, cu_seqlens_q, seq_lens, block_tables, num_seqs,
+        total_q, max_q_len, max_seq_len, max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim,
+        num_blocks, block_size, scale, sinks, dtype, partition_size, tmp_out, max_logits,
+        exp_sums, max_partitions, stream);
+    g_last = rec;
+    return rec.status;
+}
+
+int pa_split_kv_reduce(void *out, const float *tmp_out, const float *max_logits,
+                       const float *exp_sums, const int32_t *cu_seqlens_q, const int32_t *seq_lens,
+                       int32_t num_seqs, int32_t total_q, int32_t num_q_heads, int32_t head_dim,
+                       const float *sinks, int32_t partition_size, int32_t max_partitions,
+                       int32_t dtype, void *stream) {
+    pa_dispatch_info rec{};
+    rec.status = split_kv_reduce_impl(rec, out, tmp_out, max_logits, exp_sums, cu_seqlens_q,
+                                      seq_lens, num_seqs, total_q, num_q_heads, head_dim, sinks,
+                                      partition_size, max_partitions, dtype, stream);
+    g_last = rec;
+    return rec.status;
+}
+
+int pa_last_dispatch(pa_dispatch_info *info) {
+    if (!info) return PA_EINVAL;
+    *info = g_last;
+    return PA_OK;
 }
 
 int32_t pa_pick_partition_size(const int32_t *host_seq_lens, int32_t num_seqs,
@@ -244,20 +330,22 @@ int32_t pa_pick_partition_size(const int32_t *host_seq_lens, int32_t num_seqs,
                 hipSuccess)
                 return -1;
         }
-        int64_t full512 = 0, full256 = 0;
         int32_t max_len = 0;
         for (int32_t r = 0; r < num_seqs; ++r) {
-            const int32_t s = host_seq_lens[r];
-            if (s < 0) return -1;
-            full512 += s / 512;
-            full256 += s / 256;
-            max_len = s > max_len ? s : max_len;
+            if (host_seq_lens[r] < 0) return -1;
+            max_len = host_seq_lens[r] > max_len ? host_seq_lens[r] : max_len;
         }
-        // Workgroups an unsplit launch already has, and the work budget.
+        // Workgroups an unsplit launch already has, and the budget: about one
+        // workgroup per CU (calibrated; every partition costs a start-up and a
+        // merge, so the largest partition that fills the GPU wins).
         const int64_t unsplit = (int64_t)num_kv_heads * num_seqs;
-        const int64_t budget = (int64_t)PA_SPLIT_WG_PER_CU * num_cus;
-        if (max_len <= 256 || unsplit >= 2 * budget) return 0;
-        if ((int64_t)num_kv_heads * full512 >= budget) return 512;
+        const int64_t budget = (int64_t)num_cus * PA_SPLIT_FILL_NUM / PA_SPLIT_FILL_DEN;
+        if (max_len <= 256 || unsplit >= budget) return 0;
+        for (int32_t P = PA_MAX_PARTITION; P > 256; P /= 2) {
+            int64_t w = 0;
+            for (int32_t r = 0; r < num_seqs; ++r) w += (host_seq_lens[r] + P - 1) / P;
+            if ((int64_t)num_kv_heads * w >= budget) return P;
+        }
         return 256;
     } catch (...) {
         return -1;

@@ -61,17 +61,26 @@ struct ReduceParams {
     int32_t dtype;
 };
 
+// What a launcher enqueued (for the dispatch record): grid in workgroups,
+// threads per workgroup, and the kernel's tile parameters.
+struct LaunchInfo {
+    int32_t grid[3];
+    int32_t block;
+    int32_t tile[3];
+    int32_t form;  // reduce: 0 = one wave per row, 1 = one workgroup per row slice
+};
+
 // Each launcher returns hipSuccess or the error of the launch; it assumes the
-// caller validated every host-visible argument.
+// caller validated every host-visible argument.  `li` may be NULL.
 hipError_t launch_reshape_and_cache(const void *key, const void *value, void *kc, void *vc,
                                     const int64_t *slots, int32_t num_tokens, int32_t row_bytes,
                                     int64_t num_slots, hipStream_t stream);
 hipError_t launch_expand_block_tables(int32_t *dst, const int32_t *src, int32_t num_seqs,
                                       int32_t src_stride, int32_t src_blocks, int32_t dst_stride,
                                       int32_t ratio, hipStream_t stream);
-hipError_t launch_decode(const AttnParams &p, hipStream_t stream);
-hipError_t launch_prefill(const AttnParams &p, hipStream_t stream);
-hipError_t launch_reduce(const ReduceParams &p, hipStream_t stream);
+hipError_t launch_decode(const AttnParams &p, hipStream_t stream, LaunchInfo *li);
+hipError_t launch_prefill(const AttnParams &p, hipStream_t stream, LaunchInfo *li);
+hipError_t launch_reduce(const ReduceParams &p, hipStream_t stream, LaunchInfo *li);
 
 // Whether a decode instantiation exists for this geometry.
 bool decode_supported(int dtype, int head_dim, int group);

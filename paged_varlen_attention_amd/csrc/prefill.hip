@@ -443,7 +443,7 @@ __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const 
 #endif
 
 template <int D>
-hipError_t launch_d(const AttnParams &p, hipStream_t stream) {
+hipError_t launch_d(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
     constexpr int N = PA_PREFILL_N(D), NST = PA_PREFILL_NST(D);
     const int TPW = 32 / p.group;
     const int BQ = PrefillCfg<D, N, NST>::NWV * TPW;
@@ -454,6 +454,7 @@ hipError_t launch_d(const AttnParams &p, hipStream_t stream) {
     if (items > INT32_MAX - 4096) return hipErrorInvalidConfiguration;
     const int64_t unit = XCD_CHUNK > 0 ? 8 * XCD_CHUNK : 1;
     const int blocks = (int)((items + unit - 1) / unit * unit);
+    if (li) *li = LaunchInfo{{blocks, 1, 1}, 256, {N, NST, BQ}, 0};
     hipLaunchKernelGGL((prefill_kernel<D, N, NST>), dim3(blocks), dim3(256), 0, stream, q);
     return hipGetLastError();
 }
@@ -465,11 +466,11 @@ bool prefill_supported(int dtype, int head_dim, int group) {
            group <= 8;
 }
 
-hipError_t launch_prefill(const AttnParams &p, hipStream_t stream) {
+hipError_t launch_prefill(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
     switch (p.head_dim) {
-        case 64: return launch_d<64>(p, stream);
-        case 128: return launch_d<128>(p, stream);
-        case 256: return launch_d<256>(p, stream);
+        case 64: return launch_d<64>(p, stream, li);
+        case 128: return launch_d<128>(p, stream, li);
+        case 256: return launch_d<256>(p, stream, li);
         default: return hipErrorInvalidValue;
     }
 }

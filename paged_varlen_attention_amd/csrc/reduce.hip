@@ -191,49 +191,37 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(const ReduceParams p) 
     }
 }
 
-template <typename T>
-hipError_t launch_t(const ReduceParams &p, hipStream_t stream) {
+template <typename T, int D>
+hipError_t launch_td(const ReduceParams &p, hipStream_t stream, LaunchInfo *li) {
     // The row form serialises a row's partitions in one wave: right for many
     // rows with few partitions; a few long rows keep the slice form.
     if (p.max_parts <= ROWS_MAX_PARTS) {
         const int blocks = (int)(((int64_t)p.total_q * p.hq + 3) / 4);
-        switch (p.head_dim) {
-            case 64:
-                hipLaunchKernelGGL((reduce_rows_kernel<T, 64>), dim3(blocks), dim3(256), 0, stream, p);
-                break;
-            case 128:
-                hipLaunchKernelGGL((reduce_rows_kernel<T, 128>), dim3(blocks), dim3(256), 0, stream, p);
-                break;
-            case 256:
-                hipLaunchKernelGGL((reduce_rows_kernel<T, 256>), dim3(blocks), dim3(256), 0, stream, p);
-                break;
-            default: return hipErrorInvalidValue;
-        }
-        return hipGetLastError();
-    }
-    switch (p.head_dim) {
-        case 64:
-            hipLaunchKernelGGL((reduce_kernel<T, 64>), dim3(p.total_q, p.hq, 1), dim3(RT), 0,
-                               stream, p);
-            break;
-        case 128:
-            hipLaunchKernelGGL((reduce_kernel<T, 128>), dim3(p.total_q, p.hq, 1), dim3(RT), 0,
-                               stream, p);
-            break;
-        case 256:
-            hipLaunchKernelGGL((reduce_kernel<T, 256>), dim3(p.total_q, p.hq, 256 / slice_of<256>()),
-                               dim3(RT), 0, stream, p);
-            break;
-        default: return hipErrorInvalidValue;
+        if (li) *li = LaunchInfo{{blocks, 1, 1}, 256, {0, 0, 0}, 0};
+        hipLaunchKernelGGL((reduce_rows_kernel<T, D>), dim3(blocks), dim3(256), 0, stream, p);
+    } else {
+        const dim3 grid(p.total_q, p.hq, D / slice_of<D>());
+        if (li) *li = LaunchInfo{{(int)grid.x, (int)grid.y, (int)grid.z}, RT, {0, 0, 0}, 1};
+        hipLaunchKernelGGL((reduce_kernel<T, D>), grid, dim3(RT), 0, stream, p);
     }
     return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_t(const ReduceParams &p, hipStream_t stream, LaunchInfo *li) {
+    switch (p.head_dim) {
+        case 64: return launch_td<T, 64>(p, stream, li);
+        case 128: return launch_td<T, 128>(p, stream, li);
+        case 256: return launch_td<T, 256>(p, stream, li);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
-hipError_t launch_reduce(const ReduceParams &p, hipStream_t stream) {
+hipError_t launch_reduce(const ReduceParams &p, hipStream_t stream, LaunchInfo *li) {
     if (p.total_q == 0) return hipSuccess;
-    return p.dtype == 1 ? launch_t<bf16_t>(p, stream) : launch_t<float>(p, stream);
+    return p.dtype == 1 ? launch_t<bf16_t>(p, stream, li) : launch_t<float>(p, stream, li);
 }
 
 }  // namespace pa

@@ -140,11 +140,43 @@ def test_partials_bytes():
 def test_partition_policy():
     """Host-only policy with an explicit CU count (no device query)."""
     import paged_varlen_attention_amd as pa
-    cus = 256
-    assert pa.pick_partition_size([100] * 32, 8, cus) == 0            # nothing longer than 256
-    assert pa.pick_partition_size([4000] * 32, 8, cus) == 512         # 8*32*7 >= 512 full partitions
-    assert pa.pick_partition_size([32768] * 4, 4, cus) == 512         # 4*4*64 = 1024 >= 512
-    assert pa.pick_partition_size([700] * 4, 4, cus) == 256           # few full 512s
+    cus = 256                                                         # budget 224 workgroups
+    assert pa.pick_partition_size([100] * 4, 8, cus) == 0             # nothing longer than 256
+    assert pa.pick_partition_size([4000] * 32, 8, cus) == 0           # 256 unsplit >= 224
+    assert pa.pick_partition_size([4000] * 16, 8, cus) == 2048        # 8*16*2 = 256 >= 224
+    assert pa.pick_partition_size([32768] * 4, 4, cus) == 2048        # 4*4*16 = 256; 4096 gives 128
+    assert pa.pick_partition_size([65536], 8, cus) == 2048            # 8*32 = 256
+    assert pa.pick_partition_size([700] * 4, 4, cus) == 256           # nothing fills: smallest
+    assert pa.pick_partition_size([8192] * 2, 8, cus) == 512          # 8*2*16 = 256
     assert pa.pick_partition_size([3000] * 512, 8, cus) == 0          # 4096 unsplit workgroups
     with pytest.raises(ValueError):
         pa.pick_partition_size([-5], 1, cus)
+
+
+def test_dispatch_record_and_no_split_switch(monkeypatch):
+    """The record of the last call on this thread, and PA_NO_SPLIT (checked on
+    calls that enqueue nothing: an empty batch and a rejected call)."""
+    import paged_varlen_attention_amd as pa
+    lib = _lib()
+    assert lib.pa_last_dispatch(None) == 1
+    monkeypatch.delenv("PA_NO_SPLIT", raising=False)
+    assert lib.pa_varlen_attention(*attn_args(total_q=0, out=None, q=None, P=512)) == 0
+    rec = pa.last_dispatch()
+    assert rec["path"] == "none" and rec["status"] == 0 and rec["partition_size"] == 512
+    assert not rec["split_disabled"] and rec["grid"] == (0, 0, 0)
+    monkeypatch.setenv("PA_NO_SPLIT", "1")
+    assert lib.pa_varlen_attention(*attn_args(total_q=0, out=None, q=None, P=512)) == 0
+    rec = pa.last_dispatch()
+    assert rec["partition_size"] == 0 and rec["split_disabled"]
+    # with the split off, the partials are not required
+    assert lib.pa_varlen_attention(*attn_args(total_q=0, out=None, q=None, P=512, tmp=None)) == 0
+    a = dict(out=FAKE, tmp=FAKE, ml=FAKE, es=FAKE, cu=FAKE, sl=FAKE, B=2, TQ=2, hq=4, d=64,
+             sinks=None, P=256, mp=2, dtype=1, stream=None)
+    args = [a[k] for k in ("out", "tmp", "ml", "es", "cu", "sl", "B", "TQ", "hq", "d", "sinks", "P",
+                           "mp", "dtype", "stream")]
+    assert lib.pa_split_kv_reduce(*args) == 0       # skipped: nothing is enqueued
+    assert pa.last_dispatch()["path"] == "reduce_skipped"
+    monkeypatch.setenv("PA_NO_SPLIT", "0")
+    assert lib.pa_varlen_attention(*attn_args(dtype=7)) == 2
+    rec = pa.last_dispatch()
+    assert rec["path"] == "none" and rec["status"] == 2
