@@ -76,7 +76,7 @@ enum {
 #define PA_MAX_GROUP 8          /* num_q_heads / num_kv_heads */
 #define PA_MAX_SEQS 65535       /* requests per call */
 #define PA_MAX_PARTITION 8192  /* largest partition_size accepted */
-#define PA_SPLIT_FILL_NUM 7     /* the partition policy aims for 7/8 of a workgroup per CU */
+#define PA_SPLIT_FILL_NUM 5     /* the partition policy aims for 5/8 of a workgroup per CU */
 #define PA_SPLIT_FILL_DEN 8
 
 /*

@@ -140,14 +140,16 @@ def test_partials_bytes():
 def test_partition_policy():
     """Host-only policy with an explicit CU count (no device query)."""
     import paged_varlen_attention_amd as pa
-    cus = 256                                                         # budget 224 workgroups
+    cus = 256                                                         # budget 160 workgroups
     assert pa.pick_partition_size([100] * 4, 8, cus) == 0             # nothing longer than 256
-    assert pa.pick_partition_size([4000] * 32, 8, cus) == 0           # 256 unsplit >= 224
-    assert pa.pick_partition_size([4000] * 16, 8, cus) == 2048        # 8*16*2 = 256 >= 224
+    assert pa.pick_partition_size([4000] * 20, 8, cus) == 0           # 160 unsplit >= 160
+    assert pa.pick_partition_size([4000] * 16, 8, cus) == 2048        # 8*16*2 = 256; 4096 gives 128
     assert pa.pick_partition_size([32768] * 4, 4, cus) == 2048        # 4*4*16 = 256; 4096 gives 128
-    assert pa.pick_partition_size([65536], 8, cus) == 2048            # 8*32 = 256
+    assert pa.pick_partition_size([65536], 8, cus) == 2048            # 8*32 = 256; 4096 gives 128
+    assert pa.pick_partition_size([40960], 8, cus) == 2048            # 8*20 = 160 reaches the budget
+    assert pa.pick_partition_size([30720], 8, cus) == 1024            # 8*30 = 240; 2048 gives 120
     assert pa.pick_partition_size([700] * 4, 4, cus) == 256           # nothing fills: smallest
-    assert pa.pick_partition_size([8192] * 2, 8, cus) == 512          # 8*2*16 = 256
+    assert pa.pick_partition_size([8192] * 2, 8, cus) == 512          # 8*2*16 = 256; 1024 gives 128
     assert pa.pick_partition_size([3000] * 512, 8, cus) == 0          # 4096 unsplit workgroups
     with pytest.raises(ValueError):
         pa.pick_partition_size([-5], 1, cus)
