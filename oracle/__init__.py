@@ -54,9 +54,11 @@ def _declare(lib):
     lib.pa_ref_num_threads.restype = ctypes.c_int
     lib.pa_ref_reshape_and_cache.argtypes = [P, P, P, P, P, I, I, I, I, I, I]
     lib.pa_ref_expand_block_tables.argtypes = [P, P, I, I, I, I, I]
+    lib.pa_ref_copy_blocks.argtypes = [P, P, P, P, P, I, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
     lib.pa_ref_attention.argtypes = [P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, I, I, I, D, I, P]
     lib.pa_ref_attention_partials.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
                                               D, I, I, I]
+    lib.pa_ref_copy_blocks.restype = ctypes.c_int
     lib.pa_ref_split_reduce.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P]
     for f in ("pa_ref_reshape_and_cache", "pa_ref_expand_block_tables", "pa_ref_attention",
               "pa_ref_attention_partials", "pa_ref_split_reduce"):
@@ -95,6 +97,21 @@ def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, lib=None
                                       _ptr(slot_mapping), T, hkv, d, nb, bs, _dtype_code(key.dtype))
     if rc:
         raise ValueError("oracle reshape_and_cache: bad arguments")
+
+
+def copy_blocks(dst_key, dst_value, src_key, src_value, pairs, lib=None) -> None:
+    """In place on host tensors: dst[pairs[i,1]] = src[pairs[i,0]] for K and V
+    (whole blocks), pairs int64 [n, 2]; out-of-pool pairs skipped."""
+    lib = lib or _load()
+    pairs = torch.as_tensor(pairs, dtype=torch.int64).contiguous()
+    nbs, nbd = src_key.shape[0], dst_key.shape[0]
+    block_bytes = src_key[0].numel() * src_key.element_size() if nbs else 0
+    if dst_key[0].numel() * dst_key.element_size() != block_bytes:
+        raise ValueError("block sizes differ")
+    rc = lib.pa_ref_copy_blocks(_ptr(dst_key), _ptr(dst_value), _ptr(src_key), _ptr(src_value),
+                                _ptr(pairs), int(pairs.shape[0]), block_bytes, nbs, nbd)
+    if rc:
+        raise ValueError("oracle copy_blocks: bad arguments")
 
 
 def expand_block_tables(block_tables: torch.Tensor, ratio: int, lib=None) -> torch.Tensor:

@@ -63,6 +63,21 @@ int pa_ref_reshape_and_cache(const void *key, const void *value, void *key_cache
     return 0;
 }
 
+int pa_ref_copy_blocks(void *dst_key, void *dst_value, const void *src_key, const void *src_value,
+                       const int64_t *pairs, int32_t num_pairs, int64_t block_bytes,
+                       int64_t num_src_blocks, int64_t num_dst_blocks) {
+    if (num_pairs < 0 || block_bytes <= 0 || num_src_blocks < 0 || num_dst_blocks < 0) return -1;
+    for (int32_t i = 0; i < num_pairs; ++i) {
+        int64_t s = pairs[2 * i], d = pairs[2 * i + 1];
+        if (s < 0 || s >= num_src_blocks || d < 0 || d >= num_dst_blocks) continue;
+        memcpy((char *)dst_key + d * block_bytes, (const char *)src_key + s * block_bytes,
+               (size_t)block_bytes);
+        memcpy((char *)dst_value + d * block_bytes, (const char *)src_value + s * block_bytes,
+               (size_t)block_bytes);
+    }
+    return 0;
+}
+
 int pa_ref_expand_block_tables(int32_t *dst, const int32_t *src, int32_t num_seqs,
                                int32_t src_stride, int32_t src_blocks, int32_t dst_stride,
                                int32_t ratio) {

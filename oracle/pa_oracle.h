@@ -59,6 +59,15 @@ int pa_ref_reshape_and_cache(const void *key, const void *value, void *key_cache
                              int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                              int32_t block_size, int32_t dtype);
 
+/* Block copy between two caches (the KV-offloading article: evicting blocks to
+ * a host tier and restoring them, by block-id lists): for each pair i,
+ * dst[pairs[2i+1]] = src[pairs[2i]] for K and V, whole blocks of block_bytes,
+ * in pair order; pairs naming a block outside either pool are skipped.  A
+ * byte copy. */
+int pa_ref_copy_blocks(void *dst_key, void *dst_value, const void *src_key, const void *src_value,
+                       const int64_t *pairs, int32_t num_pairs, int64_t block_bytes,
+                       int64_t num_src_blocks, int64_t num_dst_blocks);
+
 /* Kernel-page view of a block table whose blocks hold `ratio` kernel pages:
  * dst[r][ratio*b + j] = ratio * src[r][b] + j, and -1 stays -1. */
 int pa_ref_expand_block_tables(int32_t *dst, const int32_t *src, int32_t num_seqs,

@@ -65,6 +65,13 @@ def cases():
         q=[[[1, 0]]],
         cache_rows={str(i): {"k": [[[i, 0]]], "v": [[[1, i]]]} for i in range(3)},
         expected_out=[[[7.0 / 15.0, 10.0 / 15.0]]])
+    c["copy_blocks_pairs"] = dict(
+        source="KV-offloading article: blocks move between the GPU cache and a host tier by block-id lists (evict and restore); a block is one page of every KV head",
+        derivation="src blocks s_b filled with b*10 + slot (K) and b*10 + slot + 100 (V); pairs (2,0), (0,1), (5,1): dst[0] = s_2, dst[1] = s_0, the pair naming src block 5 of a 3-block pool is skipped",
+        dtype="f32", block_shape=[2, 1, 1], num_src_blocks=3, num_dst_blocks=2,
+        pairs=[[2, 0], [0, 1], [5, 1]],
+        expected_dst_key=[[[[20.0]], [[21.0]]], [[[0.0]], [[1.0]]]],
+        expected_dst_value=[[[[120.0]], [[121.0]]], [[[100.0]], [[101.0]]]])
     c["reshape_and_cache_scatter"] = dict(
         source="vllm-metal kernel walkthrough, 'three Metal kernels': reshape_and_cache scatters projected K/V into the paged cache; a slot is block*block_size + offset",
         derivation="bs 2, 3 blocks, slots [5,-1,0]: token 0 -> block 2 offset 1, token 1 skipped, token 2 -> block 0 offset 0; every other slot keeps its previous content (0 here)",

@@ -430,6 +430,56 @@ def pin_sinks(lib):
             assert (out[0, h] - expect).abs().max() <= 1e-13, (sig, h)
 
 
+def pin_golden_copy_blocks(lib):
+    c = golden("copy_blocks_pairs")
+    shp = tuple(c["block_shape"])
+    nbs, nbd = c["num_src_blocks"], c["num_dst_blocks"]
+    sk = torch.zeros((nbs,) + shp, dtype=torch.float32)
+    for b in range(nbs):
+        sk[b] = (b * 10 + torch.arange(shp[0], dtype=torch.float32)).view(shp[0], 1, 1)
+    sv = sk + 100
+    dk = torch.full((nbd,) + shp, -1.0)
+    dv = dk.clone()
+    oracle.copy_blocks(dk, dv, sk, sv, c["pairs"], lib=lib)
+    assert torch.equal(dk, torch.tensor(c["expected_dst_key"])), dk
+    assert torch.equal(dv, torch.tensor(c["expected_dst_value"])), dv
+
+
+def pin_copy_blocks(lib):
+    """Against torch indexing (bitwise, NaN payloads kept), pair order for
+    repeated destinations, out-of-pool pairs skipped, and evict + restore
+    giving back the cache bit for bit."""
+    g = torch.Generator().manual_seed(5)
+    for dt, shape in ((torch.bfloat16, (16, 2, 64)), (torch.float32, (8, 4, 128))):
+        nbs, nbd = 12, 9
+        sk = torch.randn((nbs,) + shape, generator=g).to(dt)
+        sv = torch.randn((nbs,) + shape, generator=g).to(dt)
+        sk[3, 0, 0, :4] = float("nan")
+        dk = torch.randn((nbd,) + shape, generator=g).to(dt)
+        dv = torch.randn((nbd,) + shape, generator=g).to(dt)
+        pairs = torch.tensor([[3, 0], [7, 8], [0, 4], [11, 2], [20, 1], [5, -1], [6, 4]])
+        ek, ev = dk.clone(), dv.clone()
+        for s_, d_ in pairs.tolist():  # later pairs win
+            if 0 <= s_ < nbs and 0 <= d_ < nbd:
+                ek[d_] = sk[s_]
+                ev[d_] = sv[s_]
+        oracle.copy_blocks(dk, dv, sk, sv, pairs, lib=lib)
+        assert torch.equal(dk.view(torch.uint8), ek.view(torch.uint8))
+        assert torch.equal(dv.view(torch.uint8), ev.view(torch.uint8))
+        # evict three blocks to a host pool, wipe them, restore: bitwise round trip
+        hk = torch.zeros((4,) + shape, dtype=dt)
+        hv = torch.zeros_like(hk)
+        keep_k, keep_v = sk.clone(), sv.clone()
+        out = torch.tensor([[3, 0], [9, 1], [1, 2]])
+        oracle.copy_blocks(hk, hv, sk, sv, out, lib=lib)
+        sk[[3, 9, 1]] = 0
+        sv[[3, 9, 1]] = 0
+        oracle.copy_blocks(sk, sv, hk, hv, out.flip(1), lib=lib)
+        assert torch.equal(sk.view(torch.uint8), keep_k.view(torch.uint8))
+        assert torch.equal(sv.view(torch.uint8), keep_v.view(torch.uint8))
+
+
 ALL_PINS = [pin_golden_attention, pin_golden_split, pin_golden_cache_write, pin_dense,
             pin_cache_write_vs_index_copy, pin_page_permutation, pin_page_size,
-            pin_split_invariance, pin_single_request, pin_closed_forms, pin_golden_sink, pin_sinks]
+            pin_split_invariance, pin_single_request, pin_closed_forms, pin_golden_sink, pin_sinks,
+            pin_golden_copy_blocks, pin_copy_blocks]

@@ -35,6 +35,10 @@ MUTATIONS = [
     ("cache write: block offset dropped", "size_t dst = ((size_t)blk * block_size + (size_t)off) * row;", "size_t dst = ((size_t)blk * block_size) * row;"),
     ("block-table view: wrong page order", "v * ratio + j", "v + j * ratio"),
     ("V read through the K cache", "out_row[d] += scores[i] * load_elem(a->vc,", "out_row[d] += scores[i] * load_elem(a->kc,"),
+    ("block copy: source and destination ids swapped",
+     "int64_t s = pairs[2 * i], d = pairs[2 * i + 1];", "int64_t d = pairs[2 * i], s = pairs[2 * i + 1];"),
+    ("block copy: V taken from the K pool", "memcpy((char *)dst_value + d * block_bytes, (const char *)src_value",
+     "memcpy((char *)dst_value + d * block_bytes, (const char *)src_key"),
     ("sink left out of the denominator", "double z = a->sinks ? exp(sink - m) : 0.0;", "double z = 0.0;"),
     ("sink merged in natural units", "double sink2 = sinks ? (double)sinks[h] * LOG2E : -INFINITY;",
      "double sink2 = sinks ? (double)sinks[h] : -INFINITY;"),
