@@ -249,6 +249,37 @@ def pmc_traffic():
         return None
 
 
+def block_offload(device, n_blocks=4096, reps=10):
+    """pa_copy_blocks between the GPU cache and a pinned host pool: 4,096
+    blocks of 16 tokens x 8 KV heads x 128 bf16 (32 KiB each for K and for V,
+    256 MiB per direction), evict (device -> host) and restore (host ->
+    device), GB/s of block bytes moved."""
+    import torch
+    import paged_varlen_attention_amd as pa
+    shape = (16, 8, 128)
+    gk = torch.randn((n_blocks * 2,) + shape, device=device).to(torch.bfloat16)
+    gv = torch.randn_like(gk)
+    hk = torch.empty((n_blocks,) + shape, dtype=torch.bfloat16).pin_memory()
+    hv = torch.empty_like(hk).pin_memory()
+    g = torch.Generator().manual_seed(9)
+    src = torch.randperm(n_blocks * 2, generator=g)[:n_blocks]
+    out = torch.stack([src, torch.arange(n_blocks)], 1).to(torch.int64).to(device)
+    back = out.flip(1).contiguous()
+    nbytes = 2 * n_blocks * gk[0].numel() * 2
+    res = {"blocks": n_blocks, "block_bytes_per_tensor": gk[0].numel() * 2}
+    for name, args in (("evict_GB/s", (hk, hv, gk, gv, out)), ("restore_GB/s", (gk, gv, hk, hv, back))):
+        pa.copy_blocks(*args)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            pa.copy_blocks(*args)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 2)
+    return res
+
+
 def cpu_baseline(w, budget_s=10.0):
     """The fp64 oracle, as it stands, on whole batches of the same workload
     until about budget_s of wall time has passed."""
@@ -409,6 +440,8 @@ def main():
                 "step_ms_percentiles": k3["step_ms_percentiles"],
                 "warm_ms_per_step": round(s3w * 1e3, 5)}
             log(f"{name}: {sec_out[name]}")
+        sec_out["kv_block_offload_bf16"] = block_offload(device)
+        log(f"kv block offload: {sec_out['kv_block_offload_bf16']}")
         result["secondary"] = sec_out
 
     if args.copy_calibration:

@@ -101,6 +101,26 @@ int pa_reshape_and_cache(const void *key, const void *value, void *key_cache, vo
                          void *stream);
 
 /*
+ * pa_copy_blocks -- copy whole cache blocks from one cache to another by id
+ * pairs: the data movement of evicting KV blocks to a host tier and restoring
+ * them (KV-offloading article; on MI355X host memory is not the GPU's, so
+ * blocks are copied rather than re-pointed).
+ *   for each i: dst_key[pairs[i][1]] = src_key[pairs[i][0]], same for V,
+ * whole blocks of block_bytes (= block_size * Hkv * D * elt for the caches of
+ * this library).  Either cache, and `pairs` (int64 [num_pairs][2]), may be
+ * device memory or PINNED host memory (allocated pinned, e.g. hipHostMalloc
+ * or torch's pin_memory); pageable host memory is refused with PA_EINVAL.
+ * Pairs naming a block outside [0, num_src_blocks) or [0, num_dst_blocks) are
+ * skipped.  Destination ids must be distinct, and no block may be both read
+ * and written by one call (pairs run in parallel).  block_bytes must be a
+ * positive multiple of 16 and every pointer 16-byte aligned.
+ * Errors: PA_EINVAL, PA_EHIP.
+ */
+int pa_copy_blocks(void *dst_key, void *dst_value, const void *src_key, const void *src_value,
+                   const int64_t *pairs, int32_t num_pairs, int64_t block_bytes,
+                   int64_t num_src_blocks, int64_t num_dst_blocks, void *stream);
+
+/*
  * pa_expand_block_tables -- kernel-page view of a block table whose cache
  * blocks hold `ratio` kernel pages each (unified-memory article, section six:
  * one 144-token block = nine 16-token pages, the cache viewed as

@@ -48,10 +48,12 @@ def _load() -> ctypes.CDLL:
     lib.pa_partials_bytes.argtypes = [I, I, I, I, ctypes.POINTER(ctypes.c_size_t),
                                       ctypes.POINTER(ctypes.c_size_t)]
     lib.pa_last_dispatch.argtypes = [P]
+    lib.pa_copy_blocks.argtypes = [P, P, P, P, P, I, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P]
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     for f in ("pa_reshape_and_cache", "pa_expand_block_tables", "pa_varlen_attention",
-              "pa_split_kv_reduce", "pa_partials_bytes", "pa_abi_version", "pa_last_dispatch"):
+              "pa_split_kv_reduce", "pa_partials_bytes", "pa_abi_version", "pa_last_dispatch",
+              "pa_copy_blocks"):
         getattr(lib, f).restype = ctypes.c_int
     return lib
 
@@ -131,6 +133,41 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.T
         _dev(slot_mapping, "slot_mapping", torch.int64, dev), T, hkv, d, nb, bs,
         _dtype_code(key.dtype), _stream(dev))
     _check("pa_reshape_and_cache", st)
+
+
+def _gpu_visible(t: torch.Tensor, name: str) -> ctypes.c_void_p:
+    """Pointer of a dense tensor the GPU can address: on the GPU, or pinned host."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type == "cpu" and not t.is_pinned():
+        raise ValueError(f"{name} is in pageable host memory: allocate it pinned (pin_memory=True)")
+    if t.device.type not in ("cpu", "cuda"):
+        raise ValueError(f"{name} must be on the GPU or in pinned host memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def copy_blocks(dst_key: torch.Tensor, dst_value: torch.Tensor, src_key: torch.Tensor,
+                src_value: torch.Tensor, pairs: torch.Tensor) -> None:
+    """dst[pairs[i, 1]] = src[pairs[i, 0]] for K and V (whole blocks, caches
+    [num_blocks, ...]); each tensor on the GPU or in pinned host memory.
+    pairs: int64 [n, 2] (GPU or pinned).  Out-of-pool pairs are skipped;
+    destination ids must be distinct."""
+    if src_key.shape[1:] != dst_key.shape[1:] or src_key.dtype != dst_key.dtype:
+        raise ValueError("caches differ in block shape or dtype")
+    if src_value.shape != src_key.shape or dst_value.shape != dst_key.shape:
+        raise ValueError("K and V caches differ")
+    if pairs.dtype != torch.int64 or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be int64 [n, 2]")
+    dev = next((t.device for t in (dst_key, src_key, pairs) if t.device.type == "cuda"),
+               torch.device("cuda", torch.cuda.current_device()))
+    block_bytes = src_key[0].numel() * src_key.element_size() if src_key.shape[0] else 16
+    st = lib.pa_copy_blocks(_gpu_visible(dst_key, "dst_key"), _gpu_visible(dst_value, "dst_value"),
+                            _gpu_visible(src_key, "src_key"), _gpu_visible(src_value, "src_value"),
+                            _gpu_visible(pairs, "pairs"), pairs.shape[0], block_bytes,
+                            src_key.shape[0], dst_key.shape[0], _stream(dev))
+    _check("pa_copy_blocks", st)
 
 
 def expand_block_tables(block_tables: torch.Tensor, ratio: int,

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_api.cpp", "cache_write.hip", "decode.hip", "reduce.hip", "prefill.hip"]
+SOURCES = ["pa_api.cpp", "cache_write.hip", "decode.hip", "reduce.hip", "prefill.hip",
+           "block_copy.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -319,6 +319,48 @@ int pa_last_dispatch(pa_dispatch_info *info) {
     return PA_OK;
 }
 
+// Device address of memory the GPU may touch: device memory as is, pinned
+// host memory through its mapping; nullptr for pageable host memory.
+static void *device_address(const void *ptr) {
+    hipPointerAttribute_t a{};
+    if (hipPointerGetAttributes(&a, ptr) != hipSuccess) {
+        (void)hipGetLastError();  // clear the query's error
+        return nullptr;
+    }
+    if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) return const_cast<void *>(ptr);
+    if (a.type == hipMemoryTypeHost && a.devicePointer && a.hostPointer)
+        return static_cast<char *>(a.devicePointer) +
+               (static_cast<const char *>(ptr) - static_cast<const char *>(a.hostPointer));
+    return nullptr;
+}
+
+int pa_copy_blocks(void *dst_key, void *dst_value, const void *src_key, const void *src_value,
+                   const int64_t *pairs, int32_t num_pairs, int64_t block_bytes,
+                   int64_t num_src_blocks, int64_t num_dst_blocks, void *stream) {
+    try {
+        if (num_pairs < 0 || block_bytes <= 0 || block_bytes % 16 != 0 || num_src_blocks < 0 ||
+            num_dst_blocks < 0)
+            return PA_EINVAL;
+        if (num_pairs == 0) return PA_OK;
+        if (num_pairs > 65535 * 256 || num_src_blocks > INT64_MAX / block_bytes ||
+            num_dst_blocks > INT64_MAX / block_bytes)
+            return PA_EINVAL;
+        if (!dst_key || !dst_value || !src_key || !src_value || !pairs) return PA_EINVAL;
+        if (!aligned16(dst_key) || !aligned16(dst_value) || !aligned16(src_key) ||
+            !aligned16(src_value) || reinterpret_cast<uintptr_t>(pairs) % 8 != 0)
+            return PA_EINVAL;
+        void *dk = device_address(dst_key), *dv = device_address(dst_value);
+        void *sk = device_address(src_key), *sv = device_address(src_value);
+        void *pr = device_address(pairs);
+        if (!dk || !dv || !sk || !sv || !pr) return PA_EINVAL;
+        return hip_status(pa::launch_copy_blocks(dk, dv, sk, sv, static_cast<const int64_t *>(pr),
+                                                 num_pairs, block_bytes, num_src_blocks,
+                                                 num_dst_blocks, (hipStream_t)stream));
+    } catch (...) {
+        return PA_EHIP;
+    }
+}
+
 int32_t pa_pick_partition_size(const int32_t *host_seq_lens, int32_t num_seqs,
                                int32_t num_kv_heads, int32_t num_cus) {
     try {

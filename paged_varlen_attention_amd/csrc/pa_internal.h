@@ -78,6 +78,9 @@ hipError_t launch_reshape_and_cache(const void *key, const void *value, void *kc
 hipError_t launch_expand_block_tables(int32_t *dst, const int32_t *src, int32_t num_seqs,
                                       int32_t src_stride, int32_t src_blocks, int32_t dst_stride,
                                       int32_t ratio, hipStream_t stream);
+hipError_t launch_copy_blocks(void *dst_k, void *dst_v, const void *src_k, const void *src_v,
+                              const int64_t *pairs, int32_t num_pairs, int64_t block_bytes,
+                              int64_t num_src, int64_t num_dst, hipStream_t stream);
 hipError_t launch_decode(const AttnParams &p, hipStream_t stream, LaunchInfo *li);
 hipError_t launch_prefill(const AttnParams &p, hipStream_t stream, LaunchInfo *li);
 hipError_t launch_reduce(const ReduceParams &p, hipStream_t stream, LaunchInfo *li);

@@ -182,3 +182,15 @@ def test_dispatch_record_and_no_split_switch(monkeypatch):
     assert lib.pa_varlen_attention(*attn_args(dtype=7)) == 2
     rec = pa.last_dispatch()
     assert rec["path"] == "none" and rec["status"] == 2
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(n=-1), 1), (dict(bb=0), 1), (dict(bb=24), 1), (dict(ns=-1), 1), (dict(nd=-1), 1),
+    (dict(n=0), 0), (dict(dk=None), 1), (dict(pairs=None), 1), (dict(sk=ctypes.c_void_p(0x100008)), 1),
+])
+def test_copy_blocks_rejects(over, status):
+    """Checks that return before any pointer is looked at or work enqueued."""
+    a = dict(dk=FAKE, dv=FAKE, sk=FAKE, sv=FAKE, pairs=FAKE, n=2, bb=32768, ns=4, nd=4, stream=None)
+    a.update(over)
+    args = [a[k] for k in ("dk", "dv", "sk", "sv", "pairs", "n", "bb", "ns", "nd", "stream")]
+    assert _lib().pa_copy_blocks(*args) == status
