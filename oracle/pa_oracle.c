@@ -42,6 +42,53 @@ static int elem_bytes(int dtype) {
     return dtype == PA_REF_F32 ? 4 : (dtype == PA_REF_BF16 ? 2 : 0);
 }
 
+/* ---- OCP E4M3, written from the format's definition ---- */
+
+double pa_ref_e4m3_value(uint8_t code) {
+    int negative = code >> 7;
+    int e = (code >> 3) & 15; /* biased exponent */
+    int m = code & 7;         /* mantissa */
+    double mag;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        mag = ldexp((double)m / 8.0, -6);        /* subnormal: 0.m * 2^(1 - 7) */
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, e - 7); /* normal: 1.m * 2^(e - 7) */
+    return negative ? -mag : mag;
+}
+
+/* Nearest code by exhaustive search over the 127 non-negative finite codes,
+ * whose values increase with the code; of two equally near codes the one with
+ * an even last mantissa bit wins. */
+uint8_t pa_ref_e4m3_encode(double y) {
+    if (isnan(y)) return 0x7F;
+    uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    double a = fabs(y);
+    if (a > 448.0) a = 448.0; /* saturate (infinities too) */
+    int best = 0;
+    double best_err = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        double err = fabs(pa_ref_e4m3_value((uint8_t)c) - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
+int pa_ref_e4m3_values(double *out, const uint8_t *codes, int64_t n) {
+    if (n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) out[i] = pa_ref_e4m3_value(codes[i]);
+    return 0;
+}
+
+int pa_ref_e4m3_encode_f32(uint8_t *out, const float *y, int64_t n) {
+    if (n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) out[i] = pa_ref_e4m3_encode((double)y[i]);
+    return 0;
+}
+
 int pa_ref_reshape_and_cache(const void *key, const void *value, void *key_cache,
                              void *value_cache, const int64_t *slot_mapping, int32_t num_tokens,
                              int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
@@ -59,6 +106,39 @@ int pa_ref_reshape_and_cache(const void *key, const void *value, void *key_cache
         size_t dst = ((size_t)blk * block_size + (size_t)off) * row;
         memcpy((char *)key_cache + dst, (const char *)key + (size_t)t * row, row);
         memcpy((char *)value_cache + dst, (const char *)value + (size_t)t * row, row);
+    }
+    return 0;
+}
+
+/* fl32(x / s): the quotient of two values that are exact in float32, rounded
+ * to float32.  Dividing in double and rounding the double quotient to float
+ * gives the correctly rounded float32 quotient (double carries more than
+ * 2*24 + 2 significant bits, so the second rounding cannot go wrong). */
+static float quotient_f32(double x, double s) { return (float)(x / s); }
+
+int pa_ref_reshape_and_cache_fp8(const void *key, const void *value, uint8_t *key_cache,
+                                 uint8_t *value_cache, const int64_t *slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t num_blocks, int32_t block_size, int32_t dtype,
+                                 const float *k_scale, const float *v_scale) {
+    if (!elem_bytes(dtype) || num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || !k_scale || !v_scale)
+        return -1;
+    int64_t num_slots = (int64_t)num_blocks * block_size;
+    size_t row = (size_t)num_kv_heads * head_dim; /* elements (= bytes in the cache) per token */
+    for (int32_t t = 0; t < num_tokens; ++t) {
+        int64_t s = slot_mapping[t];
+        if (s < 0) continue;
+        if (s >= num_slots) return -1;
+        for (int32_t g = 0; g < num_kv_heads; ++g)
+            for (int32_t d = 0; d < head_dim; ++d) {
+                size_t src = (size_t)t * row + (size_t)g * head_dim + d;
+                size_t dst = (size_t)s * row + (size_t)g * head_dim + d;
+                key_cache[dst] = pa_ref_e4m3_encode(
+                    quotient_f32(load_elem(key, src, dtype), (double)k_scale[g]));
+                value_cache[dst] = pa_ref_e4m3_encode(
+                    quotient_f32(load_elem(value, src, dtype), (double)v_scale[g]));
+            }
     }
     return 0;
 }
@@ -104,7 +184,18 @@ typedef struct {
     int32_t num_seqs, total_q, max_blocks, hq, hkv, d, num_blocks, bs, dtype;
     double scale;
     const float *sinks; /* NULL, or one logit per query head */
+    int32_t kv_dtype;   /* dtype, or PA_REF_FP8_E4M3 */
+    const float *k_scale, *v_scale; /* 8-bit caches: one scale per KV head */
 } args_t;
+
+/* Cached element `idx` of KV head g as a double: exact widening, or for an
+ * 8-bit cache the code's value times the head's scale. */
+static double load_kv(const args_t *a, const void *cache, const float *scale, size_t idx,
+                      int32_t g) {
+    if (a->kv_dtype == PA_REF_FP8_E4M3)
+        return pa_ref_e4m3_value(((const uint8_t *)cache)[idx]) * (double)scale[g];
+    return load_elem(cache, idx, a->kv_dtype);
+}
 
 /* Where logical key i of request r lives: index of element 0 of that key's
  * row for KV head g, in elements.  -1 if the block table does not hold it. */
@@ -130,7 +221,7 @@ static int scores_for(const args_t *a, int32_t r, int32_t t, int32_t h, int32_t 
         if (kr < 0) return -1;
         double dot = 0.0;
         for (int32_t d = 0; d < a->d; ++d)
-            dot += load_elem(a->q, qbase + d, a->dtype) * load_elem(a->kc, (size_t)kr + d, a->dtype);
+            dot += load_elem(a->q, qbase + d, a->dtype) * load_kv(a, a->kc, a->k_scale, (size_t)kr + d, g);
         scores[i - k0] = a->scale * dot;
     }
     return 0;
@@ -168,7 +259,7 @@ static int attention_row(const args_t *a, int32_t t, int32_t h, double *out_row,
     for (int32_t i = 0; i < nk; ++i) {
         int64_t vr = key_row(a, r, i, g);
         for (int32_t d = 0; d < a->d; ++d)
-            out_row[d] += scores[i] * load_elem(a->vc, (size_t)vr + d, a->dtype);
+            out_row[d] += scores[i] * load_kv(a, a->vc, a->v_scale, (size_t)vr + d, g);
     }
     for (int32_t d = 0; d < a->d; ++d) out_row[d] /= z;
     return 0;
@@ -176,6 +267,11 @@ static int attention_row(const args_t *a, int32_t t, int32_t h, double *out_row,
 
 static int check_args(const args_t *a) {
     if (!elem_bytes(a->dtype)) return -1;
+    if (a->kv_dtype == PA_REF_FP8_E4M3) {
+        if (!a->k_scale || !a->v_scale) return -1;
+    } else if (a->kv_dtype != a->dtype) {
+        return -1;
+    }
     if (a->num_seqs < 0 || a->total_q < 0 || a->hq <= 0 || a->hkv <= 0 || a->d <= 0 || a->bs <= 0)
         return -1;
     if (a->hq % a->hkv) return -1;
@@ -195,10 +291,11 @@ int pa_ref_attention(double *out, const int32_t *tok, const int32_t *head, int32
                      const int32_t *block_tables, int32_t num_seqs, int32_t total_q,
                      int32_t max_blocks_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
                      int32_t head_dim, int32_t num_blocks, int32_t block_size, double scale,
-                     int32_t dtype, const float *sinks) {
+                     int32_t dtype, int32_t kv_dtype, const float *k_scale,
+                     const float *v_scale, const float *sinks) {
     args_t a = {q, key_cache, value_cache, cu_seqlens_q, seq_lens, block_tables, num_seqs,
                 total_q, max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, num_blocks,
-                block_size, dtype, scale, sinks};
+                block_size, dtype, scale, sinks, kv_dtype, k_scale, v_scale};
     if (check_args(&a)) return -1;
     int64_t rows = (tok == NULL) ? (int64_t)total_q * num_q_heads : n_rows;
     int32_t maxk = longest_seq(&a);
@@ -228,10 +325,11 @@ int pa_ref_attention_partials(double *o, double *m, double *l, const void *q,
                               int32_t max_blocks_per_seq, int32_t num_q_heads,
                               int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                               int32_t block_size, double scale, int32_t dtype,
+                              int32_t kv_dtype, const float *k_scale, const float *v_scale,
                               int32_t partition_size, int32_t max_parts) {
     args_t a = {q, key_cache, value_cache, cu_seqlens_q, seq_lens, block_tables, num_seqs,
                 total_q, max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, num_blocks,
-                block_size, dtype, scale, NULL};
+                block_size, dtype, scale, NULL, kv_dtype, k_scale, v_scale};
     if (check_args(&a) || partition_size <= 0 || max_parts <= 0) return -1;
     int64_t rows = (int64_t)total_q * num_q_heads;
     int err = 0;
@@ -276,7 +374,7 @@ int pa_ref_attention_partials(double *o, double *m, double *l, const void *q,
                 for (int32_t i = 0; i < k1 - k0; ++i) {
                     int64_t vr = key_row(&a, r, k0 + i, g);
                     for (int32_t d = 0; d < head_dim; ++d)
-                        orow[d] += scores[i] * load_elem(a.vc, (size_t)vr + d, dtype);
+                        orow[d] += scores[i] * load_kv(&a, a.vc, a.v_scale, (size_t)vr + d, g);
                 }
                 for (int32_t d = 0; d < head_dim; ++d) orow[d] /= lk;
                 m[sidx] = mk;

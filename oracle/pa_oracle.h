@@ -34,6 +34,22 @@
  * 16 bits of a float32).  Every input value is widened exactly to double and
  * all arithmetic is double; results are returned unrounded in double.
  *
+ * 8-bit KV cache (PA_REF_FP8_E4M3).  The pages list KV quantisation kernels
+ * (the kernel walkthrough's kernel table) but give no scheme, so this one is
+ * ours, stated here in full:
+ *   - the element format is the OCP 8-bit float E4M3 ("e4m3fn"): sign bit,
+ *     4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the
+ *     subnormals m/8 * 2^-6; the pattern with all exponent and mantissa bits
+ *     set is NaN; there are no infinities; the largest magnitude is 448;
+ *   - each KV head g has one float32 scale for K (k_scale[g]) and one for V
+ *     (v_scale[g]); a stored code c stands for value(c) * scale[g];
+ *   - the cache write stores, for an input element x of head g,
+ *       code = E(fl32(x / scale[g])),
+ *     where fl32 is the correctly rounded float32 quotient and E picks the
+ *     nearest E4M3 value (ties to the code with an even last mantissa bit),
+ *     magnitudes above 448 (infinities included) giving +-448 and NaN giving
+ *     the code 0x7F.  The sign of zero is kept.
+ *
  * Return value of every function: 0 on success, -1 on an argument the oracle
  * cannot interpret (bad dtype, negative sizes, a key index outside the block
  * table or the pool, or ctx < 0).
@@ -47,7 +63,17 @@
 extern "C" {
 #endif
 
-enum { PA_REF_F32 = 0, PA_REF_BF16 = 1 };
+enum { PA_REF_F32 = 0, PA_REF_BF16 = 1, PA_REF_FP8_E4M3 = 2 };
+
+/* Value of one E4M3 code (NaN for 0x7F and 0xFF). */
+double pa_ref_e4m3_value(uint8_t code);
+
+/* E(y) as defined above, for y already rounded to float32 by the caller. */
+uint8_t pa_ref_e4m3_encode(double y);
+
+/* Array forms of the two functions above (for the pins). */
+int pa_ref_e4m3_values(double *out, const uint8_t *codes, int64_t n);
+int pa_ref_e4m3_encode_f32(uint8_t *out, const float *y, int64_t n);
 
 /* Threads the OpenMP runtime will use for the row loops. */
 int pa_ref_num_threads(void);
@@ -58,6 +84,17 @@ int pa_ref_reshape_and_cache(const void *key, const void *value, void *key_cache
                              void *value_cache, const int64_t *slot_mapping, int32_t num_tokens,
                              int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                              int32_t block_size, int32_t dtype);
+
+/* Quantising cache write into 8-bit caches: for t in [0, T) with slot
+ * s = slot_mapping[t] >= 0, head g and element d,
+ *   key_cache[s / bs][s % bs][g][d] = E(fl32(key[t][g][d] / k_scale[g])),
+ * likewise value with v_scale.  Rows are PA_REF_F32 or PA_REF_BF16 (`dtype`);
+ * scales are float32 [num_kv_heads], finite and > 0. */
+int pa_ref_reshape_and_cache_fp8(const void *key, const void *value, uint8_t *key_cache,
+                                 uint8_t *value_cache, const int64_t *slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t num_blocks, int32_t block_size, int32_t dtype,
+                                 const float *k_scale, const float *v_scale);
 
 /* Block copy between two caches (the KV-offloading article: evicting blocks to
  * a host tier and restoring them, by block-id lists): for each pair i,
@@ -77,14 +114,18 @@ int pa_ref_expand_block_tables(int32_t *dst, const int32_t *src, int32_t num_seq
 /* Attention for selected (token, head) pairs: out[n][D] (double) for
  * n in [0, n_rows), row n = (tok[n], head[n]).  Pass tok = head = NULL to
  * compute every (t, h) in the natural order t*Hq + h (out = [total_q][Hq][D]).
- * sinks: NULL, or float32 [num_q_heads] sink logits (see above). */
+ * sinks: NULL, or float32 [num_q_heads] sink logits (see above).
+ * kv_dtype: the caches' element type, equal to dtype or PA_REF_FP8_E4M3; for
+ * the latter k_scale and v_scale are float32 [num_kv_heads] (NULL otherwise)
+ * and each cached element is read as value(code) * scale of its KV head. */
 int pa_ref_attention(double *out, const int32_t *tok, const int32_t *head, int32_t n_rows,
                      const void *q, const void *key_cache, const void *value_cache,
                      const int32_t *cu_seqlens_q, const int32_t *seq_lens,
                      const int32_t *block_tables, int32_t num_seqs, int32_t total_q,
                      int32_t max_blocks_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
                      int32_t head_dim, int32_t num_blocks, int32_t block_size, double scale,
-                     int32_t dtype, const float *sinks);
+                     int32_t dtype, int32_t kv_dtype, const float *k_scale,
+                     const float *v_scale, const float *sinks);
 
 /* Split-KV partials for every (t, h): partition k of the query at absolute
  * position p covers keys [k*P, min((k+1)*P, p+1)), k < ceil((p+1)/P).
@@ -92,7 +133,7 @@ int pa_ref_attention(double *out, const int32_t *tok, const int32_t *head, int32
  *   l[t][h][k]    = sum 2^(s_i*log2(e) - m)
  *   o[t][h][k][:] = sum 2^(s_i*log2(e) - m) * v_i / l
  * Entries for k >= ceil((p+1)/P) are left untouched.  Arrays are dense with
- * max_parts partitions per (t, h). */
+ * max_parts partitions per (t, h).  kv_dtype, k_scale, v_scale: as above. */
 int pa_ref_attention_partials(double *o, double *m, double *l, const void *q,
                               const void *key_cache, const void *value_cache,
                               const int32_t *cu_seqlens_q, const int32_t *seq_lens,
@@ -100,6 +141,7 @@ int pa_ref_attention_partials(double *o, double *m, double *l, const void *q,
                               int32_t max_blocks_per_seq, int32_t num_q_heads,
                               int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
                               int32_t block_size, double scale, int32_t dtype,
+                              int32_t kv_dtype, const float *k_scale, const float *v_scale,
                               int32_t partition_size, int32_t max_parts);
 
 /* Merge of the partials above: with n = ceil((p+1)/P), M = max_k m_k,

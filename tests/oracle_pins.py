@@ -479,7 +479,162 @@ def pin_copy_blocks(lib):
         assert torch.equal(sv.view(torch.uint8), keep_v.view(torch.uint8))
 
 
+# ------------------------------------------------------------ 8-bit KV cache
+
+# Values of E4M3 codes worked out by hand from the format (sign, 4-bit exponent
+# with bias 7, 3-bit mantissa; exponent 0 = subnormals m/8 * 2^-6).
+E4M3_BY_HAND = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 / 8 * 2.0 ** -6, 0x08: 2.0 ** -6,
+                0x38: 1.0, 0xB8: -1.0, 0x3F: 1.875, 0x40: 2.0, 0x77: 240.0, 0x7E: 448.0,
+                0xFE: -448.0}
+
+
+def _torch_e4m3_values():
+    return torch.arange(256, dtype=torch.int64).to(torch.uint8).view(torch.float8_e4m3fn).double()
+
+
+def pin_e4m3_format(lib):
+    """All 256 code values against torch's float8_e4m3fn (a library decode),
+    hand-worked values, the sign of zero, NaN codes and monotonic order."""
+    codes = torch.arange(256, dtype=torch.int64).to(torch.uint8)
+    v = oracle.e4m3_values(codes, lib=lib)
+    ref = _torch_e4m3_values()
+    nan = torch.isnan(ref)
+    assert torch.equal(torch.isnan(v), nan) and nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert torch.equal(v[~nan], ref[~nan])
+    for c, x in E4M3_BY_HAND.items():
+        assert float(v[c]) == x, (hex(c), float(v[c]), x)
+    assert math.copysign(1.0, float(v[0x80])) == -1.0 and float(v[0x80]) == 0.0
+    assert bool((v[1:127] > v[0:126]).all()) and bool((v[0x81:0xFF] < v[0x80:0xFE]).all())
+
+
+def pin_e4m3_encode(lib):
+    """The encoder: code -> value -> code round trip, every midpoint between
+    neighbouring codes going to the even mantissa, points just off each
+    midpoint, saturation and NaN, and torch's own float32 -> float8_e4m3fn
+    rounding on random in-range values across all binades."""
+    vals = _torch_e4m3_values()
+    finite = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    back = oracle.e4m3_encode(vals[finite].float(), lib=lib)
+    assert back.tolist() == finite
+    mids, expect, above, below = [], [], [], []
+    for c in range(0, 0x7E):
+        a, b = float(vals[c]), float(vals[c + 1])
+        m = (a + b) / 2  # exact in float32 (one more mantissa bit)
+        mids.append(m)
+        expect.append(c if c % 2 == 0 else c + 1)
+        above.append(np.nextafter(np.float32(m), np.float32(np.inf)))
+        below.append(np.nextafter(np.float32(m), np.float32(-np.inf)))
+    mids_t = torch.tensor(mids, dtype=torch.float32)
+    assert oracle.e4m3_encode(mids_t, lib=lib).tolist() == expect
+    assert oracle.e4m3_encode(-mids_t, lib=lib).tolist() == [e | 0x80 for e in expect]
+    up = oracle.e4m3_encode(torch.tensor(np.array(above, dtype=np.float32)), lib=lib).tolist()
+    dn = oracle.e4m3_encode(torch.tensor(np.array(below, dtype=np.float32)), lib=lib).tolist()
+    assert up == list(range(1, 0x7F)) and dn == list(range(0, 0x7E))
+    special = torch.tensor([448.0, 449.0, 464.0, 480.0, 1e30, float("inf"), -500.0,
+                            float("-inf"), float("nan"), -0.0, 1e-30, -1e-30, 2.0 ** -10,
+                            1.5 * 2.0 ** -10, 2.0 ** -149], dtype=torch.float32)
+    assert oracle.e4m3_encode(special, lib=lib).tolist() == [
+        0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x7F, 0x80, 0x00, 0x80, 0x00, 0x01, 0x00]
+    g = torch.Generator().manual_seed(11)
+    mag = torch.pow(10.0, torch.empty(200000).uniform_(-5.0, 2.66, generator=g))
+    sign = torch.where(torch.rand(200000, generator=g) < 0.5, -1.0, 1.0)
+    y = (mag * sign).clamp(-448.0, 448.0).float()
+    ours = oracle.e4m3_encode(y, lib=lib)
+    theirs = y.to(torch.float8_e4m3fn).view(torch.uint8)
+    assert torch.equal(ours, theirs), int((ours != theirs).sum())
+
+
+def pin_golden_fp8_cache_write(lib):
+    c = golden("fp8_cache_write")
+    hkv, d, nb, bs = c["num_kv_heads"], c["head_dim"], c["num_blocks"], c["block_size"]
+    f = lambda x: [[[float(e) for e in h] for h in t] for t in x]  # noqa: E731  ("inf", "nan")
+    key = torch.tensor(f(c["key"]), dtype=torch.float32)
+    value = torch.tensor(f(c["value"]), dtype=torch.float32)
+    kc = torch.zeros((nb, bs, hkv, d), dtype=torch.uint8)
+    vc = torch.zeros_like(kc)
+    oracle.reshape_and_cache_fp8(key, value, kc, vc, torch.tensor(c["slot_mapping"]),
+                                 torch.tensor(c["k_scale"]), torch.tensor(c["v_scale"]), lib=lib)
+    assert kc.reshape(nb * bs, hkv * d).tolist() == c["expected_key_codes"], kc
+    assert vc.reshape(nb * bs, hkv * d).tolist() == c["expected_value_codes"], vc
+
+
+def fp8_case(w, seed):
+    """Workload ``w`` with its caches quantised to E4M3 (per-head scales drawn
+    by workloads.kv_scales); NaN slots stay NaN codes."""
+    import dataclasses
+    ks, vs = W.kv_scales(seed, w.num_kv_heads)
+    return dataclasses.replace(w, key_cache=oracle.quantize_cache(w.key_cache, ks),
+                               value_cache=oracle.quantize_cache(w.value_cache, vs),
+                               k_scale=ks, v_scale=vs)
+
+
+def dequantised(w):
+    """float64 caches value(code) * scale, decoded by torch (not the oracle)."""
+    import dataclasses
+    kc = w.key_cache.double() * w.k_scale.double()[None, None, :, None]
+    vc = w.value_cache.double() * w.v_scale.double()[None, None, :, None]
+    return dataclasses.replace(w, key_cache=kc, value_cache=vc, k_scale=None, v_scale=None)
+
+
+def pin_fp8_cache_write(lib):
+    """The quantising write against torch: fp32 division, clamp to +-448,
+    torch's float32 -> float8_e4m3fn rounding; bf16 and fp32 rows."""
+    g = torch.Generator().manual_seed(13)
+    for dt in (torch.bfloat16, torch.float32):
+        T, hkv, d, nb, bs = 37, 3, 64, 6, 8
+        key = (torch.randn(T, hkv, d, generator=g) * 3).to(dt)
+        value = (torch.randn(T, hkv, d, generator=g) * 3).to(dt)
+        ks = torch.tensor([0.004, 0.01, 0.37], dtype=torch.float32)
+        vs = torch.tensor([0.0123, 1.0, 0.005], dtype=torch.float32)
+        slots = torch.randperm(nb * bs, generator=g)[:T]
+        slots[5] = -1
+        kc = torch.zeros((nb, bs, hkv, d), dtype=torch.uint8)
+        vc = torch.zeros_like(kc)
+        oracle.reshape_and_cache_fp8(key, value, kc, vc, slots, ks, vs, lib=lib)
+        for x, sc, cache in ((key, ks, kc), (value, vs, vc)):
+            y = (x.float() / sc[None, :, None]).clamp(-448.0, 448.0)
+            ref = torch.zeros_like(cache).view(nb * bs, hkv, d)
+            keep = slots >= 0
+            ref[slots[keep]] = y[keep].to(torch.float8_e4m3fn).view(torch.uint8)
+            assert torch.equal(cache.view(nb * bs, hkv, d), ref), dt
+
+
+def pin_fp8_attention(lib):
+    """Attention over 8-bit caches: against the dense numpy reference on
+    torch-decoded, scaled caches; with power-of-two scales bit-identical to
+    the oracle on an fp32 cache holding the decoded values; split partials
+    merged back to the same rows."""
+    import dataclasses
+    for i, w in enumerate(micro_cases()):
+        wq = fp8_case(w, 50 + i)
+        out = run(wq, lib)
+        ref = dense_numpy(dequantised(wq))
+        err = (out - ref).abs().max()
+        assert err <= 1e-12, (w.name, float(err))
+        for P in (8, 16):
+            o, m, l = oracle.attention_partials(wq.q, wq.key_cache, wq.value_cache,
+                                                wq.cu_seqlens_q, wq.seq_lens, wq.block_tables,
+                                                wq.scale, P, k_scale=wq.k_scale,
+                                                v_scale=wq.v_scale, lib=lib)
+            red = oracle.split_reduce(o, m, l, wq.cu_seqlens_q, wq.seq_lens, P, lib=lib)
+            rel = ((red - out).abs() / out.abs().clamp_min(1e-3)).max()
+            assert rel <= 1e-12, (w.name, P, float(rel))
+    for i, w in enumerate(micro_cases()):
+        if w.dtype != torch.float32:
+            continue
+        hkv = w.num_kv_heads
+        ks = torch.tensor([2.0 ** -(6 + h) for h in range(hkv)], dtype=torch.float32)
+        vs = torch.tensor([2.0 ** -(5 - h) for h in range(hkv)], dtype=torch.float32)
+        wq = dataclasses.replace(w, key_cache=oracle.quantize_cache(w.key_cache, ks),
+                                 value_cache=oracle.quantize_cache(w.value_cache, vs),
+                                 k_scale=ks, v_scale=vs)
+        d = dequantised(wq)
+        plain = dataclasses.replace(d, key_cache=d.key_cache.float(), value_cache=d.value_cache.float())
+        assert bitwise_equal(run(wq, lib), run(plain, lib)), w.name
+
+
 ALL_PINS = [pin_golden_attention, pin_golden_split, pin_golden_cache_write, pin_dense,
             pin_cache_write_vs_index_copy, pin_page_permutation, pin_page_size,
             pin_split_invariance, pin_single_request, pin_closed_forms, pin_golden_sink, pin_sinks,
-            pin_golden_copy_blocks, pin_copy_blocks]
+            pin_golden_copy_blocks, pin_copy_blocks, pin_e4m3_format, pin_e4m3_encode,
+            pin_golden_fp8_cache_write, pin_fp8_cache_write, pin_fp8_attention]

@@ -34,7 +34,7 @@ MUTATIONS = [
     ("cache write: K and V swapped", "memcpy((char *)key_cache + dst, (const char *)key", "memcpy((char *)key_cache + dst, (const char *)value"),
     ("cache write: block offset dropped", "size_t dst = ((size_t)blk * block_size + (size_t)off) * row;", "size_t dst = ((size_t)blk * block_size) * row;"),
     ("block-table view: wrong page order", "v * ratio + j", "v + j * ratio"),
-    ("V read through the K cache", "out_row[d] += scores[i] * load_elem(a->vc,", "out_row[d] += scores[i] * load_elem(a->kc,"),
+    ("V read through the K cache", "out_row[d] += scores[i] * load_kv(a, a->vc,", "out_row[d] += scores[i] * load_kv(a, a->kc,"),
     ("block copy: source and destination ids swapped",
      "int64_t s = pairs[2 * i], d = pairs[2 * i + 1];", "int64_t d = pairs[2 * i], s = pairs[2 * i + 1];"),
     ("block copy: V taken from the K pool", "memcpy((char *)dst_value + d * block_bytes, (const char *)src_value",
@@ -42,6 +42,20 @@ MUTATIONS = [
     ("sink left out of the denominator", "double z = a->sinks ? exp(sink - m) : 0.0;", "double z = 0.0;"),
     ("sink merged in natural units", "double sink2 = sinks ? (double)sinks[h] * LOG2E : -INFINITY;",
      "double sink2 = sinks ? (double)sinks[h] : -INFINITY;"),
+    ("e4m3: exponent bias 8", "mag = ldexp(1.0 + (double)m / 8.0, e - 7);", "mag = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    ("e4m3: subnormal exponent", "mag = ldexp((double)m / 8.0, -6);", "mag = ldexp((double)m / 8.0, -7);"),
+    ("e4m3: ties away from zero", "(err == best_err && (c & 1) == 0)", "(err == best_err)"),
+    ("e4m3: overflow to NaN", "if (a > 448.0) a = 448.0; /* saturate (infinities too) */",
+     "if (a > 448.0) return (uint8_t)(sign | 0x7F);"),
+    ("e4m3: sign dropped", "return (uint8_t)(sign | best);", "return (uint8_t)best;"),
+    ("fp8 write: scale multiplies", "quotient_f32(load_elem(key, src, dtype), (double)k_scale[g])",
+     "quotient_f32(load_elem(key, src, dtype), 1.0 / (double)k_scale[g])"),
+    ("fp8 write: V with the K scale", "quotient_f32(load_elem(value, src, dtype), (double)v_scale[g])",
+     "quotient_f32(load_elem(value, src, dtype), (double)k_scale[g])"),
+    ("fp8 write: quotient not rounded to float32", "static float quotient_f32(double x, double s) { return (float)(x / s); }",
+     "static double quotient_f32(double x, double s) { return x / s; }"),
+    ("fp8 read: V with the K scale", "load_kv(a, a->vc, a->v_scale,", "load_kv(a, a->vc, a->k_scale,"),
+    ("fp8 read: scale of the wrong head", "* (double)scale[g];", "* (double)scale[0];"),
 ]
 
 

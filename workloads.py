@@ -65,6 +65,9 @@ class Workload:
     kernel_page_ratio: int = 1
     description: str = ""
     sinks: Optional[torch.Tensor] = None  # float32 [Hq] attention-sink logits, or None
+    # 8-bit caches: float32 [Hkv] per-head scales of K and V (None for bf16/fp32 caches)
+    k_scale: Optional[torch.Tensor] = None
+    v_scale: Optional[torch.Tensor] = None
 
     @property
     def num_seqs(self) -> int:
@@ -293,6 +296,26 @@ CONFIGS = {
     "long_decode_bf16": long_decode_bf16,
     "spec_verify_bf16": spec_verify_bf16,
 }
+
+
+def kv_scales(seed: int, num_kv_heads: int):
+    """Per-KV-head scales for an 8-bit E4M3 cache holding N(0,1) data: K and V
+    scales drawn U[0.008, 0.016] (so |x| / scale reaches the format's largest
+    magnitude, 448, for |x| between 3.6 and 7.2: the tails saturate, as with a
+    scale calibrated to the bulk of the data).  Returns (k_scale, v_scale)."""
+    rng = np.random.default_rng(seed)
+    ks = rng.uniform(0.008, 0.016, size=num_kv_heads).astype(np.float32)
+    vs = rng.uniform(0.008, 0.016, size=num_kv_heads).astype(np.float32)
+    return torch.from_numpy(ks), torch.from_numpy(vs)
+
+
+def random_fp8_codes(seed: int, shape) -> torch.Tensor:
+    """Uniform draws over the 254 finite E4M3 codes (NaN codes 0x7F, 0xFF
+    excluded), as raw uint8."""
+    rng = np.random.default_rng(seed)
+    c = rng.integers(0, 254, size=int(np.prod(shape)), dtype=np.int64)
+    c = c + (c >= 0x7F)  # 0..126 and 128..254: skips 0x7F, never reaches 0xFF
+    return torch.from_numpy(c.astype(np.uint8)).reshape(shape)
 
 
 def random_case(seed: int, *, num_seqs: int, max_q: int, max_ctx: int, num_q_heads: int,
