@@ -26,7 +26,16 @@
  *    Every call only enqueues work on it and returns without synchronising.
  *  - Tensors are dense and row-major with the shapes given; no strides.
  *  - dtype: PA_F32 (IEEE float32) or PA_BF16 (bfloat16, the upper half of a
- *    float32).  Q, the caches and `out` share one dtype.  Partials are float32.
+ *    float32), the type of Q, `out` and new K/V rows.  Partials are float32.
+ *  - kv_dtype: the caches' element type, either equal to dtype or PA_FP8_E4M3:
+ *    8-bit OCP E4M3 codes (sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ *    subnormals, NaN = 0x7F/0xFF, no infinities, largest magnitude 448) with
+ *    one float32 scale per KV head for K (k_scale) and one for V (v_scale): a
+ *    stored code c of KV head g stands for value(c) * scale[g].  The pages
+ *    name KV quantisation kernels (kernel walkthrough, kernel table) but give no
+ *    scheme; this one is the library's own.  k_scale / v_scale are device
+ *    float32 [num_kv_heads], finite and > 0, and must be NULL for caches of
+ *    dtype.  8-bit caches are read with bf16 queries (dtype PA_BF16).
  *  - Layouts:
  *      q, out            [total_q, num_q_heads, head_dim]
  *      key/value rows    [num_tokens, num_kv_heads, head_dim]
@@ -62,7 +71,7 @@
 extern "C" {
 #endif
 
-enum { PA_F32 = 0, PA_BF16 = 1 };
+enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 };
 
 enum {
     PA_OK = 0,
@@ -85,19 +94,29 @@ enum {
  *
  * For every t in [0, num_tokens): s = slot_mapping[t]; if s < 0 the token is
  * skipped; otherwise key_cache[s / block_size][s % block_size][:][:] = key[t]
- * and likewise for value.  A bit copy: bytes land unchanged.  Slots must be
- * unique among the tokens of one call (else which row wins is unspecified).
+ * and likewise for value.  With kv_dtype == dtype this is a bit copy: bytes
+ * land unchanged.  With kv_dtype == PA_FP8_E4M3 every element x of KV head g is
+ * stored as the E4M3 code of the correctly rounded float32 quotient
+ * x / scale[g]: the nearest code, ties to an even mantissa; magnitudes above
+ * 448 (infinities included) store +-448, NaN stores 0x7F, the sign of zero is
+ * kept.  Slots must be unique among the tokens of one call (else which row
+ * wins is unspecified).
  *   key, value        [num_tokens, num_kv_heads, head_dim], dtype
- *   key/value_cache   [num_blocks, block_size, num_kv_heads, head_dim], dtype
+ *   key/value_cache   [num_blocks, block_size, num_kv_heads, head_dim], kv_dtype
  *   slot_mapping      int64 [num_tokens]
+ *   k_scale, v_scale  float32 [num_kv_heads] for PA_FP8_E4M3, else NULL
  * block_size may be any positive value here (e.g. 144): a slot is the same
  * memory position in every page-size view of the cache.
- * Errors: PA_EINVAL (null pointer with num_tokens > 0, sizes <= 0),
- *         PA_EUNSUPPORTED (dtype; num_kv_heads*head_dim*elt not a multiple of 16 bytes).
+ * Errors: PA_EINVAL (null pointer with num_tokens > 0, sizes <= 0, scales given
+ *         for a cache of dtype or missing for an 8-bit one),
+ *         PA_EUNSUPPORTED (dtype or kv_dtype; a cache row of
+ *         num_kv_heads*head_dim elements not a multiple of 16 bytes; an 8-bit
+ *         cache with head_dim not a multiple of 16).
  */
 int pa_reshape_and_cache(const void *key, const void *value, void *key_cache, void *value_cache,
                          const int64_t *slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                          int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t dtype,
+                         int32_t kv_dtype, const float *k_scale, const float *v_scale,
                          void *stream);
 
 /*
@@ -165,9 +184,15 @@ int pa_expand_block_tables(int32_t *dst, const int32_t *src, int32_t num_seqs, i
  *   pa_split_kv_reduce, which adds it once).  Values must be finite or -inf
  *   (-inf is the same as no sink).
  *
+ * kv_dtype, k_scale, v_scale: the caches' element type and, for PA_FP8_E4M3,
+ *   the per-KV-head scales (see the conventions).  An 8-bit cache gives the
+ *   result of the definition above over the keys value(code) * k_scale and
+ *   values value(code) * v_scale.
+ *
  * Host scalars: max_q_len = max over requests of q_len (>= 1 unless
  * total_q == 0), max_seq_len = max of seq_lens; both must be upper bounds.
- * Supported: dtype PA_F32 / PA_BF16; head_dim 64, 128, 256; block_size 8, 16,
+ * Supported: dtype PA_F32 / PA_BF16 with kv_dtype == dtype, or dtype PA_BF16
+ * with kv_dtype PA_FP8_E4M3; head_dim 64, 128, 256; block_size 8, 16,
  * 32; num_q_heads % num_kv_heads == 0 with group size <= PA_MAX_GROUP.
  * Errors: PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE (P > 0 and a partial
  * buffer is NULL or max_partitions too small), PA_EHIP.
@@ -178,7 +203,8 @@ int pa_varlen_attention(void *out, const void *q, const void *key_cache, const v
                         int32_t max_q_len, int32_t max_seq_len, int32_t max_blocks_per_seq,
                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                         int32_t num_blocks, int32_t block_size, float scale,
-                        const float *sinks, int32_t dtype, int32_t partition_size,
+                        const float *sinks, int32_t dtype, int32_t kv_dtype,
+                        const float *k_scale, const float *v_scale, int32_t partition_size,
                         float *tmp_out, float *max_logits, float *exp_sums,
                         int32_t max_partitions, void *stream);
 

@@ -157,11 +157,15 @@ def quantize_cache(cache: torch.Tensor, scale, lib=None) -> torch.Tensor:
     """A whole [num_blocks, block_size, Hkv, D] cache quantised slot by slot with
     the cache write above (NaN slots stay NaN codes); returns float8_e4m3fn."""
     nb, bs, hkv, d = cache.shape
-    rows = cache.reshape(nb * bs, hkv, d).contiguous()
-    out = torch.empty((nb, bs, hkv, d), dtype=torch.uint8)
+    rows = cache.reshape(nb * bs, hkv, d)
+    # slots that are NaN throughout (unused pool slots) store the NaN code the
+    # write gives NaN; only the others go through the write
+    used = ~torch.isnan(rows.float()).all(dim=2).all(dim=1)
+    slots = torch.nonzero(used).flatten().to(torch.int64).contiguous()
+    src = rows[slots].contiguous()
+    out = torch.full((nb, bs, hkv, d), 0x7F, dtype=torch.uint8)
     spare = torch.empty_like(out)
-    slots = torch.arange(nb * bs, dtype=torch.int64)
-    reshape_and_cache_fp8(rows, rows, out, spare, slots, scale, scale, lib=lib)
+    reshape_and_cache_fp8(src, src, out, spare, slots, scale, scale, lib=lib)
     return out.view(torch.float8_e4m3fn)
 
 

@@ -57,10 +57,21 @@ double pa_ref_e4m3_value(uint8_t code) {
     return negative ? -mag : mag;
 }
 
-/* Nearest code by exhaustive search over the 127 non-negative finite codes,
- * whose values increase with the code; of two equally near codes the one with
- * an even last mantissa bit wins. */
-uint8_t pa_ref_e4m3_encode(double y) {
+/* Values of the 127 non-negative finite codes 0x00..0x7E, filled once by
+ * e4m3_table_init() before any parallel region reads it. */
+static double e4m3_table[0x7F];
+static int e4m3_table_ready = 0;
+
+static void e4m3_table_init(void) {
+    if (e4m3_table_ready) return;
+    for (int c = 0; c <= 0x7E; ++c) e4m3_table[c] = pa_ref_e4m3_value((uint8_t)c);
+    e4m3_table_ready = 1;
+}
+
+/* Nearest code by exhaustive search over the 127 non-negative finite codes
+ * (the table must be initialised); of two equally near codes the one with an
+ * even last mantissa bit wins. */
+static uint8_t e4m3_encode_searched(double y) {
     if (isnan(y)) return 0x7F;
     uint8_t sign = signbit(y) ? 0x80 : 0x00;
     double a = fabs(y);
@@ -68,13 +79,18 @@ uint8_t pa_ref_e4m3_encode(double y) {
     int best = 0;
     double best_err = INFINITY;
     for (int c = 0; c <= 0x7E; ++c) {
-        double err = fabs(pa_ref_e4m3_value((uint8_t)c) - a);
+        double err = fabs(e4m3_table[c] - a);
         if (err < best_err || (err == best_err && (c & 1) == 0)) {
             best = c;
             best_err = err;
         }
     }
     return (uint8_t)(sign | best);
+}
+
+uint8_t pa_ref_e4m3_encode(double y) {
+    e4m3_table_init();
+    return e4m3_encode_searched(y);
 }
 
 int pa_ref_e4m3_values(double *out, const uint8_t *codes, int64_t n) {
@@ -85,7 +101,8 @@ int pa_ref_e4m3_values(double *out, const uint8_t *codes, int64_t n) {
 
 int pa_ref_e4m3_encode_f32(uint8_t *out, const float *y, int64_t n) {
     if (n < 0) return -1;
-    for (int64_t i = 0; i < n; ++i) out[i] = pa_ref_e4m3_encode((double)y[i]);
+    e4m3_table_init();
+    for (int64_t i = 0; i < n; ++i) out[i] = e4m3_encode_searched((double)y[i]);
     return 0;
 }
 
@@ -126,17 +143,22 @@ int pa_ref_reshape_and_cache_fp8(const void *key, const void *value, uint8_t *ke
         return -1;
     int64_t num_slots = (int64_t)num_blocks * block_size;
     size_t row = (size_t)num_kv_heads * head_dim; /* elements (= bytes in the cache) per token */
+    for (int32_t t = 0; t < num_tokens; ++t)
+        if (slot_mapping[t] >= num_slots) return -1;
+    e4m3_table_init();
+    /* tokens are independent (slots are distinct), so the loop over them is
+     * split across threads; each element's arithmetic is unchanged */
+#pragma omp parallel for schedule(static)
     for (int32_t t = 0; t < num_tokens; ++t) {
         int64_t s = slot_mapping[t];
         if (s < 0) continue;
-        if (s >= num_slots) return -1;
         for (int32_t g = 0; g < num_kv_heads; ++g)
             for (int32_t d = 0; d < head_dim; ++d) {
                 size_t src = (size_t)t * row + (size_t)g * head_dim + d;
                 size_t dst = (size_t)s * row + (size_t)g * head_dim + d;
-                key_cache[dst] = pa_ref_e4m3_encode(
+                key_cache[dst] = e4m3_encode_searched(
                     quotient_f32(load_elem(key, src, dtype), (double)k_scale[g]));
-                value_cache[dst] = pa_ref_e4m3_encode(
+                value_cache[dst] = e4m3_encode_searched(
                     quotient_f32(load_elem(value, src, dtype), (double)v_scale[g]));
             }
     }

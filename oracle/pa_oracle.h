@@ -89,7 +89,8 @@ int pa_ref_reshape_and_cache(const void *key, const void *value, void *key_cache
  * s = slot_mapping[t] >= 0, head g and element d,
  *   key_cache[s / bs][s % bs][g][d] = E(fl32(key[t][g][d] / k_scale[g])),
  * likewise value with v_scale.  Rows are PA_REF_F32 or PA_REF_BF16 (`dtype`);
- * scales are float32 [num_kv_heads], finite and > 0. */
+ * scales are float32 [num_kv_heads], finite and > 0.  Slots must be distinct
+ * (tokens are written in parallel). */
 int pa_ref_reshape_and_cache_fp8(const void *key, const void *value, uint8_t *key_cache,
                                  uint8_t *value_cache, const int64_t *slot_mapping,
                                  int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,

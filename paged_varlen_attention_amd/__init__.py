@@ -21,7 +21,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
 
-PA_F32, PA_BF16 = 0, 1
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP = 0, 1, 2, 3, 4
 
 
@@ -38,10 +38,10 @@ def _load() -> ctypes.CDLL:
             "(there is no fallback implementation)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
-    lib.pa_reshape_and_cache.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
+    lib.pa_reshape_and_cache.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, P, P]
     lib.pa_expand_block_tables.argtypes = [P, P, I, I, I, I, I, P]
     lib.pa_varlen_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, P,
-                                        I, I, P, P, P, I, P]
+                                        I, I, P, P, I, P, P, P, I, P]
     lib.pa_split_kv_reduce.argtypes = [P, P, P, P, P, P, I, I, I, I, P, I, I, I, P]
     lib.pa_pick_partition_size.argtypes = [P, I, I, I]
     lib.pa_pick_partition_size.restype = ctypes.c_int32
@@ -72,6 +72,30 @@ def _dtype_code(dt: torch.dtype) -> int:
     if dt == torch.bfloat16:
         return PA_BF16
     raise TypeError(f"unsupported dtype {dt}; use float32 or bfloat16")
+
+
+def _kv_code(cache: torch.Tensor, row_dtype: torch.dtype) -> int:
+    """Cache element type: 8-bit caches (float8_e4m3fn, or raw uint8 codes) are
+    E4M3; any other cache must have the row dtype."""
+    if cache.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return PA_FP8_E4M3
+    if cache.dtype != row_dtype:
+        raise TypeError(f"cache dtype {cache.dtype} differs from {row_dtype}")
+    return _dtype_code(cache.dtype)
+
+
+def _scales(k_scale, v_scale, kv_code: int, hkv: int, dev):
+    if kv_code != PA_FP8_E4M3:
+        if k_scale is not None or v_scale is not None:
+            raise ValueError("k_scale/v_scale apply to 8-bit caches only")
+        return ctypes.c_void_p(0), ctypes.c_void_p(0)
+    if k_scale is None or v_scale is None:
+        raise ValueError("8-bit caches need k_scale and v_scale (float32 [num_kv_heads])")
+    for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        if t.shape != (hkv,):
+            raise ValueError(f"{n} must be [num_kv_heads]")
+    return (_dev(k_scale, "k_scale", torch.float32, dev),
+            _dev(v_scale, "v_scale", torch.float32, dev))
 
 
 def _dev(t: Optional[torch.Tensor], name: str, dtype=None, device=None) -> ctypes.c_void_p:
@@ -118,20 +142,28 @@ def alloc_partials(total_q: int, num_q_heads: int, head_dim: int, max_parts: int
 
 
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
-                      value_cache: torch.Tensor, slot_mapping: torch.Tensor) -> None:
-    """key/value [T, Hkv, D]; caches [num_blocks, block_size, Hkv, D]; slot_mapping int64 [T]."""
+                      value_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                      k_scale: Optional[torch.Tensor] = None,
+                      v_scale: Optional[torch.Tensor] = None) -> None:
+    """key/value [T, Hkv, D]; caches [num_blocks, block_size, Hkv, D]; slot_mapping int64 [T].
+    8-bit caches (float8_e4m3fn or uint8) store E4M3 codes of row / scale and
+    need k_scale and v_scale (float32 [Hkv] on the GPU)."""
     T, hkv, d = key.shape
     nb, bs, chkv, cd = key_cache.shape
     if (chkv, cd) != (hkv, d) or value.shape != key.shape or value_cache.shape != key_cache.shape:
         raise ValueError("reshape_and_cache: shape mismatch")
     if slot_mapping.shape != (T,):
         raise ValueError("slot_mapping must be [num_tokens]")
+    if value_cache.dtype != key_cache.dtype:
+        raise TypeError("key_cache and value_cache differ in dtype")
     dev = key.device
+    kv = _kv_code(key_cache, key.dtype)
+    ks, vs = _scales(k_scale, v_scale, kv, hkv, dev)
     st = lib.pa_reshape_and_cache(
         _dev(key, "key", device=dev), _dev(value, "value", key.dtype, dev),
-        _dev(key_cache, "key_cache", key.dtype, dev), _dev(value_cache, "value_cache", key.dtype, dev),
+        _dev(key_cache, "key_cache", device=dev), _dev(value_cache, "value_cache", device=dev),
         _dev(slot_mapping, "slot_mapping", torch.int64, dev), T, hkv, d, nb, bs,
-        _dtype_code(key.dtype), _stream(dev))
+        _dtype_code(key.dtype), kv, ks, vs, _stream(dev))
     _check("pa_reshape_and_cache", st)
 
 
@@ -187,10 +219,14 @@ def varlen_attention(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torc
                      cu_seqlens_q: torch.Tensor, seq_lens: torch.Tensor, block_tables: torch.Tensor,
                      *, max_q_len: int, max_seq_len: int, scale: float, partition_size: int = 0,
                      out: Optional[torch.Tensor] = None, partials: Optional[Partials] = None,
-                     reduce: bool = True, sinks: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     reduce: bool = True, sinks: Optional[torch.Tensor] = None,
+                     k_scale: Optional[torch.Tensor] = None,
+                     v_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Paged varlen attention; with partition_size > 0 and reduce=True the split
     partials are merged by pa_split_kv_reduce on the same stream.  sinks:
-    optional float32 [Hq] attention-sink logits on the same device."""
+    optional float32 [Hq] attention-sink logits on the same device.  8-bit
+    caches (float8_e4m3fn / uint8 E4M3 codes) need k_scale and v_scale
+    (float32 [Hkv]) and bf16 queries."""
     TQ, hq, d = q.shape
     nb, bs, hkv, cd = key_cache.shape
     if cd != d or value_cache.shape != key_cache.shape:
@@ -210,15 +246,19 @@ def varlen_attention(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torc
         mp = partials.max_parts
     if sinks is not None and sinks.shape != (hq,):
         raise ValueError("sinks must be [num_q_heads]")
+    if value_cache.dtype != key_cache.dtype:
+        raise TypeError("key_cache and value_cache differ in dtype")
+    kv = _kv_code(key_cache, q.dtype)
+    ks, vs = _scales(k_scale, v_scale, kv, hkv, dev)
     s = _stream(dev)
     st = lib.pa_varlen_attention(
         _dev(out, "out", q.dtype, dev), _dev(q, "q", device=dev),
-        _dev(key_cache, "key_cache", q.dtype, dev), _dev(value_cache, "value_cache", q.dtype, dev),
+        _dev(key_cache, "key_cache", device=dev), _dev(value_cache, "value_cache", device=dev),
         _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev), _dev(seq_lens, "seq_lens", torch.int32, dev),
         _dev(block_tables, "block_tables", torch.int32, dev), B, TQ, int(max_q_len),
         int(max_seq_len), block_tables.shape[1], hq, hkv, d, nb, bs, float(scale),
         _dev(sinks, "sinks", torch.float32, dev),
-        _dtype_code(q.dtype), int(partition_size), _dev(tmp, "tmp_out", torch.float32, dev),
+        _dtype_code(q.dtype), kv, ks, vs, int(partition_size), _dev(tmp, "tmp_out", torch.float32, dev),
         _dev(ml, "max_logits", torch.float32, dev), _dev(es, "exp_sums", torch.float32, dev), mp, s)
     _check("pa_varlen_attention", st)
     if partition_size and reduce:

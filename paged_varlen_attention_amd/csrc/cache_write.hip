@@ -9,6 +9,12 @@
 // fully coalesced 128-bit accesses.  Slots outside the pool are ignored rather
 // than written.
 //
+// The 8-bit form (the library's own E4M3 scheme; the pages name KV
+// quantisation kernels without giving one) stores each element of KV head g
+// as the E4M3 code of the correctly rounded float32 quotient x / scale[g]:
+// nearest code, ties to an even mantissa, saturating at 448, NaN to 0x7F.
+// Each thread turns 16 elements of one head into one 16-byte store.
+//
 // expand_block_tables (unified-memory article, section six) rewrites a table of
 // large cache blocks into the equivalent table of kernel pages: block b of
 // `ratio` pages becomes pages ratio*b .. ratio*b + ratio-1.
@@ -32,6 +38,82 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const uint4 v = value[t * pieces_per_row + c];
     kc[s * pieces_per_row + c] = k;
     vc[s * pieces_per_row + c] = v;
+}
+
+// E4M3 code of y: round to nearest, ties to even; |y| >= 448 and infinities
+// saturate to +-448 (0x7E); NaN gives 0x7F; the sign of zero is kept.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+    const uint32_t b = __float_as_uint(y);
+    const uint32_t sign = (b >> 24) & 0x80u;
+    const uint32_t a = b & 0x7fffffffu;
+    if (a > 0x7f800000u) return 0x7fu;
+    if (a >= 0x43e00000u) return sign | 0x7eu;  // 448 = 1.75 * 2^8
+    if (a < 0x3c800000u) {
+        // below 2^-6: the codes are the multiples of 2^-9 (code 8 = 2^-6 is
+        // the smallest normal), so scale and round to an integer, ties to even
+        return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+    }
+    // normal range: keep 3 of the 23 mantissa bits, rounding to nearest even
+    // (a carry moves into the exponent), then rebias the exponent 127 -> 7
+    const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+    return sign | (r - (120u << 3));
+}
+
+template <bool F32>
+__device__ __forceinline__ void load16(const void *src, float (&f)[16]) {
+    if constexpr (F32) {
+        const float4 *p = reinterpret_cast<const float4 *>(src);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 v = p[j];
+            f[4 * j] = v.x; f[4 * j + 1] = v.y; f[4 * j + 2] = v.z; f[4 * j + 3] = v.w;
+        }
+    } else {
+        const uint4 *p = reinterpret_cast<const uint4 *>(src);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint4 v = p[j];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                f[8 * j + 2 * k] = bf16lo(w[k]);
+                f[8 * j + 2 * k + 1] = bf16hi(w[k]);
+            }
+        }
+    }
+}
+
+template <bool F32>
+__device__ __forceinline__ uint4 quantize16(const void *src, float scale) {
+    float f[16];
+    load16<F32>(src, f);
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x |= e4m3_code(f[4 * j + k] / scale) << (8 * k);
+        w[j] = x;
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <bool F32>
+__global__ __launch_bounds__(256) void quantize_cache_kernel(
+    const char *__restrict__ key, const char *__restrict__ value, uint4 *__restrict__ kc,
+    uint4 *__restrict__ vc, const int64_t *__restrict__ slots, const float *__restrict__ k_scale,
+    const float *__restrict__ v_scale, int32_t num_tokens, int32_t pieces_per_row,
+    int32_t head_dim, int64_t num_slots) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t t = i / pieces_per_row;
+    const int32_t c = (int32_t)(i - t * pieces_per_row);
+    if (t >= num_tokens) return;
+    const int64_t s = slots[t];
+    if (s < 0 || s >= num_slots) return;
+    const int32_t h = (c * 16) / head_dim;  // 16 elements never straddle two heads
+    const size_t src = ((size_t)t * pieces_per_row + c) * 16 * (F32 ? 4 : 2);
+    kc[s * pieces_per_row + c] = quantize16<F32>(key + src, k_scale[h]);
+    vc[s * pieces_per_row + c] = quantize16<F32>(value + src, v_scale[h]);
 }
 
 __global__ __launch_bounds__(256) void expand_block_tables_kernel(
@@ -58,6 +140,23 @@ hipError_t launch_reshape_and_cache(const void *key, const void *value, void *kc
                        reinterpret_cast<const uint4 *>(key), reinterpret_cast<const uint4 *>(value),
                        reinterpret_cast<uint4 *>(kc), reinterpret_cast<uint4 *>(vc), slots,
                        num_tokens, ppr, num_slots);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_cache(const void *key, const void *value, void *kc, void *vc,
+                                 const int64_t *slots, const float *k_scale,
+                                 const float *v_scale, int32_t num_tokens, int32_t row_elems,
+                                 int32_t head_dim, int64_t num_slots, bool in_f32,
+                                 hipStream_t stream) {
+    if (num_tokens == 0) return hipSuccess;
+    const int32_t ppr = row_elems / 16;
+    const int64_t total = (int64_t)num_tokens * ppr;
+    const int64_t blocks = (total + 255) / 256;
+    auto kernel = in_f32 ? quantize_cache_kernel<true> : quantize_cache_kernel<false>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const char *>(key), static_cast<const char *>(value),
+                       static_cast<uint4 *>(kc), static_cast<uint4 *>(vc), slots, k_scale, v_scale,
+                       num_tokens, ppr, head_dim, num_slots);
     return hipGetLastError();
 }
 

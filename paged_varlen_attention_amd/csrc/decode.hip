@@ -28,6 +28,11 @@
 //    accumulators stay in their registers;
 //  * PV pairs two tokens per lane: p is packed to bf16 pairs and V is
 //    interleaved with v_perm_b32 so one v_dot2c does two multiply-adds;
+//  * 8-bit E4M3 caches (the library's own KV quantisation) move half the
+//    bytes: a lane's 16 elements are two 8-byte LDS pieces, converted to bf16
+//    pairs with gfx950's v_cvt_scalef32_pk_bf16_fp8 (exact: every E4M3 value
+//    is a bf16 value), after which the bf16 path runs unchanged; the head's K
+//    scale is folded into the softmax scale and its V scale into the output;
 //  * at the end, every lane is rescaled to the wave-wide max and the lane
 //    groups of the wave are summed in registers (DPP rotations inside each
 //    16-lane row, then v_permlane16/32_swap across rows only as far as the
@@ -57,18 +62,25 @@ namespace {
 constexpr float RESCALE_THRESHOLD = 8.0f;
 
 
-template <typename T, int D, int GT, int CT_, int NW_, int NST_>
+template <typename T, bool KV8_, int D, int GT, int CT_, int NW_, int NST_>
 struct DecodeCfg {
     static constexpr bool BF16 = sizeof(T) == 2;
+    static constexpr bool KV8 = KV8_;            // caches hold E4M3 codes (T is bf16)
     static constexpr int ELT = sizeof(T);
     static constexpr int CT = CT_;               // tokens per chunk (LDS stage)
-    static constexpr int R = D * ELT;            // bytes per K/V row of one head
-    static constexpr int L = R / 32;             // lanes per token (32 bytes each)
+    static constexpr int QR = D * ELT;           // bytes per query row of one head
+    static constexpr int R = KV8 ? D : QR;       // bytes per K/V row of one head
+    static constexpr int L = QR / 32;            // lanes per token (16 or 8 elements each)
+    static constexpr int PIECE = KV8 ? 8 : 16;   // bytes of one of a lane's two row pieces
     static constexpr int TPP = 64 / L;           // tokens per pass of the wave
     static constexpr int NP = CT / TPP;          // passes per chunk
     static constexpr int EPW = 4 / ELT;          // elements per 32-bit word
-    static constexpr int NI = CT * R / 1024;     // DMA instructions per chunk per tensor
-    static constexpr int RPI = 1024 / R;         // rows moved by one DMA instruction
+    // Bytes one lane moves per DMA instruction: 16, or 4 when 16 would make
+    // one instruction span more than 8 rows (8-bit rows of 64 elements), since
+    // a chunk of 8-token pages switches page after row 8.
+    static constexpr int DW = (R * 8 < 64 * 16) ? 4 : 16;
+    static constexpr int NI = CT * R / (64 * DW);  // DMA instructions per chunk per tensor
+    static constexpr int RPI = 64 * DW / R;        // rows moved by one DMA instruction
     static constexpr int SLOT = 2 * CT * R;      // bytes of one LDS stage (K rows, then V rows)
     static constexpr int NW = NW_;
     static constexpr int NST = NST_;
@@ -90,7 +102,8 @@ struct DecodeCfg {
     static constexpr int LDS_BYTES = STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES;
     static_assert(L >= 4 && L <= 32, "row split");
     static_assert(NP >= 1 && CT % TPP == 0, "chunk covers whole passes");
-    static_assert(NI >= 1 && RPI >= 1 && CT * R % 1024 == 0, "dma shape");
+    static_assert(NI >= 1 && RPI >= 1 && RPI <= 8 && CT * R % (64 * DW) == 0, "dma shape");
+    static_assert(!KV8 || BF16, "8-bit caches are read with bf16 queries");
     static_assert((NST - 1) * VM_PER_CHUNK < 64, "vmcnt range");
     static_assert(NP % SU == 0, "pass pairing");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
@@ -99,7 +112,7 @@ struct DecodeCfg {
 // Element index (within the head's D) of word w of lane column c.
 template <class C>
 __device__ __forceinline__ int word_elem(int c, int w) {
-    // two 16-byte pieces per lane: piece i at byte (i*L + c)*16 of the row
+    // two pieces per lane: piece i holds elements (i*L + c)*16/ELT onward
     return ((w / 4) * C::L + c) * (16 / C::ELT) + (w % 4) * C::EPW;
 }
 
@@ -118,12 +131,29 @@ __device__ __forceinline__ void wait_chunks_ahead(int ahead) {
     }
 }
 
+// Four E4M3 codes -> two bf16 pairs (codes 0,1 and codes 2,3), exact.
+__device__ __forceinline__ void e4m3x4_to_bf16(uint32_t codes, uint32_t &lo, uint32_t &hi) {
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false));
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true));
+}
+
+// The lane's 8 words of a row (bf16 pairs or fp32 values): its two pieces,
+// converted to bf16 pairs for 8-bit rows.
 template <class C>
 __device__ __forceinline__ void read_row_words(const char *lds_row, int c, uint32_t (&w)[8]) {
-    const uint4 a = *reinterpret_cast<const uint4 *>(lds_row + c * 16);
-    const uint4 b = *reinterpret_cast<const uint4 *>(lds_row + (C::L + c) * 16);
-    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    if constexpr (C::KV8) {
+        const uint2 a = *reinterpret_cast<const uint2 *>(lds_row + c * 8);
+        const uint2 b = *reinterpret_cast<const uint2 *>(lds_row + (C::L + c) * 8);
+        e4m3x4_to_bf16(a.x, w[0], w[1]);
+        e4m3x4_to_bf16(a.y, w[2], w[3]);
+        e4m3x4_to_bf16(b.x, w[4], w[5]);
+        e4m3x4_to_bf16(b.y, w[6], w[7]);
+    } else {
+        const uint4 a = *reinterpret_cast<const uint4 *>(lds_row + c * 16);
+        const uint4 b = *reinterpret_cast<const uint4 *>(lds_row + (C::L + c) * 16);
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    }
 }
 
 // Max over all 64 lanes of the wave.
@@ -312,9 +342,9 @@ __device__ __forceinline__ void chunk_step(const char *kst, const char *vst, int
     }
 }
 
-template <typename T, int D, int GT, int CT, int NW, int NST>
+template <typename T, bool KV8, int D, int GT, int CT, int NW, int NST>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
-    using C = DecodeCfg<T, D, GT, CT, NW, NST>;
+    using C = DecodeCfg<T, KV8, D, GT, CT, NW, NST>;
     __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
 
     // The KV heads of one partition are adjacent in the grid, so the
@@ -395,13 +425,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
     uint32_t qw[GT][8];
     {
         const char *qbase = reinterpret_cast<const char *>(p.q) +
-                            ((size_t)q0 * p.hq + (size_t)kvh * G) * C::R;
+                            ((size_t)q0 * p.hq + (size_t)kvh * G) * C::QR;
 #pragma unroll
         for (int g = 0; g < GT; ++g) {
             if (g < G) {
-                const uint4 a = *reinterpret_cast<const uint4 *>(qbase + g * C::R + c * 16);
+                const uint4 a = *reinterpret_cast<const uint4 *>(qbase + g * C::QR + c * 16);
                 const uint4 b =
-                    *reinterpret_cast<const uint4 *>(qbase + g * C::R + (C::L + c) * 16);
+                    *reinterpret_cast<const uint4 *>(qbase + g * C::QR + (C::L + c) * 16);
                 qw[g][0] = a.x; qw[g][1] = a.y; qw[g][2] = a.z; qw[g][3] = a.w;
                 qw[g][4] = b.x; qw[g][5] = b.y; qw[g][6] = b.z; qw[g][7] = b.w;
             } else {
@@ -417,9 +447,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
     uint32_t voff[C::NI];
 #pragma unroll
     for (int ii = 0; ii < C::NI; ++ii) {
-        const int row = ii * C::RPI + lane / (C::R / 16);
-        const int piece = lane % (C::R / 16);
-        voff[ii] = (uint32_t)row * row_stride + (uint32_t)piece * 16u;
+        const int row = ii * C::RPI + lane / (C::R / C::DW);
+        const int piece = lane % (C::R / C::DW);
+        voff[ii] = (uint32_t)row * row_stride + (uint32_t)piece * C::DW;
     }
 
     const uint32_t lds_wave = lds_addr(lds) + (uint32_t)(wave * NST * C::SLOT);
@@ -454,10 +484,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
         const uint32_t ldsv = ldsk + CT * C::R;
 #pragma unroll
         for (int ii = 0; ii < C::NI; ++ii)
-            dma16(ii * C::RPI >= 8 ? kb1 : kb0, voff[ii], ldsk + ii * 1024);
+            dma_lds<C::DW>(ii * C::RPI >= 8 ? kb1 : kb0, voff[ii], ldsk + ii * 64 * C::DW);
 #pragma unroll
         for (int ii = 0; ii < C::NI; ++ii)
-            dma16((ii * C::RPI >= 8 ? kb1 : kb0) + v_minus_k, voff[ii], ldsv + ii * 1024);
+            dma_lds<C::DW>((ii * C::RPI >= 8 ? kb1 : kb0) + v_minus_k, voff[ii],
+                           ldsv + ii * 64 * C::DW);
     };
 
     // ---- online softmax state (per lane, for its token subset) ----
@@ -485,16 +516,18 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
         kst = lds + (wave * NST + k % NST) * C::SLOT;
         vst = kst + CT * C::R;
     };
+    // 8-bit caches: the head's K scale joins the softmax scale
+    const float scale_log2 = KV8 ? p.scale_log2 * p.k_scale[kvh] : p.scale_log2;
     for (int k = 0; k < nmy - 1; ++k) {
         const char *kst, *vst;
         stage(k, kst, vst);
-        chunk_step<C, GT, false>(kst, vst, c, tip, 0, 0, p.scale_log2, qw, m, mtrue, l, accv);
+        chunk_step<C, GT, false>(kst, vst, c, tip, 0, 0, scale_log2, qw, m, mtrue, l, accv);
     }
     if (nmy > 0) {
         const char *kst, *vst;
         stage(nmy - 1, kst, vst);
         const int tok0 = (c_begin + wave + (nmy - 1) * NW) * CT;
-        chunk_step<C, GT, true>(kst, vst, c, tip, tok0, tok_end, p.scale_log2, qw, m, mtrue, l,
+        chunk_step<C, GT, true>(kst, vst, c, tip, tok0, tok_end, scale_log2, qw, m, mtrue, l,
                                  accv);
     }
 
@@ -553,6 +586,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
     __syncthreads();
 
     const bool direct = nparts <= 1;
+    const float vscale = KV8 ? p.v_scale[kvh] : 1.0f;  // 8-bit caches: the head's V scale
     for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
         const int g = idx / D;
         const int d = idx - g * D;
@@ -570,12 +604,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
         }
         const int h = kvh * G + g;
         float o = num / den;
+        if constexpr (KV8) o *= vscale;
         if (direct && p.sinks) {
             // the head's sink: one more denominator term, no value (log2 units)
             const float s2 = p.sinks[h] * LOG2E_F;
             const float Mx = fmaxf(M, s2);
             const float a = exp2_diff(M, Mx);
             o = num * a / (den * a + exp2_diff(s2, Mx));
+            if constexpr (KV8) o *= vscale;
         }
         if (direct) {
             const size_t oi = ((size_t)q0 * p.hq + h) * D + d;
@@ -605,17 +641,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
 #define PA_DECODE_NST(R) 2
 #endif
 
-template <typename T, int D, int GT>
+template <typename T, bool KV8, int D, int GT>
 struct DecodeTuning {
-    static constexpr int R = D * (int)sizeof(T);
+    static constexpr int R = D * (KV8 ? 1 : (int)sizeof(T));
     static constexpr int CT = PA_DECODE_CT(R);
     static constexpr int NW = PA_DECODE_NW(R);
     static constexpr int NST = PA_DECODE_NST(R);
 };
 
-template <typename T, int D, int GT>
+template <typename T, bool KV8, int D, int GT>
 hipError_t launch_t(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
-    using Tn = DecodeTuning<T, D, GT>;
+    using Tn = DecodeTuning<T, KV8, D, GT>;
     const int parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
     const int rows = p.per_token ? p.total_q : p.num_seqs;
 #if PA_DECODE_ORDER == 0
@@ -626,32 +662,32 @@ hipError_t launch_t(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
     dim3 block(Tn::NW * 64);
     if (li) *li = LaunchInfo{{(int)grid.x, (int)grid.y, (int)grid.z}, (int)block.x,
                              {Tn::CT, Tn::NW, Tn::NST}, 0};
-    hipLaunchKernelGGL((decode_kernel<T, D, GT, Tn::CT, Tn::NW, Tn::NST>), grid, block, 0, stream,
-                       p);
+    hipLaunchKernelGGL((decode_kernel<T, KV8, D, GT, Tn::CT, Tn::NW, Tn::NST>), grid, block, 0,
+                       stream, p);
     return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, bool KV8, int D>
 hipError_t launch_d(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
     switch (p.group) {
-        case 1: return launch_t<T, D, 1>(p, stream, li);
-        case 2: return launch_t<T, D, 2>(p, stream, li);
+        case 1: return launch_t<T, KV8, D, 1>(p, stream, li);
+        case 2: return launch_t<T, KV8, D, 2>(p, stream, li);
         case 3:
-        case 4: return launch_t<T, D, 4>(p, stream, li);
+        case 4: return launch_t<T, KV8, D, 4>(p, stream, li);
         case 5:
-        case 6: return launch_t<T, D, 6>(p, stream, li);
+        case 6: return launch_t<T, KV8, D, 6>(p, stream, li);
         case 7:
-        case 8: return launch_t<T, D, 8>(p, stream, li);
+        case 8: return launch_t<T, KV8, D, 8>(p, stream, li);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <typename T>
+template <typename T, bool KV8>
 hipError_t launch_dt(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
     switch (p.head_dim) {
-        case 64: return launch_d<T, 64>(p, stream, li);
-        case 128: return launch_d<T, 128>(p, stream, li);
-        case 256: return launch_d<T, 256>(p, stream, li);
+        case 64: return launch_d<T, KV8, 64>(p, stream, li);
+        case 128: return launch_d<T, KV8, 128>(p, stream, li);
+        case 256: return launch_d<T, KV8, 256>(p, stream, li);
         default: return hipErrorInvalidValue;
     }
 }
@@ -663,9 +699,12 @@ bool decode_supported(int dtype, int head_dim, int group) {
            group >= 1 && group <= 8;
 }
 
+bool decode_kv8_supported(int head_dim, int group) { return decode_supported(1, head_dim, group); }
+
 hipError_t launch_decode(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
-    if (p.dtype == 1) return launch_dt<bf16_t>(p, stream, li);
-    return launch_dt<float>(p, stream, li);
+    if (p.kv8) return p.dtype == 1 ? launch_dt<bf16_t, true>(p, stream, li) : hipErrorInvalidValue;
+    if (p.dtype == 1) return launch_dt<bf16_t, false>(p, stream, li);
+    return launch_dt<float, false>(p, stream, li);
 }
 
 }  // namespace pa

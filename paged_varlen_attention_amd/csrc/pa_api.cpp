@@ -26,6 +26,19 @@ int log2_exact(int32_t v) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_EHIP; }
 
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Cache element type against the row dtype: PA_OK, or the status to return.
+// Scales go with 8-bit caches only.
+int check_kv(int32_t dtype, int32_t kv_dtype, const float *k_scale, const float *v_scale) {
+    if (kv_dtype == PA_FP8_E4M3) {
+        if (!k_scale || !v_scale || !aligned4(k_scale) || !aligned4(v_scale)) return PA_EINVAL;
+        return PA_OK;
+    }
+    if (kv_dtype != dtype) return PA_EUNSUPPORTED;
+    return (k_scale || v_scale) ? PA_EINVAL : PA_OK;
+}
+
 // Grid dimensions y and z are limited to 65535 workgroups.
 constexpr int32_t GRID_YZ_MAX = 65535;
 
@@ -66,7 +79,7 @@ int check_partitions(int32_t partition_size, int32_t max_seq_len, const float *t
 
 extern "C" {
 
-int pa_abi_version(void) { return 200; }
+int pa_abi_version(void) { return 300; }
 
 const char *pa_status_string(int status) {
     switch (status) {
@@ -93,20 +106,30 @@ int pa_partials_bytes(int32_t total_q, int32_t num_q_heads, int32_t head_dim,
 int pa_reshape_and_cache(const void *key, const void *value, void *key_cache, void *value_cache,
                          const int64_t *slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
                          int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t dtype,
+                         int32_t kv_dtype, const float *k_scale, const float *v_scale,
                          void *stream) {
     try {
         const int eb = elt_bytes(dtype);
         if (!eb) return PA_EUNSUPPORTED;
+        const int kst = check_kv(dtype, kv_dtype, k_scale, v_scale);
+        if (kst != PA_OK) return kst;
         if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 ||
             block_size <= 0)
             return PA_EINVAL;
         if (num_tokens == 0) return PA_OK;
         if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PA_EINVAL;
-        const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * eb;
+        const bool kv8 = kv_dtype == PA_FP8_E4M3;
+        const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * (kv8 ? 1 : eb);
         if (row_bytes % 16 != 0 || row_bytes > (1 << 30)) return PA_EUNSUPPORTED;
+        if (kv8 && head_dim % 16 != 0) return PA_EUNSUPPORTED;
         if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) ||
             !aligned16(value_cache))
             return PA_EINVAL;
+        if (kv8)
+            return hip_status(pa::launch_quantize_cache(
+                key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale, num_tokens,
+                (int32_t)row_bytes, head_dim, (int64_t)num_blocks * block_size, dtype == PA_F32,
+                (hipStream_t)stream));
         return hip_status(pa::launch_reshape_and_cache(
             key, value, key_cache, value_cache, slot_mapping, num_tokens, (int32_t)row_bytes,
             (int64_t)num_blocks * block_size, (hipStream_t)stream));
@@ -141,11 +164,16 @@ int varlen_attention_impl(pa_dispatch_info &rec, void *out, const void *q, const
                           int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
                           int32_t max_blocks_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
                           int32_t head_dim, int32_t num_blocks, int32_t block_size, float scale,
-                          const float *sinks, int32_t dtype, int32_t partition_size,
+                          const float *sinks, int32_t dtype, int32_t kv_dtype,
+                          const float *k_scale, const float *v_scale, int32_t partition_size,
                           float *tmp_out, float *max_logits, float *exp_sums,
                           int32_t max_partitions, void *stream) {
     try {
         if (!elt_bytes(dtype)) return PA_EUNSUPPORTED;
+        const int kst = check_kv(dtype, kv_dtype, k_scale, v_scale);
+        if (kst != PA_OK) return kst;
+        const bool kv8 = kv_dtype == PA_FP8_E4M3;
+        if (kv8 && dtype != PA_BF16) return PA_EUNSUPPORTED;
         if (num_seqs < 0 || total_q < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
             num_blocks <= 0 || block_size <= 0 || head_dim <= 0 || max_blocks_per_seq < 0)
             return PA_EINVAL;
@@ -204,12 +232,17 @@ int varlen_attention_impl(pa_dispatch_info &rec, void *out, const void *q, const
         p.scale_log2 = scale * 1.44269504088896340736f;
         p.sinks = sinks;
         p.dtype = dtype;
+        p.kv8 = kv8;
+        p.k_scale = kv8 ? k_scale : nullptr;
+        p.v_scale = kv8 ? v_scale : nullptr;
 
         // One query token per request -> the VALU decode kernel.  fp32 batches
-        // with longer windows also use it, one workgroup per query token; bf16
-        // prefill and mixed batches go to the MFMA tiles.
-        if (max_q_len == 1 || dtype == PA_F32) {
-            if (!pa::decode_supported(dtype, head_dim, group)) return PA_EUNSUPPORTED;
+        // and 8-bit caches with longer windows also use it, one workgroup per
+        // query token; bf16 prefill and mixed batches go to the MFMA tiles.
+        if (max_q_len == 1 || dtype == PA_F32 || kv8) {
+            if (kv8 ? !pa::decode_kv8_supported(head_dim, group)
+                    : !pa::decode_supported(dtype, head_dim, group))
+                return PA_EUNSUPPORTED;
             p.per_token = max_q_len > 1;
             if (p.per_token && total_q > GRID_YZ_MAX) return PA_EUNSUPPORTED;
             const int64_t parts =
@@ -287,15 +320,16 @@ int pa_varlen_attention(void *out, const void *q, const void *key_cache, const v
                         int32_t max_q_len, int32_t max_seq_len, int32_t max_blocks_per_seq,
                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                         int32_t num_blocks, int32_t block_size, float scale,
-                        const float *sinks, int32_t dtype, int32_t partition_size,
+                        const float *sinks, int32_t dtype, int32_t kv_dtype,
+                        const float *k_scale, const float *v_scale, int32_t partition_size,
                         float *tmp_out, float *max_logits, float *exp_sums,
                         int32_t max_partitions, void *stream) {
     pa_dispatch_info rec{};
     rec.status = varlen_attention_impl(
         rec, out, q, key_cache, value_cache, cu_seqlens_q, seq_lens, block_tables, num_seqs,
         total_q, max_q_len, max_seq_len, max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim,
-        num_blocks, block_size, scale, sinks, dtype, partition_size, tmp_out, max_logits,
-        exp_sums, max_partitions, stream);
+        num_blocks, block_size, scale, sinks, dtype, kv_dtype, k_scale, v_scale, partition_size,
+        tmp_out, max_logits, exp_sums, max_partitions, stream);
     g_last = rec;
     return rec.status;
 }

@@ -137,7 +137,31 @@ __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t
         : "v"(voff), "s"(sbase), "s"(lds)
         : "memory", "m0");
 }
+
+// The same with 4 bytes per lane (global_load_lds_dword): lane i's dword lands
+// at lds + 4*i.
+__device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, uint32_t lds) {
+    sbase = uniform_ptr(sbase);
+    lds = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %0, %1"
+        :
+        : "v"(voff), "s"(sbase), "s"(lds)
+        : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// Direct global -> LDS load of BYTES (16 or 4) per lane.
+template <int BYTES>
+__device__ __forceinline__ void dma_lds(const void *sbase, uint32_t voff, uint32_t lds) {
+    static_assert(BYTES == 16 || BYTES == 4, "LDS DMA width");
+    if constexpr (BYTES == 16)
+        dma16(sbase, voff, lds);
+    else
+        dma4(sbase, voff, lds);
+}
 
 // Wait until at most N vector-memory instructions of this wave are in flight.
 template <int N>

@@ -39,6 +39,9 @@ struct AttnParams {
     float scale_log2;       // scale * log2(e)
     const float *sinks;     // NULL or [hq] sink logits (natural-log units)
     int32_t dtype;
+    int32_t kv8;            // caches hold E4M3 codes (dtype is then bf16)
+    const float *k_scale;   // kv8: [hkv] scale of K codes, else NULL
+    const float *v_scale;   // kv8: [hkv] scale of V codes, else NULL
     int32_t per_token;      // decode kernel: grid z indexes query tokens, not requests
     int32_t grid_tiles;     // tiled kernel: virtual q-tiles (set by its launcher)
     int32_t grid_parts;     // tiled kernel: partitions in the grid (set by its launcher)
@@ -75,6 +78,13 @@ struct LaunchInfo {
 hipError_t launch_reshape_and_cache(const void *key, const void *value, void *kc, void *vc,
                                     const int64_t *slots, int32_t num_tokens, int32_t row_bytes,
                                     int64_t num_slots, hipStream_t stream);
+// 8-bit cache write: E4M3 codes of row / scale[head]; in_f32 selects float32
+// rows (else bf16).  row_elems = num_kv_heads * head_dim, a multiple of 16.
+hipError_t launch_quantize_cache(const void *key, const void *value, void *kc, void *vc,
+                                 const int64_t *slots, const float *k_scale,
+                                 const float *v_scale, int32_t num_tokens, int32_t row_elems,
+                                 int32_t head_dim, int64_t num_slots, bool in_f32,
+                                 hipStream_t stream);
 hipError_t launch_expand_block_tables(int32_t *dst, const int32_t *src, int32_t num_seqs,
                                       int32_t src_stride, int32_t src_blocks, int32_t dst_stride,
                                       int32_t ratio, hipStream_t stream);
@@ -87,6 +97,7 @@ hipError_t launch_reduce(const ReduceParams &p, hipStream_t stream, LaunchInfo *
 
 // Whether a decode instantiation exists for this geometry.
 bool decode_supported(int dtype, int head_dim, int group);
+bool decode_kv8_supported(int head_dim, int group);
 bool prefill_supported(int dtype, int head_dim, int group);
 
 }  // namespace pa

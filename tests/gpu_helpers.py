@@ -28,6 +28,16 @@ class DeviceBatch:
     max_seq_len: int
     scale: float
     sinks: Optional[torch.Tensor] = None   # float32 [Hq] on the device, or None
+    k_scale: Optional[torch.Tensor] = None  # 8-bit caches: float32 [Hkv] on the device
+    v_scale: Optional[torch.Tensor] = None
+
+
+def _cache_to(c: torch.Tensor, device) -> torch.Tensor:
+    """8-bit caches travel as their raw uint8 codes (the binding reads uint8
+    caches as E4M3)."""
+    if c.dtype == torch.float8_e4m3fn:
+        c = c.view(torch.uint8)
+    return c.to(device)
 
 
 def to_device(w, device="cuda", write_cache=True) -> DeviceBatch:
@@ -35,12 +45,14 @@ def to_device(w, device="cuda", write_cache=True) -> DeviceBatch:
     pa_reshape_and_cache first; a workload with a page ratio > 1 is then viewed
     as kernel pages (cache reshape + pa_expand_block_tables)."""
     import paged_varlen_attention_amd as pa
-    kc = w.key_cache.to(device)
-    vc = w.value_cache.to(device)
+    kc = _cache_to(w.key_cache, device)
+    vc = _cache_to(w.value_cache, device)
     bt = w.block_tables.to(device)
+    ks = None if w.k_scale is None else w.k_scale.to(device).float().contiguous()
+    vs = None if w.v_scale is None else w.v_scale.to(device).float().contiguous()
     if w.slot_mapping is not None and write_cache:
         pa.reshape_and_cache(w.new_key.to(device), w.new_value.to(device), kc, vc,
-                             w.slot_mapping.to(device))
+                             w.slot_mapping.to(device), k_scale=ks, v_scale=vs)
     if w.kernel_page_ratio > 1:
         r = w.kernel_page_ratio
         nb, bs, hkv, d = kc.shape
@@ -51,7 +63,8 @@ def to_device(w, device="cuda", write_cache=True) -> DeviceBatch:
                        cu_seqlens_q=w.cu_seqlens_q.to(device), seq_lens=w.seq_lens.to(device),
                        block_tables=bt, max_q_len=w.max_q_len, max_seq_len=w.max_seq_len,
                        scale=w.scale,
-                       sinks=None if w.sinks is None else w.sinks.to(device).float().contiguous())
+                       sinks=None if w.sinks is None else w.sinks.to(device).float().contiguous(),
+                       k_scale=ks, v_scale=vs)
 
 
 def run_gpu(b: DeviceBatch, partition_size=0, out=None, partials=None, reduce=True):
@@ -59,7 +72,8 @@ def run_gpu(b: DeviceBatch, partition_size=0, out=None, partials=None, reduce=Tr
     return pa.varlen_attention(b.q, b.key_cache, b.value_cache, b.cu_seqlens_q, b.seq_lens,
                                b.block_tables, max_q_len=b.max_q_len, max_seq_len=b.max_seq_len,
                                scale=b.scale, partition_size=partition_size, out=out,
-                               partials=partials, reduce=reduce, sinks=b.sinks)
+                               partials=partials, reduce=reduce, sinks=b.sinks,
+                               k_scale=b.k_scale, v_scale=b.v_scale)
 
 
 def errors(gpu: torch.Tensor, ref: torch.Tensor):

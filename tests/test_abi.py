@@ -46,7 +46,7 @@ def test_status_strings_and_version():
     lib = _lib()
     for s in range(5):
         assert lib.pa_status_string(s)
-    assert lib.pa_abi_version() == 200
+    assert lib.pa_abi_version() == 300
 
 
 FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: every call below is rejected
@@ -55,12 +55,15 @@ FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: every call belo
 def attn_args(**over):
     a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, cu=FAKE, sl=FAKE, bt=FAKE, num_seqs=2,
              total_q=2, max_q_len=1, max_seq_len=50, max_blocks=4, hq=4, hkv=1, d=64, nb=8,
-             bs=16, scale=0.125, sinks=None, dtype=0, P=0, tmp=None, ml=None, es=None, mp=0,
-             stream=None)
+             bs=16, scale=0.125, sinks=None, dtype=0, kv_dtype=None, ks=None, vs=None, P=0,
+             tmp=None, ml=None, es=None, mp=0, stream=None)
     a.update(over)
+    if a["kv_dtype"] is None:
+        a["kv_dtype"] = a["dtype"]
     return [a[k] for k in ("out", "q", "kc", "vc", "cu", "sl", "bt", "num_seqs", "total_q",
                            "max_q_len", "max_seq_len", "max_blocks", "hq", "hkv", "d", "nb", "bs",
-                           "scale", "sinks", "dtype", "P", "tmp", "ml", "es", "mp", "stream")]
+                           "scale", "sinks", "dtype", "kv_dtype", "ks", "vs", "P", "tmp", "ml",
+                           "es", "mp", "stream")]
 
 
 @pytest.mark.parametrize("over,status", [
@@ -75,6 +78,15 @@ def attn_args(**over):
     (dict(P=256, max_seq_len=600, max_blocks=40, tmp=FAKE, ml=FAKE, es=FAKE, mp=2), 3),
     (dict(P=256, tmp=FAKE, ml=None, es=FAKE, mp=4), 3),
     (dict(num_seqs=70000), 2), (dict(sinks=ctypes.c_void_p(0x100002)), 1),
+    # 8-bit caches: bf16 queries only, both scales required and 4-byte aligned,
+    # scales refused for caches of the query dtype, unknown cache types refused
+    (dict(kv_dtype=2, ks=FAKE, vs=FAKE), 2), (dict(dtype=1, kv_dtype=2, ks=FAKE), 1),
+    (dict(dtype=1, kv_dtype=2, vs=FAKE), 1),
+    (dict(dtype=1, kv_dtype=2, ks=ctypes.c_void_p(0x100002), vs=FAKE), 1),
+    (dict(dtype=1, ks=FAKE, vs=FAKE), 1), (dict(dtype=1, kv_dtype=0), 2),
+    (dict(dtype=1, kv_dtype=5), 2), (dict(dtype=1, kv_dtype=2, ks=FAKE, vs=FAKE, d=96), 2),
+    (dict(dtype=1, kv_dtype=2, ks=FAKE, vs=FAKE, hq=36, hkv=4), 2),
+    (dict(dtype=1, kv_dtype=2, ks=FAKE, vs=FAKE, P=512), 3),
 ])
 def test_varlen_attention_rejects(over, status):
     assert _lib().pa_varlen_attention(*attn_args(**over)) == status
@@ -89,18 +101,31 @@ def test_varlen_attention_empty_batch_is_ok_without_pointers():
     (dict(dtype=3), 2), (dict(T=-1), 1), (dict(hkv=0), 1), (dict(key=None), 1),
     (dict(slots=None), 1), (dict(d=3), 2), (dict(bs=0), 1), (dict(nb=0), 1),
     (dict(kc=ctypes.c_void_p(0x100002)), 1),
+    # 8-bit caches: scales required, refused for plain caches; rows of 16-byte
+    # multiples with head_dim a multiple of 16
+    (dict(kv_dtype=2), 1), (dict(kv_dtype=2, ks=FAKE), 1), (dict(ks=FAKE, vs=FAKE), 1),
+    (dict(kv_dtype=0), 2), (dict(kv_dtype=2, ks=FAKE, vs=FAKE, d=8), 2),
+    (dict(kv_dtype=2, ks=FAKE, vs=FAKE, d=24, hkv=2), 2),
+    (dict(kv_dtype=2, ks=FAKE, vs=FAKE, key=None), 1),
+    (dict(kv_dtype=2, ks=ctypes.c_void_p(0x100001), vs=FAKE), 1),
 ])
 def test_reshape_and_cache_rejects(over, status):
     a = dict(key=FAKE, value=FAKE, kc=FAKE, vc=FAKE, slots=FAKE, T=4, hkv=1, d=64, nb=2, bs=16,
-             dtype=1, stream=None)
+             dtype=1, kv_dtype=None, ks=None, vs=None, stream=None)
     a.update(over)
+    if a["kv_dtype"] is None:
+        a["kv_dtype"] = a["dtype"]
     args = [a[k] for k in ("key", "value", "kc", "vc", "slots", "T", "hkv", "d", "nb", "bs",
-                           "dtype", "stream")]
+                           "dtype", "kv_dtype", "ks", "vs", "stream")]
     assert _lib().pa_reshape_and_cache(*args) == status
 
 
 def test_reshape_and_cache_zero_tokens_ok():
-    assert _lib().pa_reshape_and_cache(None, None, None, None, None, 0, 1, 64, 2, 16, 1, None) == 0
+    lib = _lib()
+    assert lib.pa_reshape_and_cache(None, None, None, None, None, 0, 1, 64, 2, 16, 1, 1, None,
+                                    None, None) == 0
+    assert lib.pa_reshape_and_cache(None, None, None, None, None, 0, 1, 64, 2, 16, 1, 2, FAKE,
+                                    FAKE, None) == 0
 
 
 @pytest.mark.parametrize("over,status", [
