@@ -21,10 +21,12 @@ reported beside it.
 ``roofline`` times the dominant kernel (the decode attention launch) with HIP
 events on the stream it runs on.  ``cpu_baseline`` times the fp64 oracle on
 the same workload on this host's cores.  ``secondary`` holds the other
-workloads of the metric: long-context split-KV decode and the mixed prefill
-and speculative-verify batches (MFMA TFLOP/s), plus a uniform long-prompt
-prefill batch of the mixed batches' head shape that shows the tiled kernel's
-steady state apart from the load imbalance of short ragged batches.
+workloads of the metric: long-context split-KV decode, the two decode batches
+over 8-bit E4M3 caches (half the KV bytes), the mixed prefill and
+speculative-verify batches (MFMA TFLOP/s), a uniform long-prompt prefill batch
+of the mixed batches' head shape that shows the tiled kernel's steady state
+apart from the load imbalance of short ragged batches, and the KV block
+offload rate.
 """
 from __future__ import annotations
 
@@ -51,7 +53,7 @@ class Step:
     """One pass of the hot path over one batch, on the current stream,
     bracketed by events so each kernel's duration can be read back."""
 
-    def __init__(self, w, partition_size, copies, device, write_cache):
+    def __init__(self, w, partition_size, copies, device, write_cache, kv8=False):
         import torch
         import paged_varlen_attention_amd as pa
         self.w = w
@@ -66,9 +68,24 @@ class Step:
         self.bt_src = bt
         self.bt = pa.expand_block_tables(bt, self.ratio) if self.ratio > 1 else bt
         self.pools = []
+        self.k_scale = self.v_scale = None
+        if kv8:  # 8-bit pools: the workload's bf16 pool quantised by the library's cache write
+            import workloads as W
+            ks, vs = W.kv_scales(17, w.num_kv_heads)
+            self.k_scale, self.v_scale = ks.to(device), vs.to(device)
+            nb, bs, hkv, d = w.key_cache.shape
+            all_slots = torch.arange(nb * bs, dtype=torch.int64, device=device)
         for _ in range(copies):
             kc = w.key_cache.to(device)
             vc = w.value_cache.to(device)
+            if kv8:
+                k8 = torch.empty(kc.shape, dtype=torch.uint8, device=device)
+                v8 = torch.empty_like(k8)
+                pa.reshape_and_cache(kc.view(nb * bs, hkv, d), vc.view(nb * bs, hkv, d), k8, v8,
+                                     all_slots, k_scale=self.k_scale, v_scale=self.v_scale)
+                torch.cuda.synchronize()
+                del kc, vc
+                kc, vc = k8, v8
             self.pools.append((kc, vc))
         self.write_cache = write_cache
         if self.write_cache:
@@ -106,7 +123,8 @@ class Step:
         if record:
             ev[0].record()
         if self.write_cache:
-            pa.reshape_and_cache(self.new_k, self.new_v, kc, vc, self.slots)
+            pa.reshape_and_cache(self.new_k, self.new_v, kc, vc, self.slots,
+                                 k_scale=self.k_scale, v_scale=self.v_scale)
         if record:
             ev[1].record()
         if self.ratio > 1:
@@ -116,7 +134,8 @@ class Step:
         kkc, kvc = self.kernel_view(kc, vc)
         pa.varlen_attention(self.q, kkc, kvc, self.cu, self.sl, self.bt, max_q_len=w.max_q_len,
                             max_seq_len=w.max_seq_len, scale=w.scale, partition_size=self.P,
-                            out=self.out, partials=self.partials, reduce=False)
+                            out=self.out, partials=self.partials, reduce=False,
+                            k_scale=self.k_scale, v_scale=self.v_scale)
         if record:
             ev[3].record()
         if self.P:
@@ -155,11 +174,13 @@ class Step:
                         (t / n for t in tot)))
 
 
-def step_bytes(w, include_cache_write):
-    b = w.algorithmic_bytes()
+def step_bytes(w, include_cache_write, kv_elt_bytes=None):
+    ke = w.elt_bytes if kv_elt_bytes is None else kv_elt_bytes
+    b = w.algorithmic_bytes(ke)
     if include_cache_write:
         n = int((w.slot_mapping >= 0).sum()) if w.slot_mapping is not None else w.total_q
-        b += 2 * 2 * n * w.num_kv_heads * w.head_dim * w.elt_bytes  # K and V rows, read + write
+        # K and V rows: read at the row type, written at the cache type
+        b += 2 * n * w.num_kv_heads * w.head_dim * (w.elt_bytes + ke)
     return b
 
 
@@ -203,14 +224,14 @@ def time_kernels(step, reps):
     return step.kernel_ms()
 
 
-def measure(w, P, steps, warmup, copies, device, write_cache=True):
-    step = Step(w, P, copies, device, write_cache)
+def measure(w, P, steps, warmup, copies, device, write_cache=True, kv8=False):
+    step = Step(w, P, copies, device, write_cache, kv8)
     step.capture()
     sec = time_graph_steps(step, steps, warmup)
     pct = step_percentiles(step, max(10, steps))
     km = time_kernels(step, max(10, steps // 2))
     km["step_ms_percentiles"] = pct
-    step_warm = Step(w, P, 1, device, write_cache)
+    step_warm = Step(w, P, 1, device, write_cache, kv8)
     step_warm.capture()
     sec_warm = time_graph_steps(step_warm, max(5, steps // 2), 2)
     km_warm = time_kernels(step_warm, 5)
@@ -408,6 +429,23 @@ def main():
                 "step_ms_percentiles": k4["step_ms_percentiles"],
                 "warm_ms_per_step": round(s4w * 1e3, 5)}
             log(f"long decode P={P4}: {sec_out[f'long_decode_bf16_P{P4}']}")
+        # 8-bit E4M3 caches (the library's KV quantisation): the same decode
+        # batches with half the KV bytes
+        for name8, w8, P8 in (("gqa_decode_fp8kv_P512", w, 512), ("gqa_decode_fp8kv_P1024", w, 1024),
+                              ("long_decode_fp8kv_P1024", w4, 1024)):
+            s8, k8, s8w, _ = measure(w8, P8, steps2, 5, args.copies, device, kv8=True)
+            b8 = step_bytes(w8, True, kv_elt_bytes=1)
+            a8 = w8.algorithmic_bytes(1)
+            sec_out[name8] = {
+                "ms_per_step": round(s8 * 1e3, 5), "GB/s": round(b8 / s8 / 1e9, 2),
+                "attention_ms": round(k8["attention"], 5), "reduce_ms": round(k8["reduce"], 5),
+                "cache_write_ms": round(k8["cache_write"], 5),
+                "attention_GB/s": round(a8 / (k8["attention"] * 1e-3) / 1e9, 2),
+                "frac_hbm": round(a8 / (k8["attention"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "algorithmic_bytes_per_launch": a8,
+                "step_ms_percentiles": k8["step_ms_percentiles"],
+                "warm_ms_per_step": round(s8w * 1e3, 5)}
+            log(f"{name8}: {sec_out[name8]}")
         del w4
         # partition sizes: the mixed batches run unsplit (their rows are at
         # most 3,000 keys); the verify batch splits its long contexts so its

@@ -94,10 +94,13 @@ class Workload:
     def elt_bytes(self) -> int:
         return 4 if self.dtype == torch.float32 else 2
 
-    def algorithmic_bytes(self) -> int:
+    def algorithmic_bytes(self, kv_elt_bytes: Optional[int] = None) -> int:
         """Each visible KV row once per KV head (shared by its query-head group),
-        plus Q in and O out, plus the integer metadata."""
-        kv = int(self.seq_lens.to(torch.int64).sum()) * self.num_kv_heads * self.head_dim * 2 * self.elt_bytes
+        plus Q in and O out, plus the integer metadata.  kv_elt_bytes: bytes per
+        cached element when the cache type differs from the queries' (1 for
+        8-bit caches)."""
+        ke = self.elt_bytes if kv_elt_bytes is None else kv_elt_bytes
+        kv = int(self.seq_lens.to(torch.int64).sum()) * self.num_kv_heads * self.head_dim * 2 * ke
         qo = 2 * self.total_q * self.num_q_heads * self.head_dim * self.elt_bytes
         meta = 4 * (self.cu_seqlens_q.numel() + self.seq_lens.numel() + self.block_tables.numel())
         return kv + qo + meta
