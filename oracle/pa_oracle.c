@@ -57,14 +57,15 @@ double pa_ref_e4m3_value(uint8_t code) {
     return negative ? -mag : mag;
 }
 
-/* Values of the 127 non-negative finite codes 0x00..0x7E, filled once by
- * e4m3_table_init() before any parallel region reads it. */
-static double e4m3_table[0x7F];
+/* Values of all 256 codes (pa_ref_e4m3_value of each), filled once by
+ * e4m3_table_init() before any parallel region reads it.  The encoder
+ * searches entries 0x00..0x7E, the non-negative finite codes. */
+static double e4m3_table[256];
 static int e4m3_table_ready = 0;
 
 static void e4m3_table_init(void) {
     if (e4m3_table_ready) return;
-    for (int c = 0; c <= 0x7E; ++c) e4m3_table[c] = pa_ref_e4m3_value((uint8_t)c);
+    for (int c = 0; c < 256; ++c) e4m3_table[c] = pa_ref_e4m3_value((uint8_t)c);
     e4m3_table_ready = 1;
 }
 
@@ -214,8 +215,8 @@ typedef struct {
  * 8-bit cache the code's value times the head's scale. */
 static double load_kv(const args_t *a, const void *cache, const float *scale, size_t idx,
                       int32_t g) {
-    if (a->kv_dtype == PA_REF_FP8_E4M3)
-        return pa_ref_e4m3_value(((const uint8_t *)cache)[idx]) * (double)scale[g];
+    if (a->kv_dtype == PA_REF_FP8_E4M3) /* table initialised before the row loops */
+        return e4m3_table[((const uint8_t *)cache)[idx]] * (double)scale[g];
     return load_elem(cache, idx, a->kv_dtype);
 }
 
@@ -319,6 +320,7 @@ int pa_ref_attention(double *out, const int32_t *tok, const int32_t *head, int32
                 total_q, max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, num_blocks,
                 block_size, dtype, scale, sinks, kv_dtype, k_scale, v_scale};
     if (check_args(&a)) return -1;
+    e4m3_table_init();
     int64_t rows = (tok == NULL) ? (int64_t)total_q * num_q_heads : n_rows;
     int32_t maxk = longest_seq(&a);
     int err = 0;
@@ -353,6 +355,7 @@ int pa_ref_attention_partials(double *o, double *m, double *l, const void *q,
                 total_q, max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, num_blocks,
                 block_size, dtype, scale, NULL, kv_dtype, k_scale, v_scale};
     if (check_args(&a) || partition_size <= 0 || max_parts <= 0) return -1;
+    e4m3_table_init();
     int64_t rows = (int64_t)total_q * num_q_heads;
     int err = 0;
 #pragma omp parallel

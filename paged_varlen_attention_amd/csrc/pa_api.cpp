@@ -237,9 +237,10 @@ int varlen_attention_impl(pa_dispatch_info &rec, void *out, const void *q, const
         p.v_scale = kv8 ? v_scale : nullptr;
 
         // One query token per request -> the VALU decode kernel.  fp32 batches
-        // and 8-bit caches with longer windows also use it, one workgroup per
-        // query token; bf16 prefill and mixed batches go to the MFMA tiles.
-        if (max_q_len == 1 || dtype == PA_F32 || kv8) {
+        // with longer windows also use it, one workgroup per query token, as
+        // do 8-bit caches of 64-element heads; bf16 prefill and mixed batches
+        // go to the MFMA tiles.
+        if (max_q_len == 1 || dtype == PA_F32 || (kv8 && !pa::prefill_kv8_supported(head_dim, group))) {
             if (kv8 ? !pa::decode_kv8_supported(head_dim, group)
                     : !pa::decode_supported(dtype, head_dim, group))
                 return PA_EUNSUPPORTED;
@@ -253,7 +254,9 @@ int varlen_attention_impl(pa_dispatch_info &rec, void *out, const void *q, const
             record_launch(rec, p.per_token ? PA_PATH_DECODE_TOKEN : PA_PATH_DECODE, li);
             return lst;
         }
-        if (!pa::prefill_supported(dtype, head_dim, group)) return PA_EUNSUPPORTED;
+        if (!(kv8 ? pa::prefill_kv8_supported(head_dim, group)
+                  : pa::prefill_supported(dtype, head_dim, group)))
+            return PA_EUNSUPPORTED;
         pa::LaunchInfo li{};
         const int lst = hip_status(pa::launch_prefill(p, (hipStream_t)stream, &li));
         record_launch(rec, PA_PATH_TILED, li);

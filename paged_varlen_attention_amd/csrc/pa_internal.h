@@ -99,5 +99,6 @@ hipError_t launch_reduce(const ReduceParams &p, hipStream_t stream, LaunchInfo *
 bool decode_supported(int dtype, int head_dim, int group);
 bool decode_kv8_supported(int head_dim, int group);
 bool prefill_supported(int dtype, int head_dim, int group);
+bool prefill_kv8_supported(int head_dim, int group);
 
 }  // namespace pa

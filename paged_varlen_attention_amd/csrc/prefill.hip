@@ -25,7 +25,14 @@
 //    swizzle of the 16-byte pieces of each row (conflict-free fragment reads);
 //    NST stages, one barrier per N-key tile;
 //  * requests are mapped to workgroups without a host pass: virtual tile x
-//    belongs to the last request r with cu[r]/BQ + r <= x (surplus tiles exit).
+//    belongs to the last request r with cu[r]/BQ + r <= x (surplus tiles exit);
+//  * 8-bit E4M3 caches (the library's own KV quantisation, D >= 128): tiles
+//    arrive by DMA into an 8-bit LDS ring (one instruction = 8 keys x 128
+//    bytes, so it never crosses a page), and after a barrier all threads
+//    convert the tile into the bf16 tile layout above with
+//    v_cvt_scalef32_pk_bf16_fp8 (exact), zeroing V rows past the sequence;
+//    the MFMA code is unchanged.  The head's K scale joins the softmax scale
+//    and its V scale the final normaliser.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -36,8 +43,9 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
 constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units
 
-template <int D, int N_, int NST_>
+template <int D, int N_, int NST_, bool KV8_ = false>
 struct PrefillCfg {
+    static constexpr bool KV8 = KV8_;             // caches hold E4M3 codes
     static constexpr int NWV = 4;                 // waves per workgroup
     static constexpr int N = N_;                  // keys per tile
     static constexpr int NST = NST_;              // LDS stages
@@ -53,10 +61,20 @@ struct PrefillCfg {
     static constexpr int IPG = GROUP_BYTES / 1024;  // DMA instructions per key group
     static constexpr int NI = T_BYTES / 1024;     // DMA instructions per tile
     static constexpr int NI_W = NI / NWV;         // per wave, per tensor
-    static constexpr int LDS_BYTES = NST * STAGE;
+    // 8-bit caches: NST raw stages (K tile, then V tile, N*D bytes each) ahead
+    // of one bf16 stage the MFMAs read
+    static constexpr int RG = KV8 ? D : R;        // bytes of a cached K/V row of one head
+    static constexpr int RAW_T = N * D;           // one 8-bit tile
+    static constexpr int RAW_STAGE = 2 * RAW_T;
+    static constexpr int IPG8 = D / 128;          // DMA instructions per 8-key group, 8-bit
+    static constexpr int NI8_W = RAW_T / 1024 / NWV;  // per wave, per tensor, 8-bit
+    static constexpr int RAW_BYTES = KV8 ? NST * RAW_STAGE : 0;
+    static constexpr int LDS_BYTES = KV8 ? RAW_BYTES + STAGE : NST * STAGE;
+    static_assert(!KV8 || (D >= 128 && RAW_T % (1024 * NWV) == 0), "8-bit tile shape");
     static_assert(NI % NWV == 0, "tile split over the waves");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
     static_assert(2 * NI_W * (NST - 1) < 64, "vmcnt range");
+    static_assert(2 * NI8_W * NST < 64, "vmcnt range");
 };
 
 // Tile layout in LDS (K and V alike).  Keys come in groups of KG = 8; a
@@ -113,9 +131,9 @@ constexpr int XCD_CHUNK = PA_PREFILL_XCD_CHUNK;
 #endif
 constexpr bool PF_SCHED = PA_PREFILL_SCHED;
 
-template <int D, int N, int NST>
+template <int D, int N, int NST, bool KV8>
 __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const AttnParams p) {
-    using C = PrefillCfg<D, N, NST>;
+    using C = PrefillCfg<D, N, NST, KV8>;
     constexpr int PF_K = PA_PREFILL_PF_K(D), PF_V = PA_PREFILL_PF_V(D);
     __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
 
@@ -181,7 +199,10 @@ __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const 
     // the running max can be taken on the raw scores and the scale applied
     // inside the exponent; a zero scale becomes the smallest normal float,
     // which leaves every visible weight exactly 1 and masked ones 0.
-    const float sl2 = fmaxf(fabsf(p.scale_log2), 1.17549435e-38f);
+    // (8-bit caches: S holds code units of K, so the head's K scale joins it)
+    const float sl2 =
+        fmaxf(fabsf(p.scale_log2) * (KV8 ? p.k_scale[kvh] : 1.f),
+              1.17549435e-38f);
     bf16x8_t qb[C::KS];
     {
         const uint32_t flip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
@@ -207,9 +228,9 @@ __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const 
     int win_page = k_lo >> lbs;
     int btv = load_window(win_page);
 
-    const uint32_t row_stride = (uint32_t)p.hkv * C::R;
+    const uint32_t row_stride = (uint32_t)p.hkv * C::RG;
     const uint64_t page_bytes = (uint64_t)bs * row_stride;
-    const uint64_t head_off = (uint64_t)kvh * C::R;
+    const uint64_t head_off = (uint64_t)kvh * C::RG;
     const char *kc = reinterpret_cast<const char *>(p.kc);
     const int64_t v_minus_k = reinterpret_cast<const char *>(p.vc) - kc;
 
@@ -238,6 +259,30 @@ __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const 
             const uint32_t l = lds0 + stage * C::STAGE + c * 1024;
             dma16(base, dma_voff, l);
             dma16(base + v_minus_k, dma_voff, l + C::T_BYTES);
+        }
+    };
+
+    // 8-bit caches: instruction c of a raw tile covers key group c / IPG8,
+    // bytes 128*(c % IPG8) .. +128 of those 8 rows; lane l brings 16 codes of
+    // key l%8, piece l/8, landing at c*1024 + 16*l of the raw tile.
+    const uint32_t dma_voff8 = (uint32_t)(lane & 7) * row_stride + (uint32_t)(lane >> 3) * 16u;
+    auto issue8 = [&](int kt, int stage) {
+        const int lp0 = kt >> lbs;
+        if (lp0 + ((C::N - 1) >> lbs) - win_page >= 64) {  // long ranges: slide the window
+            win_page = lp0;
+            btv = load_window(win_page);
+        }
+#pragma unroll
+        for (int i = 0; i < C::NI8_W; ++i) {
+            const int c = wave * C::NI8_W + i;
+            const int k8 = kt + C::KG * (c / C::IPG8);
+            const int lp = min(k8 >> lbs, seq_pages - 1);
+            const int phys = __builtin_amdgcn_readlane(btv, lp - win_page);
+            const char *base = kc + (uint64_t)phys * page_bytes + head_off +
+                               (uint32_t)(k8 & (bs - 1)) * row_stride + 128 * (c % C::IPG8);
+            const uint32_t l = lds0 + stage * C::RAW_STAGE + c * 1024;
+            dma16(base, dma_voff8, l);
+            dma16(base + v_minus_k, dma_voff8, l + C::RAW_T);
         }
     };
 
@@ -272,29 +317,80 @@ __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const 
 
     const int ntiles = (k_hi - k_lo + C::N - 1) / C::N;
     constexpr int VM = 2 * C::NI_W;
+    constexpr int VM8 = 2 * C::NI8_W;
+    if constexpr (KV8) {
 #pragma unroll
-    for (int s = 0; s < NST - 1; ++s)
-        if (s < ntiles) issue(k_lo + s * C::N, s);
+        for (int s = 0; s < NST; ++s)
+            if (s < ntiles) issue8(k_lo + s * C::N, s);
+    } else {
+#pragma unroll
+        for (int s = 0; s < NST - 1; ++s)
+            if (s < ntiles) issue(k_lo + s * C::N, s);
+    }
 
     for (int it = 0; it < ntiles; ++it) {
         const int kt = k_lo + it * C::N;
         const int stage = it % NST;
-        if (it + NST - 1 < ntiles) issue(kt + (NST - 1) * C::N, (it + NST - 1) % NST);
-        wait_tiles_ahead<VM, NST - 1>(min(NST - 1, ntiles - 1 - it));
-        const char *kst = lds + stage * C::STAGE;
-        char *vst = const_cast<char *>(kst) + C::T_BYTES;
-        if (kt + C::N > seq_len) {
-            // V rows past the sequence may hold anything (NaN): zero them, since
-            // p = 0 does not cancel a NaN inside the MFMA
+        const char *kst;
+        char *vst;
+        if constexpr (KV8) {
+            // raw tile `it` is in once this wave's older DMA has landed; the
+            // barrier also means every wave is done with the bf16 stage
+            wait_tiles_ahead<VM8, NST - 1>(min(NST - 1, ntiles - 1 - it));
             __syncthreads();
-            for (int i = threadIdx.x; i < C::N * C::PPR; i += 256) {
-                const int row = i / C::PPR;
-                if (kt + row >= seq_len)
-                    *reinterpret_cast<uint4 *>(vst + tile_off<C>(row, i % C::PPR)) =
-                        make_uint4(0, 0, 0, 0);
+            kst = lds + C::RAW_BYTES;
+            vst = const_cast<char *>(kst) + C::T_BYTES;
+            const char *raw = lds + stage * C::RAW_STAGE;
+            // 16 codes (key `key`, 16-byte piece rp of its row) -> bf16 pieces
+            // 2rp and 2rp+1; keys vary fastest so reads and writes are
+            // conflict-free; V rows past the sequence become zeros (NaN codes
+            // would survive p = 0 inside the MFMA)
+            constexpr int CH = C::N * (D / 16);  // 16-byte raw pieces per tensor
+            for (int i = threadIdx.x; i < 2 * CH; i += 256) {
+                const bool isv = i >= CH;
+                const int ii = isv ? i - CH : i;
+                const int key = ii % C::N, rp = ii / C::N;
+                const uint4 w = *reinterpret_cast<const uint4 *>(
+                    raw + (isv ? C::RAW_T : 0) + ((key >> 3) * C::IPG8 + (rp >> 3)) * 1024 +
+                    (((rp & 7) << 3) + (key & 7)) * 16);
+                uint4 lo, hi;
+                if (isv && kt + key >= seq_len) {
+                    lo = make_uint4(0, 0, 0, 0);
+                    hi = lo;
+                } else {
+                    lo.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false));
+                    lo.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true));
+                    lo.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false));
+                    lo.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true));
+                    hi.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.z, 1.0f, false));
+                    hi.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.z, 1.0f, true));
+                    hi.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.w, 1.0f, false));
+                    hi.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.w, 1.0f, true));
+                }
+                char *dst = (isv ? vst : const_cast<char *>(kst));
+                *reinterpret_cast<uint4 *>(dst + tile_off<C>(key, 2 * rp)) = lo;
+                *reinterpret_cast<uint4 *>(dst + tile_off<C>(key, 2 * rp + 1)) = hi;
             }
+            __syncthreads();  // the bf16 tile is complete and the raw stage is free
+            if (it + NST < ntiles) issue8(kt + NST * C::N, stage);
+        } else {
+            if (it + NST - 1 < ntiles) issue(kt + (NST - 1) * C::N, (it + NST - 1) % NST);
+            wait_tiles_ahead<VM, NST - 1>(min(NST - 1, ntiles - 1 - it));
+            kst = lds + stage * C::STAGE;
+            vst = const_cast<char *>(kst) + C::T_BYTES;
+            if (kt + C::N > seq_len) {
+                // V rows past the sequence may hold anything (NaN): zero them, since
+                // p = 0 does not cancel a NaN inside the MFMA
+                __syncthreads();
+                for (int i = threadIdx.x; i < C::N * C::PPR; i += 256) {
+                    const int row = i / C::PPR;
+                    if (kt + row >= seq_len)
+                        *reinterpret_cast<uint4 *>(vst + tile_off<C>(row, i % C::PPR)) =
+                            make_uint4(0, 0, 0, 0);
+                }
+            }
+            __syncthreads();  // every wave's DMA share of this tile is in
         }
-        __syncthreads();  // every wave's DMA share of this tile is in
 
         // ---- S^T = K Q^T, 32-key blocks ----
         // K fragments are streamed PF_K reads ahead of their MFMA (the
@@ -384,7 +480,9 @@ __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const 
                 if (PF_SCHED) __builtin_amdgcn_sched_barrier(0);
             }
         }
-        __syncthreads();  // everyone is done with this stage before it is refilled
+        // everyone is done with this stage before it is refilled (8-bit caches:
+        // the next iteration's first barrier protects the bf16 stage)
+        if constexpr (!KV8) __syncthreads();
     }
 
     // ---- finish: full exp-sum of the row, normalise, store ----
@@ -395,13 +493,14 @@ __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const 
     if (!row_valid) return;
     const int n_parts = p.partition ? pos / p.partition + 1 : 1;
     if (p.partition && part >= n_parts) return;  // no keys of this row here
-    float inv = 1.f / l;
+    // 8-bit caches: O holds code units of V, so the head's V scale joins 1/l
+    float inv = (KV8 ? p.v_scale[kvh] : 1.f) / l;
     if (n_parts == 1 && p.sinks) {
         // the head's sink: one more denominator term, no value (log2 units)
         const float s2 = p.sinks[head] * LOG2E_F;
         const float Mx = fmaxf(m, s2);
         const float a = exp2_diff(m, Mx);
-        inv = a / (l * a + exp2_diff(s2, Mx));
+        inv = (KV8 ? p.v_scale[kvh] : 1.f) * a / (l * a + exp2_diff(s2, Mx));
     }
     if (n_parts == 1) {
         uint16_t *orow = reinterpret_cast<uint16_t *>(p.out) + ((size_t)t_glob * p.hq + head) * D;
@@ -442,7 +541,7 @@ __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const 
 #define PA_PREFILL_NST(D) 2
 #endif
 
-template <int D>
+template <int D, bool KV8>
 hipError_t launch_d(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
     constexpr int N = PA_PREFILL_N(D), NST = PA_PREFILL_NST(D);
     const int TPW = 32 / p.group;
@@ -455,7 +554,7 @@ hipError_t launch_d(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
     const int64_t unit = XCD_CHUNK > 0 ? 8 * XCD_CHUNK : 1;
     const int blocks = (int)((items + unit - 1) / unit * unit);
     if (li) *li = LaunchInfo{{blocks, 1, 1}, 256, {N, NST, BQ}, 0};
-    hipLaunchKernelGGL((prefill_kernel<D, N, NST>), dim3(blocks), dim3(256), 0, stream, q);
+    hipLaunchKernelGGL((prefill_kernel<D, N, NST, KV8>), dim3(blocks), dim3(256), 0, stream, q);
     return hipGetLastError();
 }
 
@@ -466,11 +565,22 @@ bool prefill_supported(int dtype, int head_dim, int group) {
            group <= 8;
 }
 
+bool prefill_kv8_supported(int head_dim, int group) {
+    return (head_dim == 128 || head_dim == 256) && group >= 1 && group <= 8;
+}
+
 hipError_t launch_prefill(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
+    if (p.kv8) {
+        switch (p.head_dim) {
+            case 128: return launch_d<128, true>(p, stream, li);
+            case 256: return launch_d<256, true>(p, stream, li);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (p.head_dim) {
-        case 64: return launch_d<64>(p, stream, li);
-        case 128: return launch_d<128>(p, stream, li);
-        case 256: return launch_d<256>(p, stream, li);
+        case 64: return launch_d<64, false>(p, stream, li);
+        case 128: return launch_d<128, false>(p, stream, li);
+        case 256: return launch_d<256, false>(p, stream, li);
         default: return hipErrorInvalidValue;
     }
 }

@@ -139,10 +139,59 @@ def test_fp8_multi_token_windows(hq, hkv, d, bs):
     w = _fp8(w, seed=d + bs)
     ref = oracle.run_workload(w)
     b = to_device(w)
+    import paged_varlen_attention_amd as pa
     for P in (0, 256):
-        out = run_gpu(b, P)
+        parts = (pa.alloc_partials(w.total_q, hq, d, pa.max_partitions(w.max_seq_len, P), "cuda")
+                 if P else None)
+        out = run_gpu(b, P, partials=parts, reduce=False)
+        # 8-bit pages of 128- and 256-element heads run on the MFMA tiles
+        assert pa.last_dispatch()["path"] == ("tiled" if d >= 128 else "decode_per_token")
+        if P:
+            pa.split_kv_reduce(out, parts, b.cu_seqlens_q, b.seq_lens, P)
         torch.cuda.synchronize()
         assert_close(out, ref, torch.bfloat16, f"fp8 windows P={P}")
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (24, 4, 256), (16, 2, 256), (12, 4, 128),
+                                      (8, 8, 128)])
+def test_fp8_tiled_geometries(hq, hkv, d, bs):
+    """Ragged q_len 1..45 over cached prefixes 0..300 (several q-tiles and key
+    tiles with ragged tails) on 8-bit pages, every partition size."""
+    w = _fp8(W.random_case(7300 + hq * 7 + d + bs, num_seqs=6, max_q=45, max_ctx=300,
+                           num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
+                           dtype=torch.bfloat16), seed=hq + bs)
+    ref = oracle.run_workload(w)
+    b = to_device(w)
+    for P in (0, 256, 512):
+        out = run_gpu(b, P)
+        torch.cuda.synchronize()
+        assert_close(out, ref, torch.bfloat16, f"fp8 tiles P={P}")
+
+
+def test_fp8_mixed_chunked_prefill():
+    """The mixed chunked-prefill batch A (6,000 prompt tokens + 8 decode
+    tokens, 16/2/256) over 8-bit pages; every row, unsplit and split."""
+    w = _fp8(W.mixed_prefill_bf16(variant="A"), seed=3)
+    ref = oracle.run_workload(w)
+    b = to_device(w)
+    for P in (0, 512):
+        out = run_gpu(b, P)
+        torch.cuda.synchronize()
+        assert_close(out, ref, torch.bfloat16, f"fp8 mixed P={P}")
+
+
+def test_fp8_spec_verify_with_cache_write():
+    """Verify windows and two 512-token chunks over 1k..8k contexts, 144-token
+    blocks seen as 9x16 pages, the new K/V quantised by the cache write first;
+    every row, split at 1024."""
+    w = _fp8(W.spec_verify_bf16(), seed=5)
+    ref = oracle.run_workload(w)
+    b = to_device(w)
+    for P in (0, 1024):
+        out = run_gpu(b, P)
+        torch.cuda.synchronize()
+        assert_close(out, ref, torch.bfloat16, f"fp8 verify P={P}")
 
 
 def test_fp8_every_code_and_sinks():
