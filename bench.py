@@ -456,16 +456,21 @@ def main():
             num_blocks=8 * 8192 // 16 + 8, dtype=torch.bfloat16,
             description="8 x 4096-token prompt chunks over 4096 cached tokens, 16/2/256")
         for name, P3 in (("mixed_prefill_bf16_A", 0), ("mixed_prefill_bf16_B", 0),
-                         ("spec_verify_bf16", 1024), ("prefill_uniform_bf16", 0)):
+                         ("spec_verify_bf16", 1024), ("prefill_uniform_bf16", 0),
+                         ("mixed_prefill_fp8kv_B", 0), ("prefill_uniform_fp8kv", 0)):
+            kv8 = "fp8kv" in name
             try:
-                w3 = uniform() if name == "prefill_uniform_bf16" else W.CONFIGS[name]()
-                s3, k3, s3w, _ = measure(w3, P3, steps2, 5, 2, device)
+                if name.startswith("prefill_uniform"):
+                    w3 = uniform()
+                else:
+                    w3 = W.CONFIGS[name.replace("fp8kv", "bf16")]()
+                s3, k3, s3w, _ = measure(w3, P3, steps2, 5, 2, device, kv8=kv8)
             except Exception as e:  # report, do not hide: the line says what failed
                 sec_out[name] = {"error": str(e)[:200]}
                 log(f"{name}: {e}")
                 continue
             f3 = w3.algorithmic_flops()
-            b3 = step_bytes(w3, True)
+            b3 = step_bytes(w3, True, kv_elt_bytes=1 if kv8 else None)
             sec_out[name] = {
                 "partition_size": P3,
                 "ms_per_step": round(s3 * 1e3, 5),
