@@ -11,8 +11,8 @@
 //
 // The design is our own for CDNA4 (gfx950):
 //  * one workgroup = one q-tile of one request x one KV head (x one split-KV
-//    partition); 4 waves x 32 rows, the rows being (token, head-of-group)
-//    pairs, so every K/V tile loaded serves the whole GQA group;
+//    partition); 4 waves (8 at D = 256) x 32 rows, the rows being (token,
+//    head-of-group) pairs, so every K/V tile loaded serves the whole GQA group;
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: Q^T stays in registers as the
 //    B operand for the whole key loop, K tiles are the A operand read from LDS;
 //    a lane's accumulator column is one query row, so the softmax statistics
@@ -43,10 +43,11 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
 constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units
 
-template <int D, int N_, int NST_, bool KV8_ = false>
+template <int D, int N_, int NST_, bool KV8_ = false, int NWV_ = 4>
 struct PrefillCfg {
     static constexpr bool KV8 = KV8_;             // caches hold E4M3 codes
-    static constexpr int NWV = 4;                 // waves per workgroup
+    static constexpr int NWV = NWV_;              // waves per workgroup (4 or 8)
+    static constexpr int NTH = NWV * 64;          // threads per workgroup
     static constexpr int N = N_;                  // keys per tile
     static constexpr int NST = NST_;              // LDS stages
     static constexpr int NB = N / 32;             // 32-key blocks of S^T per tile
@@ -131,9 +132,10 @@ constexpr int XCD_CHUNK = PA_PREFILL_XCD_CHUNK;
 #endif
 constexpr bool PF_SCHED = PA_PREFILL_SCHED;
 
-template <int D, int N, int NST, bool KV8>
-__global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const AttnParams p) {
-    using C = PrefillCfg<D, N, NST, KV8>;
+template <int D, int N, int NST, bool KV8, int NWV>
+__global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefill_kernel(
+    const AttnParams p) {
+    using C = PrefillCfg<D, N, NST, KV8, NWV>;
     constexpr int PF_K = PA_PREFILL_PF_K(D), PF_V = PA_PREFILL_PF_V(D);
     __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
 
@@ -346,7 +348,7 @@ __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const 
             // conflict-free; V rows past the sequence become zeros (NaN codes
             // would survive p = 0 inside the MFMA)
             constexpr int CH = C::N * (D / 16);  // 16-byte raw pieces per tensor
-            for (int i = threadIdx.x; i < 2 * CH; i += 256) {
+            for (int i = threadIdx.x; i < 2 * CH; i += C::NTH) {
                 const bool isv = i >= CH;
                 const int ii = isv ? i - CH : i;
                 const int key = ii % C::N, rp = ii / C::N;
@@ -382,7 +384,7 @@ __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const 
                 // V rows past the sequence may hold anything (NaN): zero them, since
                 // p = 0 does not cancel a NaN inside the MFMA
                 __syncthreads();
-                for (int i = threadIdx.x; i < C::N * C::PPR; i += 256) {
+                for (int i = threadIdx.x; i < C::N * C::PPR; i += C::NTH) {
                     const int row = i / C::PPR;
                     if (kt + row >= seq_len)
                         *reinterpret_cast<uint4 *>(vst + tile_off<C>(row, i % C::PPR)) =
@@ -533,7 +535,12 @@ __global__ __launch_bounds__(256, PA_PREFILL_MINW(D)) void prefill_kernel(const 
     }
 }
 
-// Keys per tile and LDS stages by head size.
+// Keys per tile, LDS stages and waves per workgroup by head size.  D = 256
+// runs 8 waves (one workgroup per CU, each K/V tile in LDS serving 256 rows):
+// 3-5% faster on long prompts than two 4-wave workgroups; D <= 128 keeps 4.
+#ifndef PA_PREFILL_NWV
+#define PA_PREFILL_NWV(D) ((D) >= 256 ? 8 : 4)
+#endif
 #ifndef PA_PREFILL_N
 #define PA_PREFILL_N(D) ((D) >= 256 ? 32 : 64)
 #endif
@@ -545,7 +552,8 @@ template <int D, bool KV8>
 hipError_t launch_d(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
     constexpr int N = PA_PREFILL_N(D), NST = PA_PREFILL_NST(D);
     const int TPW = 32 / p.group;
-    const int BQ = PrefillCfg<D, N, NST>::NWV * TPW;
+    constexpr int NWV = PA_PREFILL_NWV(D);
+    const int BQ = NWV * TPW;
     AttnParams q = p;
     q.grid_tiles = p.total_q / BQ + p.num_seqs;
     q.grid_parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
@@ -553,8 +561,9 @@ hipError_t launch_d(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
     if (items > INT32_MAX - 4096) return hipErrorInvalidConfiguration;
     const int64_t unit = XCD_CHUNK > 0 ? 8 * XCD_CHUNK : 1;
     const int blocks = (int)((items + unit - 1) / unit * unit);
-    if (li) *li = LaunchInfo{{blocks, 1, 1}, 256, {N, NST, BQ}, 0};
-    hipLaunchKernelGGL((prefill_kernel<D, N, NST, KV8>), dim3(blocks), dim3(256), 0, stream, q);
+    if (li) *li = LaunchInfo{{blocks, 1, 1}, NWV * 64, {N, NST, BQ}, 0};
+    hipLaunchKernelGGL((prefill_kernel<D, N, NST, KV8, NWV>), dim3(blocks), dim3(NWV * 64), 0,
+                       stream, q);
     return hipGetLastError();
 }
 
