@@ -11,8 +11,9 @@
 //
 // The design is our own for CDNA4 (gfx950):
 //  * one workgroup = one q-tile of one request x one KV head (x one split-KV
-//    partition); 4 waves (8 at D = 256) x 32 rows, the rows being (token,
-//    head-of-group) pairs, so every K/V tile loaded serves the whole GQA group;
+//    partition); 4 waves (8 at D = 256 on large batches) x 32 rows, the rows
+//    being (token, head-of-group) pairs, so every K/V tile loaded serves the
+//    whole GQA group;
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: Q^T stays in registers as the
 //    B operand for the whole key loop, K tiles are the A operand read from LDS;
 //    a lane's accumulator column is one query row, so the softmax statistics
@@ -535,11 +536,14 @@ __global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefil
     }
 }
 
-// Keys per tile, LDS stages and waves per workgroup by head size.  D = 256
-// runs 8 waves (one workgroup per CU, each K/V tile in LDS serving 256 rows):
-// 3-5% faster on long prompts than two 4-wave workgroups; D <= 128 keeps 4.
-#ifndef PA_PREFILL_NWV
-#define PA_PREFILL_NWV(D) ((D) >= 256 ? 8 : 4)
+// Keys per tile and LDS stages by head size.  Waves per workgroup: 4, or at
+// D = 256 on large batches 8 (one workgroup per CU, each K/V tile in LDS
+// serving 256 rows): 5% faster on long uniform prompts, but 3-4% slower on
+// ragged batches of a few hundred workgroups, whose critical path the larger
+// q-tiles lengthen.  The switch is at PA_PREFILL_WIDE_ITEMS work items of
+// 8-wave size (4 per CU on 256 CUs).
+#ifndef PA_PREFILL_WIDE_ITEMS
+#define PA_PREFILL_WIDE_ITEMS 1024
 #endif
 #ifndef PA_PREFILL_N
 #define PA_PREFILL_N(D) ((D) >= 256 ? 32 : 64)
@@ -548,11 +552,10 @@ __global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefil
 #define PA_PREFILL_NST(D) 2
 #endif
 
-template <int D, bool KV8>
-hipError_t launch_d(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
+template <int D, bool KV8, int NWV>
+hipError_t launch_dw(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
     constexpr int N = PA_PREFILL_N(D), NST = PA_PREFILL_NST(D);
     const int TPW = 32 / p.group;
-    constexpr int NWV = PA_PREFILL_NWV(D);
     const int BQ = NWV * TPW;
     AttnParams q = p;
     q.grid_tiles = p.total_q / BQ + p.num_seqs;
@@ -565,6 +568,17 @@ hipError_t launch_d(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
     hipLaunchKernelGGL((prefill_kernel<D, N, NST, KV8, NWV>), dim3(blocks), dim3(NWV * 64), 0,
                        stream, q);
     return hipGetLastError();
+}
+
+template <int D, bool KV8>
+hipError_t launch_d(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
+    if constexpr (D >= 256) {
+        const int64_t bq8 = 8 * (32 / p.group);
+        const int64_t parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
+        const int64_t items8 = (p.total_q / bq8 + p.num_seqs) * p.hkv * parts;
+        if (items8 >= PA_PREFILL_WIDE_ITEMS) return launch_dw<D, KV8, 8>(p, stream, li);
+    }
+    return launch_dw<D, KV8, 4>(p, stream, li);
 }
 
 }  // namespace

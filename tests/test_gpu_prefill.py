@@ -129,3 +129,30 @@ def test_large_partitions(max_q):
         out = run_gpu(b, P)
         torch.cuda.synchronize()
         assert_close(out, ref, torch.bfloat16, f"max_q={max_q} P={P}")
+
+
+@pytest.mark.parametrize("kv8", [False, True], ids=["bf16", "fp8"])
+def test_wide_workgroups(kv8):
+    """A D=256 batch large enough for 8-wave workgroups (64/8 heads, ten
+    450..500-token prompts over short prefixes): the launch takes the 8-wave
+    kernel, and sampled rows match the oracle; also with 8-bit caches."""
+    import paged_varlen_attention_amd as pa
+    import oracle_pins as pins
+    from gpu_helpers import sample_rows
+    w = W.random_case(4242, num_seqs=10, min_q=450, max_q=500, max_ctx=200, num_q_heads=64,
+                      num_kv_heads=8, head_dim=256, block_size=16, dtype=torch.bfloat16)
+    if kv8:
+        w = pins.fp8_case(w, seed=42)
+    rows = sample_rows(w, 160, seed=3)
+    ref = oracle.run_workload(w, rows=rows)
+    b = to_device(w)
+    for P in (0, 256):
+        parts = (pa.alloc_partials(w.total_q, 64, 256, pa.max_partitions(w.max_seq_len, P), "cuda")
+                 if P else None)
+        out = run_gpu(b, P, partials=parts, reduce=False)
+        assert pa.last_dispatch()["block"] == 512  # 8 waves
+        if P:
+            pa.split_kv_reduce(out, parts, b.cu_seqlens_q, b.seq_lens, P, sinks=b.sinks)
+        torch.cuda.synchronize()
+        got = torch.stack([out[t, h] for t, h in rows])
+        assert_close(got, ref, torch.bfloat16, f"wide P={P}")
