@@ -44,12 +44,6 @@
 namespace pa {
 namespace {
 
-#ifndef PA_DECODE_HEAD_FASTEST
-#define PA_DECODE_HEAD_FASTEST 1
-#endif
-#ifndef PA_DECODE_ORDER
-#define PA_DECODE_ORDER 2
-#endif
 // Merge states a wave leaves in LDS: 1 = rows merged in registers first.
 #ifndef PA_DECODE_SPW_MAX
 #define PA_DECODE_SPW_MAX(L) 4
@@ -352,22 +346,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
     using C = DecodeCfg<T, KV8, D, GT, CT, NW, NST>;
     __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
 
-    // The KV heads of one partition are adjacent in the grid, so the
-    // workgroups that run together read the same pages (all heads' rows of a
-    // page are contiguous) rather than 1/Hkv of many different pages.
-#if PA_DECODE_ORDER == 0
-    const int kvh = PA_DECODE_HEAD_FASTEST ? blockIdx.x : blockIdx.y;
-    const int part = PA_DECODE_HEAD_FASTEST ? blockIdx.y : blockIdx.x;
-    const int zrow = blockIdx.z;
-#elif PA_DECODE_ORDER == 1   // partition-major: grid (hkv, rows, parts)
-    const int kvh = blockIdx.x;
-    const int part = blockIdx.z;
-    const int zrow = blockIdx.y;
-#else                        // partition-major, last partitions first
+    // Grid (hkv, rows, parts).  The KV heads of one partition are adjacent,
+    // so the workgroups that run together read the same pages (all heads'
+    // rows of a page are contiguous) rather than 1/Hkv of many different
+    // pages.  Partitions are slowest and taken last-first: the last, often
+    // partial, partitions of every request are dispatched first and the full
+    // first partitions last, which shortens the tail.
     const int kvh = blockIdx.x;
     const int part = gridDim.z - 1 - blockIdx.z;
     const int zrow = blockIdx.y;
-#endif
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane % C::L;    // column of the row this lane holds
@@ -687,11 +674,7 @@ hipError_t launch_t(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
     using Tn = DecodeTuning<T, KV8, D, GT>;
     const int parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
     const int rows = p.per_token ? p.total_q : p.num_seqs;
-#if PA_DECODE_ORDER == 0
-    dim3 grid = PA_DECODE_HEAD_FASTEST ? dim3(p.hkv, parts, rows) : dim3(parts, p.hkv, rows);
-#else
-    dim3 grid = dim3(p.hkv, rows, parts);
-#endif
+    const dim3 grid(p.hkv, rows, parts);
     dim3 block(Tn::NW * 64);
     if (li) *li = LaunchInfo{{(int)grid.x, (int)grid.y, (int)grid.z}, (int)block.x,
                              {Tn::CT, Tn::NW, Tn::NST}, 0};

@@ -27,9 +27,9 @@
 //    NST stages, one barrier per N-key tile;
 //  * requests are mapped to workgroups without a host pass: virtual tile x
 //    belongs to the last request r with cu[r]/BQ + r <= x (surplus tiles exit);
-//  * 8-bit E4M3 caches (the library's own KV quantisation, D >= 128): tiles
-//    arrive by DMA into an 8-bit LDS ring (one instruction = 8 keys x 128
-//    bytes, so it never crosses a page), and after a barrier all threads
+//  * 8-bit E4M3 caches (the library's own KV quantisation): tiles arrive by
+//    DMA into an 8-bit LDS ring (one instruction = 8 keys x 128 bytes, or 4
+//    whole 64-byte rows, so it never crosses a page), and after a barrier all threads
 //    convert the tile into the bf16 tile layout above with
 //    v_cvt_scalef32_pk_bf16_fp8 (exact), zeroing V rows past the sequence;
 //    the MFMA code is unchanged.  The head's K scale joins the softmax scale
@@ -68,11 +68,17 @@ struct PrefillCfg {
     static constexpr int RG = KV8 ? D : R;        // bytes of a cached K/V row of one head
     static constexpr int RAW_T = N * D;           // one 8-bit tile
     static constexpr int RAW_STAGE = 2 * RAW_T;
-    static constexpr int IPG8 = D / 128;          // DMA instructions per 8-key group, 8-bit
-    static constexpr int NI8_W = RAW_T / 1024 / NWV;  // per wave, per tensor, 8-bit
+    // 8-bit DMA: D >= 128 moves 8 keys x 128 bytes per instruction (16 bytes a
+    // lane); 64-byte rows (D = 64) move 4 whole rows per instruction (4 bytes
+    // a lane), landing row-major
+    static constexpr bool ROWS8 = D < 128;
+    static constexpr int DW8 = ROWS8 ? 4 : 16;
+    static constexpr int IPG8 = ROWS8 ? 1 : D / 128;  // instructions per 8-key group (D >= 128)
+    static constexpr int NI8_W = RAW_T / (64 * DW8) / NWV;  // per wave, per tensor, 8-bit
     static constexpr int RAW_BYTES = KV8 ? NST * RAW_STAGE : 0;
     static constexpr int LDS_BYTES = KV8 ? RAW_BYTES + STAGE : NST * STAGE;
-    static_assert(!KV8 || (D >= 128 && RAW_T % (1024 * NWV) == 0), "8-bit tile shape");
+    static_assert(!KV8 || ((D == 64 || D >= 128) && RAW_T % (64 * DW8 * NWV) == 0),
+                  "8-bit tile shape");
     static_assert(NI % NWV == 0, "tile split over the waves");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
     static_assert(2 * NI_W * (NST - 1) < 64, "vmcnt range");
@@ -267,8 +273,12 @@ __global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefil
 
     // 8-bit caches: instruction c of a raw tile covers key group c / IPG8,
     // bytes 128*(c % IPG8) .. +128 of those 8 rows; lane l brings 16 codes of
-    // key l%8, piece l/8, landing at c*1024 + 16*l of the raw tile.
-    const uint32_t dma_voff8 = (uint32_t)(lane & 7) * row_stride + (uint32_t)(lane >> 3) * 16u;
+    // key l%8, piece l/8, landing at c*1024 + 16*l of the raw tile.  With
+    // 64-byte rows, instruction c covers keys 4c .. 4c+3 whole (lane l: key
+    // l/16, bytes 4*(l%16)), landing row-major at c*256 + 4*l.
+    const uint32_t dma_voff8 =
+        C::ROWS8 ? (uint32_t)(lane >> 4) * row_stride + (uint32_t)(lane & 15) * 4u
+                 : (uint32_t)(lane & 7) * row_stride + (uint32_t)(lane >> 3) * 16u;
     auto issue8 = [&](int kt, int stage) {
         const int lp0 = kt >> lbs;
         if (lp0 + ((C::N - 1) >> lbs) - win_page >= 64) {  // long ranges: slide the window
@@ -278,14 +288,16 @@ __global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefil
 #pragma unroll
         for (int i = 0; i < C::NI8_W; ++i) {
             const int c = wave * C::NI8_W + i;
-            const int k8 = kt + C::KG * (c / C::IPG8);
+            // first key of the instruction (a 4- or 8-key group: never two pages)
+            const int k8 = kt + (C::ROWS8 ? 4 * c : C::KG * (c / C::IPG8));
             const int lp = min(k8 >> lbs, seq_pages - 1);
             const int phys = __builtin_amdgcn_readlane(btv, lp - win_page);
             const char *base = kc + (uint64_t)phys * page_bytes + head_off +
-                               (uint32_t)(k8 & (bs - 1)) * row_stride + 128 * (c % C::IPG8);
-            const uint32_t l = lds0 + stage * C::RAW_STAGE + c * 1024;
-            dma16(base, dma_voff8, l);
-            dma16(base + v_minus_k, dma_voff8, l + C::RAW_T);
+                               (uint32_t)(k8 & (bs - 1)) * row_stride +
+                               (C::ROWS8 ? 0 : 128 * (c % C::IPG8));
+            const uint32_t l = lds0 + stage * C::RAW_STAGE + c * 64 * C::DW8;
+            dma_lds<C::DW8>(base, dma_voff8, l);
+            dma_lds<C::DW8>(base + v_minus_k, dma_voff8, l + C::RAW_T);
         }
     };
 
@@ -353,9 +365,10 @@ __global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefil
                 const bool isv = i >= CH;
                 const int ii = isv ? i - CH : i;
                 const int key = ii % C::N, rp = ii / C::N;
-                const uint4 w = *reinterpret_cast<const uint4 *>(
-                    raw + (isv ? C::RAW_T : 0) + ((key >> 3) * C::IPG8 + (rp >> 3)) * 1024 +
-                    (((rp & 7) << 3) + (key & 7)) * 16);
+                const int roff = C::ROWS8 ? key * D + rp * 16
+                                          : ((key >> 3) * C::IPG8 + (rp >> 3)) * 1024 +
+                                                (((rp & 7) << 3) + (key & 7)) * 16;
+                const uint4 w = *reinterpret_cast<const uint4 *>(raw + (isv ? C::RAW_T : 0) + roff);
                 uint4 lo, hi;
                 if (isv && kt + key >= seq_len) {
                     lo = make_uint4(0, 0, 0, 0);
@@ -589,12 +602,13 @@ bool prefill_supported(int dtype, int head_dim, int group) {
 }
 
 bool prefill_kv8_supported(int head_dim, int group) {
-    return (head_dim == 128 || head_dim == 256) && group >= 1 && group <= 8;
+    return (head_dim == 64 || head_dim == 128 || head_dim == 256) && group >= 1 && group <= 8;
 }
 
 hipError_t launch_prefill(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
     if (p.kv8) {
         switch (p.head_dim) {
+            case 64: return launch_d<64, true>(p, stream, li);
             case 128: return launch_d<128, true>(p, stream, li);
             case 256: return launch_d<256, true>(p, stream, li);
             default: return hipErrorInvalidValue;

@@ -30,8 +30,6 @@ def test_zero_length_requests(d, kind):
     """Requests with q_len 0 (one with an empty cache, one with a prefix)
     between prefill, decode and verify requests; keys ending on page (16) and
     partition (256) boundaries."""
-    if kind == "fp8" and d == 64:
-        pytest.skip("64-element 8-bit heads take the per-token path, covered in test_gpu_fp8")
     q_lens = [0, 20, 0, 1, 0, 33, 256, 3]
     seq_lens = [0, 20, 17, 256, 0, 100, 512, 272]
     dt = torch.float32 if kind == "f32" else torch.bfloat16

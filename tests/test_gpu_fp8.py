@@ -144,8 +144,8 @@ def test_fp8_multi_token_windows(hq, hkv, d, bs):
         parts = (pa.alloc_partials(w.total_q, hq, d, pa.max_partitions(w.max_seq_len, P), "cuda")
                  if P else None)
         out = run_gpu(b, P, partials=parts, reduce=False)
-        # 8-bit pages of 128- and 256-element heads run on the MFMA tiles
-        assert pa.last_dispatch()["path"] == ("tiled" if d >= 128 else "decode_per_token")
+        # windows over 8-bit pages run on the MFMA tiles
+        assert pa.last_dispatch()["path"] == "tiled"
         if P:
             pa.split_kv_reduce(out, parts, b.cu_seqlens_q, b.seq_lens, P)
         torch.cuda.synchronize()
@@ -154,7 +154,7 @@ def test_fp8_multi_token_windows(hq, hkv, d, bs):
 
 @pytest.mark.parametrize("bs", [8, 16, 32])
 @pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (24, 4, 256), (16, 2, 256), (12, 4, 128),
-                                      (8, 8, 128)])
+                                      (8, 8, 128), (4, 1, 64), (14, 2, 64)])
 def test_fp8_tiled_geometries(hq, hkv, d, bs):
     """Ragged q_len 1..45 over cached prefixes 0..300 (several q-tiles and key
     tiles with ragged tails) on 8-bit pages, every partition size."""
