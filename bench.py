@@ -240,6 +240,7 @@ def measure(w, P, steps, warmup, copies, device, write_cache=True, kv8=False):
 
 
 DECODE_SOURCES = ("paged_varlen_attention_amd/csrc/decode.hip",
+                  "paged_varlen_attention_amd/csrc/decode_mfma.hip",
                   "paged_varlen_attention_amd/csrc/pa_device.h",
                   "paged_varlen_attention_amd/csrc/pa_internal.h")
 PMC_SUMMARY = "profiles/decode_gqa_decode_bf16_pmc.md"
@@ -400,7 +401,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_kernel (pa_varlen_attention, split 512)",
+            "kernel": "decode_mfma_kernel (pa_varlen_attention, split 512)",
             "achieved": round(achieved, 3),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -18,8 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_api.cpp", "cache_write.hip", "decode.hip", "reduce.hip", "prefill.hip",
-           "block_copy.hip"]
+SOURCES = ["pa_api.cpp", "cache_write.hip", "decode.hip", "decode_mfma.hip", "reduce.hip",
+           "prefill.hip", "block_copy.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -29,7 +29,8 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-ffp-contract=fast", "-fno-gpu-rdc"]
 # Per-source extras.  The MFMA kernel rescales its accumulators with VALU
 # instructions, which cannot read AGPRs: keep MFMA operands in VGPRs.
-EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -1,6 +1,8 @@
-// decode.hip -- paged GQA decode attention for gfx950: one workgroup per query
-// token (decode batches; and every token of fp32 batches, whose key range ends
-// at the token's own causal position).
+// decode.hip -- paged GQA decode attention for gfx950 on the vector ALUs: one
+// workgroup per query token (decode batches over 8-bit caches and fp32
+// batches; every token of fp32 batches, whose key range ends at the token's own
+// causal position).  bf16 decode batches over bf16 caches take the MFMA form
+// in decode_mfma.hip.
 //
 // What it computes follows the vllm-metal kernel walkthrough ("What is Paged
 // Attention"; GQA decode tips 1-4): softmax(q.k * scale) v over the keys of one
@@ -53,6 +55,10 @@ namespace {
 // on bf16 caches.
 #ifndef PA_DECODE_PRIO
 #define PA_DECODE_PRIO(KV8) (KV8)
+#endif
+// bf16 decode batches over bf16 caches take the MFMA kernel (decode_mfma.hip).
+#ifndef PA_DECODE_MFMA
+#define PA_DECODE_MFMA 1
 #endif
 #ifndef PA_DECODE_LAZY
 #define PA_DECODE_LAZY 1
@@ -718,6 +724,9 @@ bool decode_supported(int dtype, int head_dim, int group) {
 bool decode_kv8_supported(int head_dim, int group) { return decode_supported(1, head_dim, group); }
 
 hipError_t launch_decode(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
+#if PA_DECODE_MFMA
+    if (decode_mfma_supported(p)) return launch_decode_mfma(p, stream, li);
+#endif
     if (p.kv8) return p.dtype == 1 ? launch_dt<bf16_t, true>(p, stream, li) : hipErrorInvalidValue;
     if (p.dtype == 1) return launch_dt<bf16_t, false>(p, stream, li);
     return launch_dt<float, false>(p, stream, li);

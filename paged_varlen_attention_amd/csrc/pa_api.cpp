@@ -236,9 +236,11 @@ int varlen_attention_impl(pa_dispatch_info &rec, void *out, const void *q, const
         p.k_scale = kv8 ? k_scale : nullptr;
         p.v_scale = kv8 ? v_scale : nullptr;
 
-        // One query token per request -> the VALU decode kernel.  fp32 batches
-        // with longer windows also use it, one workgroup per query token; bf16
-        // prefill and mixed batches (bf16 or 8-bit caches) go to the MFMA tiles.
+        // One query token per request -> the decode kernels (bf16 MFMA for bf16
+        // caches, vector ALUs for 8-bit caches and fp32).  fp32 batches with
+        // longer windows also use the latter, one workgroup per query token;
+        // bf16 prefill and mixed batches (bf16 or 8-bit caches) go to the MFMA
+        // tiles.
         if (max_q_len == 1 || dtype == PA_F32) {
             if (kv8 ? !pa::decode_kv8_supported(head_dim, group)
                     : !pa::decode_supported(dtype, head_dim, group))
