@@ -1,6 +1,6 @@
 // decode_mfma.hip -- paged GQA decode attention for gfx950 with the group's
 // scores and PV on bf16 MFMA: decode batches (one query token per request)
-// with bf16 queries over bf16 caches.
+// with bf16 queries over bf16 or 8-bit (E4M3) caches.
 //
 // What it computes is the same as the VALU decode kernel (vllm-metal kernel
 // walkthrough, "What is Paged Attention"; GQA decode tips 1-4): softmax(q.k *
@@ -36,7 +36,16 @@
 //    the O^T column of a lane is its own head, so rescales are per lane;
 //  * the reference max is raised lazily (only when a chunk's max passes it by
 //    more than 8 in log2 units), and every wave is rescaled to the true max
-//    before the LDS merge, so the statistics stored for the reduce are exact.
+//    before the LDS merge, so the statistics stored for the reduce are exact;
+//  * 8-bit caches: 32-key chunks land as raw E4M3 rows (16-byte pieces XOR-
+//    swizzled by row) and are converted in registers after the fragment reads
+//    (v_cvt_scalef32_pk_bf16_fp8, exact).  S^T is two 16-key blocks whose rows
+//    are permuted so that a lane's 8 scores are 8 consecutive keys, the B
+//    operand of a 32-key v_mfma_f32_16x16x32_bf16 for O^T; its V^T operand
+//    (8 keys of one column) comes from ds_read_b64_tr_b8.  The head's K scale
+//    joins the softmax scale and its V scale the output.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -45,31 +54,38 @@ namespace {
 
 constexpr float MF_RESCALE_THRESHOLD = 8.0f;  // log2 units
 
-template <int D, int NW_, int NST_>
+template <int D, bool KV8_, int NW_, int NST_>
 struct MfCfg {
-    static constexpr int CT = 16;                // keys per chunk: the 16 rows of S^T
-    static constexpr int R = D * 2;              // bytes of a bf16 K/V row of one head
-    static constexpr int PPR = R / 16;           // 16-byte pieces per row
-    static constexpr int GROUP_BYTES = 8 * R;    // one 8-key group of the tile layout
+    static constexpr bool KV8 = KV8_;            // caches hold E4M3 codes
+    static constexpr int CT = KV8 ? 32 : 16;     // keys per chunk (one or two 16-row S^T blocks)
+    static constexpr int QR = D * 2;             // bytes of a bf16 query row of one head
+    static constexpr int R = KV8 ? D : 2 * D;    // bytes of a cached K/V row of one head
     static constexpr int TILE = CT * R;          // K (or V) tile of one chunk
     static constexpr int SLOT = 2 * TILE;        // one LDS stage: K tile, then V tile
-    static constexpr int IPG = PPR / 8;          // DMA instructions per key group (1 KB each)
-    static constexpr int NI = 2 * IPG;           // per tile
+    // bytes one lane moves per DMA instruction: 16, or 4 for 64-byte 8-bit
+    // rows (so one instruction never spans more than 8 rows, i.e. one page)
+    static constexpr int DW = (KV8 && D < 128) ? 4 : 16;
+    static constexpr int NI = TILE / (64 * DW);  // DMA instructions per tile
+    static constexpr int RPI = 64 * DW / R;      // rows per instruction (8-bit tiles)
     static constexpr int VM_PER_CHUNK = 2 * NI;  // K and V
+    static constexpr int PPR = R / 16;           // 16-byte pieces per row
+    static constexpr int GROUP_BYTES = 8 * R;    // one 8-key group of the bf16 tile layout
+    static constexpr int IPG = PPR / 8;          // bf16: DMA instructions per key group (1 KB each)
     static constexpr int KS = D / 32;            // k-steps of S^T (16x16x32)
-    static constexpr int DB = D / 16;            // 16-row blocks of O^T (16x16x16)
+    static constexpr int DB = D / 16;            // 16-row blocks of O^T
     static constexpr int NW = NW_;
     static constexpr int NST = NST_;
     static constexpr int GMAX = 8;               // largest group served
     static constexpr int STATE_FLOATS = GMAX * D + 2 * GMAX;  // O^T rows of the group, m, l
     static constexpr int STAGE_BYTES = NW * NST * SLOT;
-    static constexpr int QI = (GMAX * R + 1023) / 1024;  // most DMA instructions for a group's queries
+    static constexpr int QI = (GMAX * QR + 1023) / 1024;  // most DMA instructions for a group's queries
     static constexpr int QBYTES = QI * 1024;     // per wave: the group's query rows
     static constexpr int RING_BYTES = STAGE_BYTES + NW * QBYTES;
     static constexpr int MERGE_BYTES = NW * STATE_FLOATS * 4;
     static constexpr int LDS_BYTES = RING_BYTES > MERGE_BYTES ? RING_BYTES : MERGE_BYTES;
-    static_assert(PPR % 8 == 0, "whole 128-byte lines per row");
-    static_assert((NST - 1) * VM_PER_CHUNK < 64, "vmcnt range");
+    static_assert(KV8 || PPR % 8 == 0, "whole 128-byte lines per row");
+    static_assert(!KV8 || (RPI >= 1 && RPI <= 8 && CT % RPI == 0), "8-bit DMA shape");
+    static_assert(NST * VM_PER_CHUNK < 64, "vmcnt range");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -78,6 +94,34 @@ struct MfCfg {
 template <int R>
 __device__ __forceinline__ int mf_tile_off(int key, int piece) {
     return (key >> 3) * (8 * R) + piece * 128 + (((key & 7) ^ ((piece & 1) << 2)) << 4);
+}
+
+// Byte offset of 16-byte piece p of row t (0..31) in an 8-bit tile of D-byte
+// rows: row-major with the piece index XORed by f(t).  With a = bits 3-4 of
+// t, e = bit 2 and c = bits 0-1, A = a ^ 2e, and f = A (D = 64), 2A + c/2
+// (D = 128) or 4A + c (D = 256), the two fragment reads are free of bank
+// conflicts: 16 lanes reading one 8-byte column of rows 8a' + 4e' + c' (S^T
+// K rows, e' fixed) or of the 8 rows 8a' .. 8a'+7 (V^T transpose reads) all
+// land on distinct 8-byte words of a 256-byte bank line.
+template <int D>
+__device__ __forceinline__ int kv8_f(int t) {
+    const int A = (((t >> 3) ^ (((t >> 2) & 1) << 1)) & 3);
+    if constexpr (D == 64) return A;
+    else if constexpr (D == 128) return (A << 1) | ((t & 3) >> 1);
+    else return (A << 2) | (t & 3);
+}
+template <int D>
+__device__ __forceinline__ int kv8_off(int t, int p) {
+    return t * D + ((p ^ kv8_f<D>(t)) << 4);
+}
+
+// Eight E4M3 codes (two words) -> eight bf16 (exact).
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+    const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    const auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // Wait until this wave's DMA for the chunk `ahead` chunks before the newest
@@ -193,6 +237,106 @@ __device__ __forceinline__ void mf_chunk(Frags<C> &f, const bf16x8_t (&qb)[C::KS
     }
 }
 
+// An 8-bit chunk's fragments, raw codes: K rows of both S^T blocks (8 dims
+// of one key each) and V^T (8 keys of one column each).
+template <class C>
+struct Frags8 {
+    uint2 k[2][C::KS];
+    uint2 v[C::DB];
+};
+
+// Fragment reads of an 8-bit stage.  S^T block b2 row r holds key
+// 8 (r / 4) + r % 4 + 4 b2, so the lane of column c and group g ends up with
+// the scores of keys 8 g .. 8 g + 7.  The V^T transpose read: lane j of group g
+// passes row 8 g + j / 2, bytes 16 b + 8 (j % 2) .. +7, and receives column
+// 16 b + j of rows 8 g .. 8 g + 7.
+template <class C, int D>
+__device__ __forceinline__ void mf_read8(const char *st, int col, int grp, Frags8<C> &f) {
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) {
+        const int t = 8 * (col >> 2) + (col & 3) + 4 * b2;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+            f.k[b2][ks] = *reinterpret_cast<const uint2 *>(st + kv8_off<D>(t, 2 * ks + (grp >> 1)) +
+                                                           8 * (grp & 1));
+    }
+    const int tv = 8 * grp + (col >> 1);
+#pragma unroll
+    for (int b = 0; b < C::DB; ++b) {
+        typedef __attribute__((ext_vector_type(2))) int i32x2_t;
+        const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2_t *)(st + C::TILE + kv8_off<D>(tv, b) +
+                                                          8 * (col & 1)));
+        f.v[b] = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+    }
+}
+
+// One 32-key 8-bit chunk: S^T (two blocks), online softmax, O^T with K = 32.
+template <class C, bool MASKED>
+__device__ __forceinline__ void mf_chunk8(Frags8<C> &f, const bf16x8_t (&qb)[C::KS], int key0,
+                                          int tok_end, float scale_log2, float &m, float &mtrue,
+                                          float &l, f32x4_t (&o)[C::DB]) {
+    f32x4_t s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2)
+            s[b2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                e4m3x8_to_bf16(f.k[b2][ks].x, f.k[b2][ks].y), qb[ks], s[b2], 0, 0, 0);
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        x[j] = s[j >> 2][j & 3] * scale_log2;  // key key0 + j
+        if (MASKED && key0 + j >= tok_end) x[j] = NEG_INF;
+    }
+    float cmax = x[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, x[j]);
+    const float cm = rows_max(cmax);
+    mtrue = fmaxf(mtrue, cm);
+    if constexpr (!MASKED) {
+        const bool up = cm > m + MF_RESCALE_THRESHOLD;
+        if (__builtin_amdgcn_ballot_w64(up)) {
+            const float mn = up ? cm : m;
+            const float alpha = exp2_diff(m, mn);
+            m = mn;
+            l *= alpha;
+#pragma unroll
+            for (int b = 0; b < C::DB; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[b][i] *= alpha;
+        }
+    } else {
+        const float mn = fmaxf(m, cm);
+        const float alpha = exp2_diff(m, mn);
+        m = mn;
+        l *= alpha;
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[b][i] *= alpha;
+    }
+    float pr[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        pr[j] = MASKED ? exp2_diff(x[j], m) : __builtin_amdgcn_exp2f(x[j] - m);
+        l += pr[j];
+    }
+    const uint4 pw = make_uint4(pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3]),
+                                pack_bf16(pr[4], pr[5]), pack_bf16(pr[6], pr[7]));
+    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+    for (int b = 0; b < C::DB; ++b) {
+        bf16x8_t a = e4m3x8_to_bf16(f.v[b].x, f.v[b].y);
+        if constexpr (MASKED) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (key0 + j >= tok_end) a[j] = (__bf16)0.f;
+        }
+        o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[b], 0, 0, 0);
+    }
+}
+
 // Register staging: a chunk's fragments are read into registers as soon as
 // it lands, and its LDS stage is refilled right away, so NST + 1 chunks are in
 // flight while a wave computes instead of NST - 1.
@@ -203,10 +347,14 @@ __device__ __forceinline__ void mf_chunk(Frags<C> &f, const bf16x8_t (&qb)[C::KS
 #ifndef PA_MF_STAGE
 #define PA_MF_STAGE 1
 #endif
+// 8-bit caches on this kernel (else the vector-ALU decode kernel).
+#ifndef PA_MF_KV8
+#define PA_MF_KV8 1
+#endif
 
-template <int D, int NW, int NST>
+template <int D, bool KV8, int NW, int NST>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const AttnParams p) {
-    using C = MfCfg<D, NW, NST>;
+    using C = MfCfg<D, KV8, NW, NST>;
     __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
 
     const int kvh = blockIdx.x;
@@ -215,13 +363,13 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const AttnParams p
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15;  // MFMA column: head `col` of the group
-    const int grp = lane >> 4;  // lane group: keys 4 grp .. 4 grp + 3 of a chunk
+    const int grp = lane >> 4;  // lane group: keys 4 grp .. 4 grp + 3 of a 16-key block
     constexpr int CT = C::CT;
     const int tok_begin = p.partition ? part * p.partition : 0;
     const int bs = p.block_size;
     const int lbs = p.log2_bs;
     const int c_begin = tok_begin / CT;
-    const int ppc = bs < CT ? CT / bs : 1;  // pages per chunk: 1, or 2 for 8-token pages
+    const int ppc = bs < CT ? CT / bs : 1;  // pages per chunk: 1, 2 or 4
     const int cpw = 64 / ppc;               // chunks covered by one block-table window
 
     // Block-table window: lane i holds page (i / cpw) of the wave's chunk
@@ -256,11 +404,26 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const AttnParams p
     const uint64_t page_bytes = (uint64_t)bs * row_stride;
     const uint64_t head_off = (uint64_t)kvh * C::R;
 
-    // DMA lane offsets: lane i of an instruction fills tile slot i of a
-    // 1 KB block (8 pieces of one 8-key group), i.e. key (i % 8) ^ 4 ((i / 8) & 1)
-    // of the group and piece 8 q + i / 8.
+    // DMA lane offsets.  bf16: lane i of an instruction fills tile slot i of
+    // a 1 KB block (8 pieces of one 8-key group), i.e. key (i % 8) ^ 4 ((i / 8) & 1)
+    // of the group and piece 8 q + i / 8.  8-bit: instruction n fills rows
+    // n RPI .. (n + 1) RPI - 1 of the tile, lane i the DW bytes at tile offset
+    // n 64 DW + i DW, which hold piece s ^ f(row) of its row (s = the slot).
     const int dkey = (lane & 7) ^ (((lane >> 3) & 1) << 2);
     const uint32_t voff0 = (uint32_t)dkey * row_stride + (uint32_t)(lane >> 3) * 16;
+    uint32_t voff8[KV8 ? C::NI : 1];
+    if constexpr (KV8) {
+        constexpr int LPR = C::R / C::DW;  // lanes per row
+#pragma unroll
+        for (int n = 0; n < C::NI; ++n) {
+            const int ri = lane / LPR;     // row within the instruction
+            const int w = lane % LPR;      // DW-byte word within the row
+            const int t = n * C::RPI + ri;
+            const int slot = w * C::DW / 16;
+            const int piece = slot ^ kv8_f<D>(t);
+            voff8[n] = (uint32_t)ri * row_stride + (uint32_t)(piece * 16 + (w * C::DW) % 16);
+        }
+    }
     const uint32_t lds_wave = lds_addr(lds) + (uint32_t)(wave * NST * C::SLOT);
 
     auto issue = [&](int k, int s) {
@@ -271,30 +434,48 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const AttnParams p
         const int tok0 = (c_begin + wave + k * NW) * CT;
         const int idx = k - win_base;
         const int phys0 = __builtin_amdgcn_readlane(btv, idx);
-        const uint64_t off0 = (uint64_t)phys0 * page_bytes +
-                              (uint64_t)(tok0 & (bs - 1)) * row_stride + head_off;
-        uint64_t off1 = off0 + 8ull * row_stride;
-        if (ppc == 2) {
-            // keys 8..15 live in the next page; past the sequence those keys
-            // are masked, so page 0 is re-read instead.
-            const int phys1 =
-                tok0 + 8 < seq_len ? __builtin_amdgcn_readlane(btv, idx + cpw) : phys0;
-            off1 = (uint64_t)phys1 * page_bytes + head_off;
+        if constexpr (KV8) {
+            // rows n RPI.. of the chunk are in page (n RPI) / bs of the chunk;
+            // pages past the sequence hold only masked keys: page 0 is re-read
+            const uint32_t ldsk = lds_wave + (uint32_t)(s * C::SLOT);
+#pragma unroll
+            for (int n = 0; n < C::NI; ++n) {
+                const int t0 = n * C::RPI;
+                const int j = bs < CT ? (t0 >> lbs) : 0;
+                const int phys = (j == 0 || tok0 + j * bs >= seq_len)
+                                     ? phys0
+                                     : __builtin_amdgcn_readlane(btv, idx + j * cpw);
+                const uint64_t off = (uint64_t)phys * page_bytes +
+                                     (uint64_t)((tok0 + t0) & (bs - 1)) * row_stride + head_off;
+                dma_lds<C::DW>(kc + off, voff8[n], ldsk + n * 64 * C::DW);
+                dma_lds<C::DW>(kc + off + v_minus_k, voff8[n], ldsk + C::TILE + n * 64 * C::DW);
+            }
+        } else {
+            const uint64_t off0 = (uint64_t)phys0 * page_bytes +
+                                  (uint64_t)(tok0 & (bs - 1)) * row_stride + head_off;
+            uint64_t off1 = off0 + 8ull * row_stride;
+            if (ppc == 2) {
+                // keys 8..15 live in the next page; past the sequence those keys
+                // are masked, so page 0 is re-read instead.
+                const int phys1 =
+                    tok0 + 8 < seq_len ? __builtin_amdgcn_readlane(btv, idx + cpw) : phys0;
+                off1 = (uint64_t)phys1 * page_bytes + head_off;
+            }
+            const char *kb[2] = {kc + off0, kc + off1};
+            const uint32_t ldsk = lds_wave + (uint32_t)(s * C::SLOT);
+            const uint32_t ldsv = ldsk + C::TILE;
+#pragma unroll
+            for (int gk = 0; gk < 2; ++gk)
+#pragma unroll
+                for (int q = 0; q < C::IPG; ++q)
+                    dma_lds<16>(kb[gk], voff0 + q * 128, ldsk + gk * C::GROUP_BYTES + q * 1024);
+#pragma unroll
+            for (int gk = 0; gk < 2; ++gk)
+#pragma unroll
+                for (int q = 0; q < C::IPG; ++q)
+                    dma_lds<16>(kb[gk] + v_minus_k, voff0 + q * 128,
+                                ldsv + gk * C::GROUP_BYTES + q * 1024);
         }
-        const char *kb[2] = {kc + off0, kc + off1};
-        const uint32_t ldsk = lds_wave + (uint32_t)(s * C::SLOT);
-        const uint32_t ldsv = ldsk + C::TILE;
-#pragma unroll
-        for (int gk = 0; gk < 2; ++gk)
-#pragma unroll
-            for (int q = 0; q < C::IPG; ++q)
-                dma_lds<16>(kb[gk], voff0 + q * 128, ldsk + gk * C::GROUP_BYTES + q * 1024);
-#pragma unroll
-        for (int gk = 0; gk < 2; ++gk)
-#pragma unroll
-            for (int q = 0; q < C::IPG; ++q)
-                dma_lds<16>(kb[gk] + v_minus_k, voff0 + q * 128,
-                            ldsv + gk * C::GROUP_BYTES + q * 1024);
     };
 
     // Chunk 0 first (its issue waits for the block-table window), then the
@@ -308,8 +489,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const AttnParams p
         issue(0, 0);
         const uint32_t lds_q = lds_addr(lds) + (uint32_t)(C::STAGE_BYTES + wave * C::QBYTES);
         const char *qg = reinterpret_cast<const char *>(p.q) +
-                         ((size_t)q0 * p.hq + (size_t)kvh * G) * C::R;
-        const int qbytes = G * C::R;
+                         ((size_t)q0 * p.hq + (size_t)kvh * G) * C::QR;
+        const int qbytes = G * C::QR;
 #pragma unroll
         for (int j = 0; j < C::QI; ++j) {
             if (j * 1024 < qbytes) {
@@ -323,7 +504,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const AttnParams p
         // Q^T, the B operand of S^T: head `col` (zero past the group), dims
         // 32 ks + 8 grp .. +7 of k-step ks
         mf_wait_ahead<C::VM_PER_CHUNK, PRE - 1>(min(PRE, nmy) - 1);
-        const char *qrow = lds + C::STAGE_BYTES + wave * C::QBYTES + col * C::R + 16 * grp;
+        const char *qrow = lds + C::STAGE_BYTES + wave * C::QBYTES + col * C::QR + 16 * grp;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
             if (col < G) {
@@ -341,19 +522,27 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const AttnParams p
     f32x4_t o[C::DB];
 #pragma unroll
     for (int b = 0; b < C::DB; ++b) o[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const float scale_log2 = p.scale_log2;
-    // fragment addresses inside a stage: K rows `col`, pieces 4 ks + grp; V^T
-    // transpose reads of key 4 grp + col / 4, elements 16 b + 4 (col % 4)
-    const int ka_off = mf_tile_off<C::R>(col, grp);
-    const int va_off = C::TILE + mf_tile_off<C::R>(4 * grp + (col >> 2), (col >> 1) & 1) + (col & 1) * 8;
+    // 8-bit caches: the head's K scale joins the softmax scale
+    const float scale_log2 = KV8 ? p.scale_log2 * p.k_scale[kvh] : p.scale_log2;
+    // bf16 fragment addresses inside a stage: K rows `col`, pieces 4 ks + grp;
+    // V^T transpose reads of key 4 grp + col / 4, elements 16 b + 4 (col % 4)
+    const int ka_off = KV8 ? 0 : mf_tile_off<C::R>(col, grp);
+    const int va_off =
+        KV8 ? 0 : C::TILE + mf_tile_off<C::R>(4 * grp + (col >> 2), (col >> 1) & 1) + (col & 1) * 8;
+    using F = typename std::conditional<KV8, Frags8<C>, Frags<C>>::type;
+    auto read = [&](const char *st, F &f) {
+        if constexpr (KV8)
+            mf_read8<C, D>(st, col, grp, f);
+        else
+            mf_read<C>(st + ka_off, st + va_off, f);
+    };
 
     // Land chunk k and read its fragments.  Without staging the stage it
     // reads is refilled one step later; with staging right after the reads.
-    auto stage = [&](int k, Frags<C> &f) {
+    auto stage = [&](int k, F &f) {
         if constexpr (PA_MF_STAGE) {
             mf_wait_ahead<C::VM_PER_CHUNK, NST - 1>(min(NST - 1, nmy - 1 - k));
-            const char *st = lds + (wave * NST + k % NST) * C::SLOT;
-            mf_read<C>(st + ka_off, st + va_off, f);
+            read(lds + (wave * NST + k % NST) * C::SLOT, f);
             if (k + NST < nmy) {
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage k is read
                 issue(k + NST, k % NST);
@@ -361,20 +550,26 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const AttnParams p
         } else {
             if (k + NST - 1 < nmy) issue(k + NST - 1, (k + NST - 1) % NST);
             mf_wait_ahead<C::VM_PER_CHUNK, NST - 1>(min(NST - 1, nmy - 1 - k));
-            const char *st = lds + (wave * NST + k % NST) * C::SLOT;
-            mf_read<C>(st + ka_off, st + va_off, f);
+            read(lds + (wave * NST + k % NST) * C::SLOT, f);
         }
     };
+    auto step = [&](F &f, auto masked, int key0) {
+        if constexpr (KV8)
+            mf_chunk8<C, decltype(masked)::value>(f, qb, key0, tok_end, scale_log2, m, mtrue, l, o);
+        else
+            mf_chunk<C, decltype(masked)::value>(f, qb, key0, tok_end, scale_log2, m, mtrue, l, o);
+    };
     for (int k = 0; k < nmy - 1; ++k) {
-        Frags<C> f;
+        F f;
         stage(k, f);
-        mf_chunk<C, false>(f, qb, 0, 0, scale_log2, m, mtrue, l, o);
+        step(f, std::false_type{}, 0);
     }
     if (nmy > 0) {
-        Frags<C> f;
+        F f;
         stage(nmy - 1, f);
-        const int key0 = (c_begin + wave + (nmy - 1) * NW) * CT + 4 * grp;
-        mf_chunk<C, true>(f, qb, key0, tok_end, scale_log2, m, mtrue, l, o);
+        // key of the lane's first score: 4 grp (bf16 block) or 8 grp (8-bit pair of blocks)
+        const int key0 = (c_begin + wave + (nmy - 1) * NW) * CT + (KV8 ? 8 : 4) * grp;
+        step(f, std::true_type{}, key0);
     }
 
     // ---- the wave's state: exp-sum over its 4 lane groups, everything
@@ -405,6 +600,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const AttnParams p
     __syncthreads();
 
     const bool direct = nparts <= 1;
+    const float vscale = KV8 ? p.v_scale[kvh] : 1.0f;  // 8-bit caches: the head's V scale
     for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
         const int g = idx / D;
         const int d = idx - g * D;
@@ -428,6 +624,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const AttnParams p
             const float a = exp2_diff(M, Mx);
             o_ = num * a / (den * a + exp2_diff(s2, Mx));
         }
+        if constexpr (KV8) o_ *= vscale;
         if (direct) {
             reinterpret_cast<uint16_t *>(p.out)[((size_t)q0 * p.hq + h) * D + d] = to_bf16(o_);
         } else {
@@ -450,32 +647,39 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const AttnParams p
 #define PA_MF_NST(D) 2
 #endif
 
-template <int D>
+template <int D, bool KV8>
 hipError_t launch_mf(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
     constexpr int NW = PA_MF_NW(D);
     constexpr int NST = PA_MF_NST(D);
     const int parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
     const dim3 grid(p.hkv, p.num_seqs, parts);
     const dim3 block(NW * 64);
-    if (li) *li = LaunchInfo{{(int)grid.x, (int)grid.y, (int)grid.z}, (int)block.x, {16, NW, NST}, 0};
-    hipLaunchKernelGGL((decode_mfma_kernel<D, NW, NST>), grid, block, 0, stream, p);
+    if (li)
+        *li = LaunchInfo{{(int)grid.x, (int)grid.y, (int)grid.z}, (int)block.x,
+                         {MfCfg<D, KV8, NW, NST>::CT, NW, NST}, 0};
+    hipLaunchKernelGGL((decode_mfma_kernel<D, KV8, NW, NST>), grid, block, 0, stream, p);
     return hipGetLastError();
+}
+
+template <bool KV8>
+hipError_t launch_mf_d(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
+    switch (p.head_dim) {
+        case 64: return launch_mf<64, KV8>(p, stream, li);
+        case 128: return launch_mf<128, KV8>(p, stream, li);
+        case 256: return launch_mf<256, KV8>(p, stream, li);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
 bool decode_mfma_supported(const AttnParams &p) {
-    return !p.per_token && p.dtype == 1 && !p.kv8 && p.group >= 1 && p.group <= 8 &&
-           (p.head_dim == 64 || p.head_dim == 128 || p.head_dim == 256);
+    return !p.per_token && p.dtype == 1 && (!p.kv8 || PA_MF_KV8) && p.group >= 1 &&
+           p.group <= 8 && (p.head_dim == 64 || p.head_dim == 128 || p.head_dim == 256);
 }
 
 hipError_t launch_decode_mfma(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
-    switch (p.head_dim) {
-        case 64: return launch_mf<64>(p, stream, li);
-        case 128: return launch_mf<128>(p, stream, li);
-        case 256: return launch_mf<256>(p, stream, li);
-        default: return hipErrorInvalidValue;
-    }
+    return p.kv8 ? launch_mf_d<true>(p, stream, li) : launch_mf_d<false>(p, stream, li);
 }
 
 }  // namespace pa
