@@ -156,3 +156,30 @@ def test_wide_workgroups(kv8):
         torch.cuda.synchronize()
         got = torch.stack([out[t, h] for t, h in rows])
         assert_close(got, ref, torch.bfloat16, f"wide P={P}")
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_wide_workgroups_long_prompts(bs):
+    """8-wave workgroups (64/8 heads, D=256) over prompts of 1,500..2,000
+    tokens on short cached prefixes: each workgroup walks dozens of key tiles,
+    the last one cut by the sequence end (V rows past it zeroed); sampled rows
+    include every request's last tokens."""
+    import paged_varlen_attention_amd as pa
+    from gpu_helpers import sample_rows
+    w = W.random_case(5150 + bs, num_seqs=3, min_q=1500, max_q=2000, max_ctx=300, num_q_heads=64,
+                      num_kv_heads=8, head_dim=256, block_size=bs, dtype=torch.bfloat16)
+    rows = sample_rows(w, 160, seed=bs)
+    ends = w.cu_seqlens_q[1:].tolist()
+    rows += [(t - 1, h) for t in ends for h in (0, 7, 63)]
+    ref = oracle.run_workload(w, rows=rows)
+    b = to_device(w)
+    for P in (0, 512):
+        parts = (pa.alloc_partials(w.total_q, 64, 256, pa.max_partitions(w.max_seq_len, P), "cuda")
+                 if P else None)
+        out = run_gpu(b, P, partials=parts, reduce=False)
+        assert pa.last_dispatch()["block"] == 512  # 8 waves
+        if P:
+            pa.split_kv_reduce(out, parts, b.cu_seqlens_q, b.seq_lens, P, sinks=b.sinks)
+        torch.cuda.synchronize()
+        got = torch.stack([out[t, h] for t, h in rows])
+        assert_close(got, ref, torch.bfloat16, f"wide long bs={bs} P={P}")
