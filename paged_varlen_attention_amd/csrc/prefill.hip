@@ -22,8 +22,8 @@
 //    the V^T A-operand fragments come from the row-major V tile through
 //    ds_read_b64_tr_b16 (gfx950's LDS transpose read), so V needs no transpose
 //    pass;
-//  * K and V tiles move HBM -> LDS by global_load_lds_dwordx4 with an XOR
-//    swizzle of the 16-byte pieces of each row (conflict-free fragment reads);
+//  * K and V tiles move HBM -> LDS by global_load_lds_dwordx4 into a
+//    swizzled piece-major layout (bank-conflict-free fragment reads);
 //    NST stages, one barrier per N-key tile;
 //  * requests are mapped to workgroups without a host pass: virtual tile x
 //    belongs to the last request r with cu[r]/BQ + r <= x (surplus tiles exit);
@@ -87,20 +87,28 @@ struct PrefillCfg {
 
 // Tile layout in LDS (K and V alike).  Keys come in groups of KG = 8; a
 // group stores piece-major: piece p (16 bytes: elements 8p..8p+7) of its 8
-// keys is one 128-byte line, and on odd pieces the key slot is XORed with 4:
-//   off(key, p) = (key / 8) * 8R + p * 128 + ((key % 8) ^ 4 (p & 1)) * 16.
+// keys is one 128-byte line.  Odd key groups store the two lines of each
+// piece pair swapped (stored piece s = p ^ (group & 1)), and the key slot is
+// XORed with 4 when bits 0 and 1 of s differ:
+//   off(key, p) = (key / 8) * 8R + s * 128 + ((key % 8) ^ 4 ((s ^ s / 2) & 1)) * 16.
+// The LDS serves 256 bytes (64 banks) a cycle, so every 16 lanes of a
+// ds_read_b128 and every 32 lanes of a ds_read_b64_tr_b16 must cover all
+// banks (the counters showed half of the LDS cycles lost to conflicts with
+// the plain piece-major layout; with this one there are none):
 // * S^T A operand (ds_read_b128): 8 consecutive lanes read 8 keys of one
-//   piece -- one line, all banks -- and a lane's address changes with the
-//   k-step only by an immediate.
-// * V^T A operand (ds_read_b64_tr_b16): a 16-lane group reads 4 keys x 2
-//   adjacent pieces; the XOR puts the two pieces on opposite 64-byte halves.
+//   piece -- one line -- and the next 8 lanes the same piece of the next key
+//   group, which the swap puts on the other half of the banks; the address
+//   changes with the k-step by an immediate (two bases, by k-step parity).
+// * V^T A operand (ds_read_b64_tr_b16): 32 lanes read 4 keys x 4 adjacent
+//   pieces; the slot XOR puts the four 64-byte runs on four bank quarters.
 // * DMA: one global_load_lds_dwordx4 fills 1 KB = 8 pieces of one key group
 //   with 128 contiguous bytes of each key row (one 8-key group never spans
-//   two pages since pages hold a multiple of 8 keys), and a lane's source
-//   offset inside the page is the same for every instruction.
+//   two pages since pages hold a multiple of 8 keys); a lane's source offset
+//   inside the page is one of two values (even or odd key group).
 template <class C>
 __device__ __forceinline__ int tile_off(int key, int piece) {
-    return (key >> 3) * C::GROUP_BYTES + piece * 128 + (((key & 7) ^ ((piece & 1) << 2)) << 4);
+    const int sp = piece ^ ((key >> 3) & 1);  // odd key groups swap the lines of a piece pair
+    return (key >> 3) * C::GROUP_BYTES + sp * 128 + (((key & 7) ^ (((sp ^ (sp >> 1)) & 1) << 2)) << 4);
 }
 
 // Wait until the DMA of the tile `ahead` tiles before the newest one landed.
@@ -248,7 +256,10 @@ __global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefil
     // brings piece 8*(c % IPG) + l/8 of key slot l%8 (its key is the slot
     // XORed back, which is the same involution).
     const uint32_t dma_voff =
-        (uint32_t)((lane & 7) ^ (((lane >> 3) & 1) << 2)) * row_stride + (uint32_t)(lane >> 3) * 16u;
+        (uint32_t)((lane & 7) ^ ((((lane >> 3) ^ (lane >> 4)) & 1) << 2)) * row_stride +
+        (uint32_t)(lane >> 3) * 16u;
+    // odd key groups: the line of stored piece 8q + l/8 holds piece 8q + (l/8 ^ 1)
+    const uint32_t dma_voff_odd = dma_voff + (uint32_t)((((lane >> 3) ^ 1) - (lane >> 3)) * 16);
     const uint32_t lds0 = lds_addr(lds);
 
     auto issue = [&](int kt, int stage) {
@@ -266,8 +277,9 @@ __global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefil
             const char *base = kc + (uint64_t)phys * page_bytes + head_off +
                                (uint32_t)(k8 & (bs - 1)) * row_stride + 128 * (c % C::IPG);
             const uint32_t l = lds0 + stage * C::STAGE + c * 1024;
-            dma16(base, dma_voff, l);
-            dma16(base + v_minus_k, dma_voff, l + C::T_BYTES);
+            const uint32_t vo = ((c / C::IPG) & 1) ? dma_voff_odd : dma_voff;
+            dma16(base, vo, l);
+            dma16(base + v_minus_k, vo, l + C::T_BYTES);
         }
     };
 
@@ -325,10 +337,18 @@ __global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefil
     // + 4*(s%4), i.e. piece 4db + 2*(group&1) + (s/2)%2, byte 8*(s%2).
     const int tg = lane >> 4;
     const int ts = lane & 15;
-    const int k_base = ((lane & 31) >> 3) * C::GROUP_BYTES + h * 128 + (((lane & 7) ^ (h << 2)) << 4);
+    const int kg = (lane & 31) >> 3;  // key group of the lane's key; odd ones swap line pairs
+    const int kp = h ^ (kg & 1);
+    // the key slot's XOR follows the parity of the stored piece's two low
+    // bits, which alternates with the k-step
+    const int k_base = kg * C::GROUP_BYTES + kp * 128 + (((lane & 7) ^ (kp << 2)) << 4);
+    const int k_base_odd = kg * C::GROUP_BYTES + kp * 128 + (((lane & 7) ^ ((kp ^ 1) << 2)) << 4);
     const int v_pb = (ts >> 1) & 1;
-    const int v_base = (2 * (tg & 1) + v_pb) * 128 + (((4 * h + (ts >> 2)) ^ (v_pb << 2)) << 4) +
-                       8 * (ts & 1);
+    const int v_base = (2 * (tg & 1) + v_pb) * 128 +
+                       (((4 * h + (ts >> 2)) ^ ((v_pb ^ (tg & 1)) << 2)) << 4) + 8 * (ts & 1);
+    // the same key slot in the odd key group (key + 8): its piece pair swapped
+    const int v_base_odd = C::GROUP_BYTES + (2 * (tg & 1) + (v_pb ^ 1)) * 128 +
+                           (((4 * h + (ts >> 2)) ^ ((v_pb ^ 1 ^ (tg & 1)) << 2)) << 4) + 8 * (ts & 1);
 
     const int ntiles = (k_hi - k_lo + C::N - 1) / C::N;
     constexpr int VM = 2 * C::NI_W;
@@ -417,8 +437,8 @@ __global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefil
         for (int b = 0; b < C::NB; ++b) {
             s[b] = f32x16_t{};
             auto kread = [&](int ks) {
-                return *reinterpret_cast<const uint4 *>(kst + k_base + b * 4 * C::GROUP_BYTES +
-                                                        ks * 256);
+                return *reinterpret_cast<const uint4 *>(kst + ((ks & 1) ? k_base_odd : k_base) +
+                                                        b * 4 * C::GROUP_BYTES + ks * 256);
             };
             uint4 ka[PF_K];
 #pragma unroll
@@ -478,7 +498,7 @@ __global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefil
                 const char *a = vst + v_base + (4 * b + 2 * (i / C::DB)) * C::GROUP_BYTES +
                                 (i % C::DB) * 512;
                 const s16x4_t lo = lds_read_tr16(a);
-                const s16x4_t hi = lds_read_tr16(a + C::GROUP_BYTES);
+                const s16x4_t hi = lds_read_tr16(a - v_base + v_base_odd);
                 const s16x4_t av[2] = {lo, hi};
                 return __builtin_bit_cast(bf16x8_t, av);
             };
