@@ -142,6 +142,11 @@ __device__ __forceinline__ void wait_tiles_ahead(int ahead) {
 #define PA_PREFILL_XCD_CHUNK 8
 #endif
 constexpr int XCD_CHUNK = PA_PREFILL_XCD_CHUNK;
+// Requests ordered by key count in the work order (launches of up to 64
+// requests).
+#ifndef PA_PREFILL_SORT
+#define PA_PREFILL_SORT 1
+#endif
 #ifndef PA_PREFILL_SCHED
 #define PA_PREFILL_SCHED 1
 #endif
@@ -175,18 +180,42 @@ __global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefil
     if (lam >= n_items) return;
     lam = n_items - 1 - lam;
     const int x = lam % p.grid_tiles;
-    int r;
-    {
+    int r, tile;
+    if (PA_PREFILL_SORT && p.num_seqs <= 64) {
+        // Up to 64 requests: the virtual tiles list the requests by key count,
+        // fewest first, each with exactly its own q-tiles, so that the
+        // last-first dispatch starts the requests with the most keys (and
+        // their longest q-tiles) first -- a decode row over a long context
+        // costs as much as a prompt's last q-tile and must not come last.
+        // Every wave computes the same table, one request per lane.
+        const int i = lane;
+        int ql = 0, sl = 0;
+        if (i < p.num_seqs) {
+            ql = p.cu_q[i + 1] - p.cu_q[i];
+            sl = p.seq_lens[i];
+        }
+        const int nt = ql > 0 ? (ql + BQ - 1) / BQ : 0;
+        int start = 0;
+        for (int j = 0; j < p.num_seqs; ++j) {
+            const int slj = __builtin_amdgcn_readlane(sl, j);
+            const int ntj = __builtin_amdgcn_readlane(nt, j);
+            start += (slj < sl || (slj == sl && j < i)) ? ntj : 0;
+        }
+        const uint64_t mine = __ballot(i < p.num_seqs && x >= start && x < start + nt);
+        if (!mine) return;  // surplus virtual tile
+        r = (int)__builtin_ctzll(mine);
+        tile = x - __builtin_amdgcn_readlane(start, r);
+    } else {
         int lo = 0, hi = p.num_seqs - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (p.cu_q[mid] / BQ + mid <= x) lo = mid; else hi = mid - 1;
         }
         r = lo;
+        tile = x - (p.cu_q[r] / BQ + r);
     }
     const int q_begin = p.cu_q[r];
     const int q_len = p.cu_q[r + 1] - q_begin;
-    const int tile = x - (q_begin / BQ + r);
     const int j0 = tile * BQ;  // first token of the tile within the request
     if (tile < 0 || j0 >= q_len) return;
     const int seq_len = p.seq_lens[r];
