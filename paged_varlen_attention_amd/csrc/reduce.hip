@@ -132,43 +132,68 @@ __global__ __launch_bounds__(256) void reduce_rows_kernel(const ReduceParams p) 
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // t * Hq + h
     if (row >= p.total_q * p.hq) return;
     const int t = row / p.hq;
-    int lo = 0, hi = p.num_seqs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (p.cu_q[mid] <= t) lo = mid; else hi = mid - 1;
+    // owner request of token t (the last r with cu[r] <= t) and its lengths:
+    // up to 64 requests in one round of loads, one request per lane
+    int q_len, pos;
+    if (p.num_seqs <= 64) {
+        const bool in = lane < p.num_seqs;
+        const int c0 = in ? p.cu_q[lane] : 0;
+        const int c1 = in ? p.cu_q[lane + 1] : 0;
+        const int sl = in ? p.seq_lens[lane] : 0;
+        const uint64_t le = __ballot(in && c0 <= t);
+        const int r = le ? 63 - __builtin_clzll(le) : 0;
+        const int cr = __builtin_amdgcn_readlane(c0, r);
+        q_len = __builtin_amdgcn_readlane(c1, r) - cr;
+        pos = __builtin_amdgcn_readlane(sl, r) - q_len + (t - cr);
+    } else {
+        int lo = 0, hi = p.num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.cu_q[mid] <= t) lo = mid; else hi = mid - 1;
+        }
+        q_len = p.cu_q[lo + 1] - p.cu_q[lo];
+        pos = p.seq_lens[lo] - q_len + (t - p.cu_q[lo]);
     }
-    const int q_len = p.cu_q[lo + 1] - p.cu_q[lo];
-    const int pos = p.seq_lens[lo] - q_len + (t - p.cu_q[lo]);
     const int n = pos / p.partition + 1;
-    if (n <= 1 || n > p.max_parts || pos < 0) return;
+    if (n <= 1 || n > p.max_parts || pos < 0 || n > ROWS_MAX_PARTS) return;
 
+    // statistics and every partial of the row requested together
     const size_t srow = (size_t)row * p.max_parts;
     const float m = lane < n ? p.max_logits[srow + lane] : NEG_INF;
+    const float es = lane < n ? p.exp_sums[srow + lane] : 0.f;
+    const float *o = p.tmp_out + srow * D + lane * E;
+    float v[ROWS_MAX_PARTS][E];
+#pragma unroll
+    for (int k = 0; k < ROWS_MAX_PARTS; ++k) {
+        if (k < n) {
+            if constexpr (E == 4) {
+                const float4 x = *reinterpret_cast<const float4 *>(o + (size_t)k * D);
+                v[k][0] = x.x; v[k][1] = x.y; v[k][2] = x.z; v[k][3] = x.w;
+            } else if constexpr (E == 2) {
+                const float2 x = *reinterpret_cast<const float2 *>(o + (size_t)k * D);
+                v[k][0] = x.x; v[k][1] = x.y;
+            } else {
+                v[k][0] = o[(size_t)k * D];
+            }
+        }
+    }
     // the head's sink joins the max and, once, the denominator (log2 units)
     const float s2 = p.sinks ? p.sinks[row % p.hq] * LOG2E_F : NEG_INF;
     const float M = fmaxf(group_max<64>(m), s2);
-    const float w = lane < n ? p.exp_sums[srow + lane] * exp2_diff(m, M) : 0.f;
+    const float w = lane < n ? es * exp2_diff(m, M) : 0.f;
     const float W = group_sum<64>(w) + exp2_diff(s2, M);
 
-    const float *o = p.tmp_out + srow * D + lane * E;
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    for (int k = 0; k < n; ++k) {
-        const float wk =
-            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
-        float v[E];
-        if constexpr (E == 4) {
-            const float4 x = *reinterpret_cast<const float4 *>(o + (size_t)k * D);
-            v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-        } else if constexpr (E == 2) {
-            const float2 x = *reinterpret_cast<const float2 *>(o + (size_t)k * D);
-            v[0] = x.x; v[1] = x.y;
-        } else {
-            v[0] = o[(size_t)k * D];
-        }
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = fmaf(wk, v[e], acc[e]);
+    for (int k = 0; k < ROWS_MAX_PARTS; ++k) {
+        if (k < n) {
+            const float wk = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] = fmaf(wk, v[k][e], acc[e]);
+        }
     }
     const float inv = 1.f / W;
     const size_t oi = (size_t)row * D + lane * E;
