@@ -22,8 +22,8 @@
 //  * grid = (kv_heads, requests, partitions), partitions last-first; NW waves
 //    take the 16-key chunks of the partition round-robin, each with a private
 //    ring of NST LDS stages, so no barrier is needed until the final merge;
-//  * K/V rows move HBM -> LDS with global_load_lds_dwordx4 into the tiled
-//    kernel's tile layout: keys in groups of 8, each 16-byte piece of the 8
+//  * K/V rows move HBM -> LDS with global_load_lds_dwordx4 into a
+//    piece-major layout: keys in groups of 8, each 16-byte piece of the 8
 //    keys one 128-byte line, the key slot XORed with 4 on odd pieces; one
 //    instruction fills 8 pieces of one key group, so a lane's source offset
 //    within the page is fixed and an instruction never spans two pages;
@@ -69,7 +69,7 @@ struct MfCfg {
     static constexpr int RPI = 64 * DW / R;      // rows per instruction (8-bit tiles)
     static constexpr int VM_PER_CHUNK = 2 * NI;  // K and V
     static constexpr int PPR = R / 16;           // 16-byte pieces per row
-    static constexpr int GROUP_BYTES = 8 * R;    // one 8-key group of the bf16 tile layout
+    static constexpr int GROUP_BYTES = 8 * R;    // one 8-key group of the bf16 layout
     static constexpr int IPG = PPR / 8;          // bf16: DMA instructions per key group (1 KB each)
     static constexpr int KS = D / 32;            // k-steps of S^T (16x16x32)
     static constexpr int DB = D / 16;            // 16-row blocks of O^T
@@ -90,7 +90,7 @@ struct MfCfg {
 };
 
 // Byte offset of piece p (elements 8p..8p+7) of key `key` in a tile whose rows
-// are R bytes: the layout of the tiled kernel (see the file comment).
+// are R bytes: the piece-major layout of the file comment.
 template <int R>
 __device__ __forceinline__ int mf_tile_off(int key, int piece) {
     return (key >> 3) * (8 * R) + piece * 128 + (((key & 7) ^ ((piece & 1) << 2)) << 4);
@@ -337,16 +337,6 @@ __device__ __forceinline__ void mf_chunk8(Frags8<C> &f, const bf16x8_t (&qb)[C::
     }
 }
 
-// Register staging: a chunk's fragments are read into registers as soon as
-// it lands, and its LDS stage is refilled right away, so NST + 1 chunks are in
-// flight while a wave computes instead of NST - 1.
-// Partition order in the grid: 1 = last partitions first, 0 = first first.
-#ifndef PA_MF_PART_ORDER
-#define PA_MF_PART_ORDER 1
-#endif
-#ifndef PA_MF_STAGE
-#define PA_MF_STAGE 1
-#endif
 // 8-bit caches on this kernel (else the vector-ALU decode kernel).
 #ifndef PA_MF_KV8
 #define PA_MF_KV8 1
@@ -358,7 +348,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const AttnParams p
     __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
 
     const int kvh = blockIdx.x;
-    const int part = PA_MF_PART_ORDER ? gridDim.z - 1 - blockIdx.z : blockIdx.z;
+    const int part = gridDim.z - 1 - blockIdx.z;
     const int r = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -483,7 +473,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const AttnParams p
     // area, then the other chunks ahead of the loop: the queries land with
     // chunk 0 and no compiler-counted load is outstanding once the chunk waits
     // start.
-    constexpr int PRE = PA_MF_STAGE ? NST : NST - 1;  // chunks issued ahead of the loop
+    constexpr int PRE = NST;  // chunks issued ahead of the loop
     bf16x8_t qb[C::KS];
     if (nmy > 0) {
         issue(0, 0);
@@ -537,20 +527,15 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const AttnParams p
             mf_read<C>(st + ka_off, st + va_off, f);
     };
 
-    // Land chunk k and read its fragments.  Without staging the stage it
-    // reads is refilled one step later; with staging right after the reads.
+    // Land chunk k and read its fragments into registers (register staging):
+    // its LDS stage is refilled right after the reads, so NST + 1 chunks are
+    // in flight while the wave computes instead of NST - 1.
     auto stage = [&](int k, F &f) {
-        if constexpr (PA_MF_STAGE) {
-            mf_wait_ahead<C::VM_PER_CHUNK, NST - 1>(min(NST - 1, nmy - 1 - k));
-            read(lds + (wave * NST + k % NST) * C::SLOT, f);
-            if (k + NST < nmy) {
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage k is read
-                issue(k + NST, k % NST);
-            }
-        } else {
-            if (k + NST - 1 < nmy) issue(k + NST - 1, (k + NST - 1) % NST);
-            mf_wait_ahead<C::VM_PER_CHUNK, NST - 1>(min(NST - 1, nmy - 1 - k));
-            read(lds + (wave * NST + k % NST) * C::SLOT, f);
+        mf_wait_ahead<C::VM_PER_CHUNK, NST - 1>(min(NST - 1, nmy - 1 - k));
+        read(lds + (wave * NST + k % NST) * C::SLOT, f);
+        if (k + NST < nmy) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage k is read
+            issue(k + NST, k % NST);
         }
     };
     auto step = [&](F &f, auto masked, int key0) {
