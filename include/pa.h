@@ -248,14 +248,21 @@ int32_t pa_pick_partition_size(const int32_t *host_seq_lens, int32_t num_seqs,
 /*
  * Dispatch record: what the calling thread's last pa_varlen_attention or
  * pa_split_kv_reduce call decided (the kernel walkthrough's dispatch layer,
- * made inspectable).  Environment switch, read at every call:
+ * made inspectable).  Environment switches, read at every call:
  *   PA_NO_SPLIT=1  pa_varlen_attention ignores partition_size (every row is
  *                  finished in place, partial buffers untouched) and
  *                  pa_split_kv_reduce does nothing.
+ *   PA_DECODE_ROWS=0|1|2  decode batches over bf16 caches: 0 keeps the
+ *                  per-KV-head decode kernel (grid = KV heads x requests x
+ *                  partitions); 2 takes the whole-row kernel (grid = requests
+ *                  x partitions, every KV head per workgroup) whenever the
+ *                  head shape allows it; 1 (default) takes it when the launch
+ *                  has at least 128 (request, partition) items.  Results agree
+ *                  within rounding either way.
  */
 enum {
     PA_PATH_NONE = 0,        /* rejected, or nothing to do (empty batch) */
-    PA_PATH_DECODE = 1,      /* VALU decode kernel, one workgroup per request */
+    PA_PATH_DECODE = 1,      /* decode kernels, one workgroup per request (and KV head) */
     PA_PATH_DECODE_TOKEN = 2,/* VALU decode kernel, one workgroup per query token */
     PA_PATH_TILED = 3,       /* bf16 MFMA tile kernel */
     PA_PATH_REDUCE_ROWS = 4, /* split-KV reduce, one wave per row */

@@ -725,6 +725,7 @@ bool decode_kv8_supported(int head_dim, int group) { return decode_supported(1, 
 
 hipError_t launch_decode(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
 #if PA_DECODE_MFMA
+    if (decode_rows_supported(p)) return launch_decode_rows(p, stream, li);
     if (decode_mfma_supported(p)) return launch_decode_mfma(p, stream, li);
 #endif
     if (p.kv8) return p.dtype == 1 ? launch_dt<bf16_t, true>(p, stream, li) : hipErrorInvalidValue;

@@ -139,21 +139,6 @@ __device__ __forceinline__ void mf_wait_ahead(int ahead) {
     }
 }
 
-// Max and sum over the 4 lane groups (16-lane rows) of the wave: lanes
-// c, c+16, c+32, c+48 hold the same head.
-__device__ __forceinline__ float rows_max(float x) {
-    const RowPair a = row_pair16(x);
-    x = fmaxf(a.a, a.b);
-    const RowPair b = row_pair32(x);
-    return fmaxf(b.a, b.b);
-}
-__device__ __forceinline__ float rows_sum(float x) {
-    const RowPair a = row_pair16(x);
-    x = a.a + a.b;
-    const RowPair b = row_pair32(x);
-    return b.a + b.b;
-}
-
 // A chunk's MFMA fragments: K rows (A operand of S^T) and V^T (A operand of O^T).
 template <class C>
 struct Frags {

@@ -108,6 +108,22 @@ __device__ __forceinline__ RowPair row_pair32(float x) {
     return {__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
+// Max and sum over the 4 lane groups (16-lane rows) of the wave: lanes c,
+// c+16, c+32 and c+48 (one column of a 16x16 MFMA accumulator) get the same
+// result.
+__device__ __forceinline__ float rows_max(float x) {
+    const RowPair a = row_pair16(x);
+    x = fmaxf(a.a, a.b);
+    const RowPair b = row_pair32(x);
+    return fmaxf(b.a, b.b);
+}
+__device__ __forceinline__ float rows_sum(float x) {
+    const RowPair a = row_pair16(x);
+    x = a.a + a.b;
+    const RowPair b = row_pair32(x);
+    return b.a + b.b;
+}
+
 // ---- direct global -> LDS loads (gfx950 global_load_lds_dwordx4) ---------
 //
 // Each active lane copies 16 bytes from (sbase + voff) to LDS address
