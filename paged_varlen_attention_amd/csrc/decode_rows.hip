@@ -36,8 +36,11 @@
 //    fragment read (one piece of 16 block rows) cover all 64 banks, and it
 //    maps rows 0..7 (and 8..15) to distinct halves sigma/2, so the 32 lanes of
 //    a V^T transpose read (pieces 2b and 2b+1 of 8 rows) cover them too;
-//  * the waves' states are merged in LDS at the end, as in the per-head
-//    kernel, for all Hq query heads at once.
+//  * the waves' states meet in LDS in the accumulator layout: every wave
+//    holds the same (head, dim) at the same lane and register, so each lane
+//    merges one float4 position of all waves and stores 4 consecutive dims
+//    (one workgroup per CU leaves no other workgroup to hide this epilogue, so
+//    it is kept to a few vector LDS reads per lane).
 #include <cstdlib>
 #include <type_traits>
 
@@ -65,8 +68,8 @@ struct RowCfg {
     static constexpr int QHMAX = 16 * NB;  // most query heads (HPB x group <= 16 per block)
     static constexpr int RING = NW * NST * SLOT;
     static constexpr int QBYTES = QHMAX * 2 * D;
-    static constexpr int STATE_FLOATS = QHMAX * D + 2 * QHMAX;
-    static constexpr int MERGE = NW * STATE_FLOATS * 4;
+    static constexpr int MERGE_O = NW * NB * DB * 64 * 16;  // the waves' O^T accumulators
+    static constexpr int MERGE = MERGE_O + 2 * NW * NB * 16 * 4;  // + max and exp-sum per column
     static constexpr int LDS_BYTES = RING + QBYTES > MERGE ? RING + QBYTES : MERGE;
     static_assert(KPB >= 2 && KPB <= 8 && NB >= 1 && NB <= 2, "block shape");
     static_assert(D >= 128, "pieces per head row >= 16 (the swizzle XORs 4 bits)");
@@ -346,54 +349,65 @@ __global__ __launch_bounds__(NW * 64) void decode_rows_kernel(const AttnParams p
             for (int e = 0; e < 4; ++e) o[X][b][e] *= f;
     }
 
-    // ---- one state per wave to LDS, then all threads merge the waves ----
+    // ---- the waves' states to LDS in the accumulator layout (conflict-free:
+    // a lane's float4 at lane-consecutive addresses), then wave w finishes the
+    // 16-dim tiles j = w, w + NW, .. of the NB x DB: every lane merges the same
+    // register position of all waves and stores 4 consecutive dims ----
     __syncthreads();  // every wave is done with its stages and the query area
-    float *mrg = reinterpret_cast<float *>(lds);
-    if (col < ncol) {
-        float *st = mrg + wave * C::STATE_FLOATS;
+    f32x4_t *mo = reinterpret_cast<f32x4_t *>(lds);
+    float *mm = reinterpret_cast<float *>(lds + C::MERGE_O);  // [wave][block][column]
+    float *ml = mm + NW * NB * 16;
 #pragma unroll
-        for (int X = 0; X < NB; ++X) {
-            const int qh = X * ncol + col;
+    for (int X = 0; X < NB; ++X) {
 #pragma unroll
-            for (int b = 0; b < C::DB; ++b)
-                *reinterpret_cast<f32x4_t *>(st + qh * D + 16 * b + 4 * grp) = o[X][b];
-            if (grp == 0) {
-                st[C::QHMAX * D + qh] = mtrue[X];
-                st[C::QHMAX * D + C::QHMAX + qh] = l[X];
-            }
+        for (int b = 0; b < C::DB; ++b) mo[((wave * NB + X) * C::DB + b) * 64 + lane] = o[X][b];
+        if (grp == 0) {
+            mm[(wave * NB + X) * 16 + col] = mtrue[X];
+            ml[(wave * NB + X) * 16 + col] = l[X];
         }
     }
     __syncthreads();
 
     const bool direct = nparts <= 1;
-    for (int idx = threadIdx.x; idx < QH * D; idx += NW * 64) {
-        const int h = idx / D;
-        const int d = idx - h * D;
+    for (int j = wave; j < NB * C::DB; j += NW) {
+        const int X = j / C::DB;
+        const int b = j - X * C::DB;
+        float mw[NW];
         float M = NEG_INF;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, mrg[w * C::STATE_FLOATS + C::QHMAX * D + h]);
-        float num = 0.f, den = 0.f;
+        for (int w = 0; w < NW; ++w) {
+            mw[w] = mm[(w * NB + X) * 16 + col];
+            M = fmaxf(M, mw[w]);
+        }
+        f32x4_t num = {0.f, 0.f, 0.f, 0.f};
+        float den = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            const float *st = mrg + w * C::STATE_FLOATS;
-            const float f = exp2_diff(st[C::QHMAX * D + h], M);
-            num += st[h * D + d] * f;
-            den += st[C::QHMAX * D + C::QHMAX + h] * f;
+            const float f = exp2_diff(mw[w], M);
+            num += mo[((w * NB + X) * C::DB + b) * 64 + lane] * f;
+            den += ml[(w * NB + X) * 16 + col] * f;
         }
-        float o_ = num / den;
-        if (direct && p.sinks) {
-            // the head's sink: one more denominator term, no value (log2 units)
-            const float s2 = p.sinks[h] * LOG2E_F;
-            const float Mx = fmaxf(M, s2);
-            const float a = exp2_diff(M, Mx);
-            o_ = num * a / (den * a + exp2_diff(s2, Mx));
-        }
+        if (col >= ncol) continue;
+        const int h = X * ncol + col;
+        const int d0 = 16 * b + 4 * grp;
         if (direct) {
-            reinterpret_cast<uint16_t *>(p.out)[((size_t)q0 * p.hq + h) * D + d] = to_bf16(o_);
+            float inv = 1.f / den;
+            if (p.sinks) {
+                // the head's sink: one more denominator term, no value (log2 units)
+                const float s2 = p.sinks[h] * LOG2E_F;
+                const float Mx = fmaxf(M, s2);
+                const float a = exp2_diff(M, Mx);
+                inv = a / (den * a + exp2_diff(s2, Mx));
+            }
+            *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.out) +
+                                       ((size_t)q0 * p.hq + h) * D + d0) =
+                make_uint2(pack_bf16(num[0] * inv, num[1] * inv), pack_bf16(num[2] * inv, num[3] * inv));
         } else {
             const size_t si = ((size_t)q0 * p.hq + h) * p.max_parts + part;
-            p.tmp_out[si * D + d] = o_;
-            if (d == 0) {
+            const float inv = 1.f / den;
+            *reinterpret_cast<f32x4_t *>(p.tmp_out + si * D + d0) =
+                f32x4_t{num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv};
+            if (b == 0 && grp == 0) {
                 p.max_logits[si] = M;
                 p.exp_sums[si] = den;
             }
