@@ -24,23 +24,18 @@
 namespace pa {
 namespace {
 
-// Grid (token, piece block): no division for the token index, and the
-// slot and the row's data are requested together (one memory round trip
-// before the stores instead of two).
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const uint4 *__restrict__ key, const uint4 *__restrict__ value, uint4 *__restrict__ kc,
-    uint4 *__restrict__ vc, const int64_t *__restrict__ slots, int32_t pieces_per_row,
-    int64_t num_slots) {
-    const int64_t t = blockIdx.x;
-    const int32_t c = (int32_t)(blockIdx.y * blockDim.x + threadIdx.x);
-    if (c >= pieces_per_row) return;
+    uint4 *__restrict__ vc, const int64_t *__restrict__ slots, int32_t num_tokens,
+    int32_t pieces_per_row, int64_t num_slots) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t t = i / pieces_per_row;
+    const int32_t c = (int32_t)(i - t * pieces_per_row);
+    if (t >= num_tokens) return;
     const int64_t s = slots[t];
+    if (s < 0 || s >= num_slots) return;
     const uint4 k = key[t * pieces_per_row + c];
     const uint4 v = value[t * pieces_per_row + c];
-    // keep the row loads above the slot test (the compiler would sink them
-    // into its branch, after the slot's round trip)
-    asm volatile("" ::"v"(k.x), "v"(k.y), "v"(k.z), "v"(k.w), "v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
-    if (s < 0 || s >= num_slots) return;
     kc[s * pieces_per_row + c] = k;
     vc[s * pieces_per_row + c] = v;
 }
@@ -107,22 +102,18 @@ template <bool F32>
 __global__ __launch_bounds__(256) void quantize_cache_kernel(
     const char *__restrict__ key, const char *__restrict__ value, uint4 *__restrict__ kc,
     uint4 *__restrict__ vc, const int64_t *__restrict__ slots, const float *__restrict__ k_scale,
-    const float *__restrict__ v_scale, int32_t pieces_per_row, int32_t head_dim,
-    int64_t num_slots) {
-    const int64_t t = blockIdx.x;  // grid (token, piece block), as above
-    const int32_t c = (int32_t)(blockIdx.y * blockDim.x + threadIdx.x);
-    if (c >= pieces_per_row) return;
+    const float *__restrict__ v_scale, int32_t num_tokens, int32_t pieces_per_row,
+    int32_t head_dim, int64_t num_slots) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t t = i / pieces_per_row;
+    const int32_t c = (int32_t)(i - t * pieces_per_row);
+    if (t >= num_tokens) return;
     const int64_t s = slots[t];
+    if (s < 0 || s >= num_slots) return;
     const int32_t h = (c * 16) / head_dim;  // 16 elements never straddle two heads
     const size_t src = ((size_t)t * pieces_per_row + c) * 16 * (F32 ? 4 : 2);
-    const uint4 qk = quantize16<F32>(key + src, k_scale[h]);
-    const uint4 qv = quantize16<F32>(value + src, v_scale[h]);
-    // the loads stay above the slot test
-    asm volatile("" ::"v"(qk.x), "v"(qk.y), "v"(qk.z), "v"(qk.w), "v"(qv.x), "v"(qv.y), "v"(qv.z),
-                 "v"(qv.w));
-    if (s < 0 || s >= num_slots) return;
-    kc[s * pieces_per_row + c] = qk;
-    vc[s * pieces_per_row + c] = qv;
+    kc[s * pieces_per_row + c] = quantize16<F32>(key + src, k_scale[h]);
+    vc[s * pieces_per_row + c] = quantize16<F32>(value + src, v_scale[h]);
 }
 
 __global__ __launch_bounds__(256) void expand_block_tables_kernel(
@@ -143,11 +134,12 @@ hipError_t launch_reshape_and_cache(const void *key, const void *value, void *kc
                                     int64_t num_slots, hipStream_t stream) {
     if (num_tokens == 0) return hipSuccess;
     const int32_t ppr = row_bytes / 16;
-    const int32_t tb = ppr >= 256 ? 256 : (ppr + 63) / 64 * 64;
-    hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)num_tokens, (ppr + tb - 1) / tb),
-                       dim3(tb), 0, stream, reinterpret_cast<const uint4 *>(key),
-                       reinterpret_cast<const uint4 *>(value), reinterpret_cast<uint4 *>(kc),
-                       reinterpret_cast<uint4 *>(vc), slots, ppr, num_slots);
+    const int64_t total = (int64_t)num_tokens * ppr;
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(reshape_and_cache_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const uint4 *>(key), reinterpret_cast<const uint4 *>(value),
+                       reinterpret_cast<uint4 *>(kc), reinterpret_cast<uint4 *>(vc), slots,
+                       num_tokens, ppr, num_slots);
     return hipGetLastError();
 }
 
@@ -158,12 +150,13 @@ hipError_t launch_quantize_cache(const void *key, const void *value, void *kc, v
                                  hipStream_t stream) {
     if (num_tokens == 0) return hipSuccess;
     const int32_t ppr = row_elems / 16;
-    const int32_t tb = ppr >= 256 ? 256 : (ppr + 63) / 64 * 64;
+    const int64_t total = (int64_t)num_tokens * ppr;
+    const int64_t blocks = (total + 255) / 256;
     auto kernel = in_f32 ? quantize_cache_kernel<true> : quantize_cache_kernel<false>;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)num_tokens, (ppr + tb - 1) / tb), dim3(tb), 0, stream,
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const char *>(key), static_cast<const char *>(value),
                        static_cast<uint4 *>(kc), static_cast<uint4 *>(vc), slots, k_scale, v_scale,
-                       ppr, head_dim, num_slots);
+                       num_tokens, ppr, head_dim, num_slots);
     return hipGetLastError();
 }
 
