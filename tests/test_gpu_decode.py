@@ -42,8 +42,11 @@ def test_decode_geometries(hq, hkv, d, bs, dtype):
         assert_close(out, ref, dtype, f"P={P}")
 
 
-def test_gqa_decode_batch_split512():
-    """32 requests, ctx U[512,4096], 32/8/128 bf16, split 512 + reduce; every row."""
+@pytest.mark.parametrize("form", ["1", "0"], ids=["auto-whole-row", "per-head"])
+def test_gqa_decode_batch_split512(form, monkeypatch):
+    """32 requests, ctx U[512,4096], 32/8/128 bf16, split 512 + reduce; every row;
+    the launch bench.py times (whole-row kernel) and the per-KV-head kernel."""
+    monkeypatch.setenv("PA_DECODE_ROWS", form)
     w = W.gqa_decode_bf16()
     ref = oracle.run_workload(w)
     b = to_device(w)
@@ -65,9 +68,12 @@ def test_long_context_decode(P):
     assert_close(out, ref, torch.bfloat16, f"long decode P={P}")
 
 
-def test_split_partials_match_oracle():
-    """The partials themselves (log2-space max, exp-sum, normalised output)."""
+@pytest.mark.parametrize("form", ["0", "2"], ids=["per-head", "whole-row"])
+def test_split_partials_match_oracle(form, monkeypatch):
+    """The partials themselves (log2-space max, exp-sum, normalised output),
+    from both bf16 decode kernels."""
     import paged_varlen_attention_amd as pa
+    monkeypatch.setenv("PA_DECODE_ROWS", form)
     w = W.random_case(77, num_seqs=4, max_q=1, max_ctx=1500, num_q_heads=16, num_kv_heads=2,
                       head_dim=128, block_size=16, dtype=torch.bfloat16)
     P = 256
