@@ -33,9 +33,11 @@
 //  * LDS row layout: the 16-byte pieces of row (t, head) are XORed with
 //    sigma(i) = (2i mod 16) | (i / 8), i = (head mod HPB) KPB + t its row in
 //    the block.  sigma is a bijection on 0..15, so the 16 lanes of a K
-//    fragment read (one piece of 16 block rows) cover all 64 banks, and it
-//    maps rows 0..7 (and 8..15) to distinct halves sigma/2, so the 32 lanes of
-//    a V^T transpose read (pieces 2b and 2b+1 of 8 rows) cover them too;
+//    fragment read (one piece of 16 block rows) reach 16 distinct 16-byte
+//    slots, and it maps rows 0..7 (and 8..15) to distinct halves sigma/2, so
+//    the 32 lanes of a V^T transpose read (pieces 2b and 2b+1 of 8 rows)
+//    cover all banks (counted: no conflicts; the K reads still show about one
+//    extra cycle each, which does not limit this memory-bound kernel);
 //  * the waves' states meet in LDS in the accumulator layout: every wave
 //    holds the same (head, dim) at the same lane and register, so each lane
 //    merges one float4 position of all waves and stores 4 consecutive dims
