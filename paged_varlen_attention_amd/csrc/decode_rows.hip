@@ -70,9 +70,9 @@ struct RowCfg {
     static constexpr int QHMAX = 16 * NB;  // most query heads (HPB x group <= 16 per block)
     static constexpr int RING = NW * NST * SLOT;
     static constexpr int QBYTES = QHMAX * 2 * D;
-    static constexpr int MERGE_O = NW * NB * DB * 64 * 16;  // the waves' O^T accumulators
-    static constexpr int MERGE = MERGE_O + 2 * NW * NB * 16 * 4;  // + max and exp-sum per column
-    static constexpr int LDS_BYTES = RING + QBYTES > MERGE ? RING + QBYTES : MERGE;
+    static constexpr int LDS_BYTES = RING + QBYTES;
+    // a wave's state (O^T accumulators, max and exp-sum per column) fits its ring
+    static_assert(NB * DB * 1024 + 2 * NB * 16 * 4 <= NST * SLOT, "state in the ring");
     static_assert(KPB >= 2 && KPB <= 8 && NB >= 1 && NB <= 2, "block shape");
     static_assert(D >= 128, "pieces per head row >= 16 (the swizzle XORs 4 bits)");
     static_assert(TILE % 1024 == 0 && VM < 64, "DMA shape");
@@ -351,21 +351,29 @@ __global__ __launch_bounds__(NW * 64) void decode_rows_kernel(const AttnParams p
             for (int e = 0; e < 4; ++e) o[X][b][e] *= f;
     }
 
-    // ---- the waves' states to LDS in the accumulator layout (conflict-free:
-    // a lane's float4 at lane-consecutive addresses), then wave w finishes the
-    // 16-dim tiles j = w, w + NW, .. of the NB x DB: every lane merges the same
-    // register position of all waves and stores 4 consecutive dims ----
-    __syncthreads();  // every wave is done with its stages and the query area
-    f32x4_t *mo = reinterpret_cast<f32x4_t *>(lds);
-    float *mm = reinterpret_cast<float *>(lds + C::MERGE_O);  // [wave][block][column]
-    float *ml = mm + NW * NB * 16;
+    // ---- each wave parks its state in its own ring (its DMA has landed and
+    // its reads are done, so no barrier is needed first) in the accumulator
+    // layout (a lane's float4 at lane-consecutive addresses); after one
+    // barrier wave w finishes the 16-dim tiles j = w, w + NW, .. of the
+    // NB x DB: every lane merges the same register position of all waves and
+    // stores 4 consecutive dims ----
+    auto ring_o = [&](int w) {
+        return reinterpret_cast<f32x4_t *>(lds + w * NST * C::SLOT);
+    };
+    auto ring_m = [&](int w) {  // [block][column] max, then exp-sum
+        return reinterpret_cast<float *>(lds + w * NST * C::SLOT + NB * C::DB * 1024);
+    };
+    {
+        f32x4_t *mo = ring_o(wave);
+        float *mm = ring_m(wave);
 #pragma unroll
-    for (int X = 0; X < NB; ++X) {
+        for (int X = 0; X < NB; ++X) {
 #pragma unroll
-        for (int b = 0; b < C::DB; ++b) mo[((wave * NB + X) * C::DB + b) * 64 + lane] = o[X][b];
-        if (grp == 0) {
-            mm[(wave * NB + X) * 16 + col] = mtrue[X];
-            ml[(wave * NB + X) * 16 + col] = l[X];
+            for (int b = 0; b < C::DB; ++b) mo[(X * C::DB + b) * 64 + lane] = o[X][b];
+            if (grp == 0) {
+                mm[X * 16 + col] = mtrue[X];
+                mm[NB * 16 + X * 16 + col] = l[X];
+            }
         }
     }
     __syncthreads();
@@ -378,7 +386,7 @@ __global__ __launch_bounds__(NW * 64) void decode_rows_kernel(const AttnParams p
         float M = NEG_INF;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            mw[w] = mm[(w * NB + X) * 16 + col];
+            mw[w] = ring_m(w)[X * 16 + col];
             M = fmaxf(M, mw[w]);
         }
         f32x4_t num = {0.f, 0.f, 0.f, 0.f};
@@ -386,8 +394,8 @@ __global__ __launch_bounds__(NW * 64) void decode_rows_kernel(const AttnParams p
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             const float f = exp2_diff(mw[w], M);
-            num += mo[((w * NB + X) * C::DB + b) * 64 + lane] * f;
-            den += ml[(w * NB + X) * 16 + col] * f;
+            num += ring_o(w)[(X * C::DB + b) * 64 + lane] * f;
+            den += ring_m(w)[NB * 16 + X * 16 + col] * f;
         }
         if (col >= ncol) continue;
         const int h = X * ncol + col;
