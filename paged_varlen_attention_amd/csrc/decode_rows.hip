@@ -70,7 +70,7 @@ struct RowCfg {
     static constexpr int QHMAX = 16 * NB;  // most query heads (HPB x group <= 16 per block)
     static constexpr int RING = NW * NST * SLOT;
     static constexpr int QBYTES = QHMAX * 2 * D;
-    static constexpr int LDS_BYTES = RING + QBYTES;
+    static constexpr int LDS_BYTES = RING + NW * QBYTES;  // a query area per wave
     // a wave's state (O^T accumulators, max and exp-sum per column) fits its ring
     static_assert(NB * DB * 1024 + 2 * NB * 16 * 4 <= NST * SLOT, "state in the ring");
     static_assert(KPB >= 2 && KPB <= 8 && NB >= 1 && NB <= 2, "block shape");
@@ -158,17 +158,18 @@ __global__ __launch_bounds__(NW * 64) void decode_rows_kernel(const AttnParams p
             dma_lds<16>(kc + off + v_minus_k, voff[n], ldsk + C::TILE + n * 1024);
     };
 
-    // Chunk 0, then this wave's share of the request's query rows (all heads,
-    // QH x 2D contiguous bytes) into the shared query area, then the other
-    // ring stage; after the waits and a barrier every wave reads its Q^T.
-    const uint32_t lds_q = lds_addr(lds) + (uint32_t)C::RING;
+    // Chunk 0, then the request's query rows (all heads, QH x 2D contiguous
+    // bytes) into this wave's own query area, then the other ring stage; the
+    // wave reads its Q^T once its own DMA has landed (no barrier: the waves
+    // start their streams independently).
+    const int q_area = C::RING + wave * C::QBYTES;
     if (nmy > 0) issue(0, 0);
     {
         const char *qg = reinterpret_cast<const char *>(p.q) + (size_t)q0 * p.hq * (2 * D);
         const int qbytes = QH * 2 * D;
-        for (int j = wave; j * 1024 < qbytes; j += NW) {
+        for (int j = 0; j * 1024 < qbytes; ++j) {
             const uint32_t off = (uint32_t)(j * 1024 + lane * 16);
-            dma_lds<16>(qg, off < (uint32_t)qbytes ? off : 0u, lds_q + j * 1024);
+            dma_lds<16>(qg, off < (uint32_t)qbytes ? off : 0u, lds_addr(lds) + q_area + j * 1024);
         }
     }
     if (NST > 1 && nmy > 1) issue(1, 1);
@@ -176,7 +177,6 @@ __global__ __launch_bounds__(NW * 64) void decode_rows_kernel(const AttnParams p
         wait_vmcnt<C::VM>();
     else
         wait_vmcnt<0>();
-    __syncthreads();
 
     // Q^T of block X (B operand of S^T): column `col` is query head
     // X HPB G + col (zero past the block's HPB G heads), dims 32 ks + 8 grp ..
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(NW * 64) void decode_rows_kernel(const AttnParams p
     const int ncol = HPB * G;
 #pragma unroll
     for (int X = 0; X < NB; ++X) {
-        const char *qrow = lds + C::RING + (X * ncol + col) * (2 * D) + 16 * grp;
+        const char *qrow = lds + q_area + (X * ncol + col) * (2 * D) + 16 * grp;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
             if (col < ncol) {
