@@ -13,7 +13,9 @@
 // quantisation kernels without giving one) stores each element of KV head g
 // as the E4M3 code of the correctly rounded float32 quotient x / scale[g]:
 // nearest code, ties to an even mantissa, saturating at 448, NaN to 0x7F.
-// Each thread turns 16 elements of one head into one 16-byte store.
+// Each thread turns 4 elements of one head into one 4-byte store: the
+// correctly rounded divisions dominate the kernel, so they are spread over
+// four times the threads of a 16-byte-per-thread form.
 //
 // expand_block_tables (unified-memory article, section six) rewrites a table of
 // large cache blocks into the equivalent table of kernel pages: block b of
@@ -59,61 +61,44 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
     return sign | (r - (120u << 3));
 }
 
+// Four consecutive elements (bf16 or float32) as floats.
 template <bool F32>
-__device__ __forceinline__ void load16(const void *src, float (&f)[16]) {
+__device__ __forceinline__ void load4(const void *src, float (&f)[4]) {
     if constexpr (F32) {
-        const float4 *p = reinterpret_cast<const float4 *>(src);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float4 v = p[j];
-            f[4 * j] = v.x; f[4 * j + 1] = v.y; f[4 * j + 2] = v.z; f[4 * j + 3] = v.w;
-        }
+        const float4 v = *reinterpret_cast<const float4 *>(src);
+        f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
     } else {
-        const uint4 *p = reinterpret_cast<const uint4 *>(src);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint4 v = p[j];
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                f[8 * j + 2 * k] = bf16lo(w[k]);
-                f[8 * j + 2 * k + 1] = bf16hi(w[k]);
-            }
-        }
+        const uint2 v = *reinterpret_cast<const uint2 *>(src);
+        f[0] = bf16lo(v.x); f[1] = bf16hi(v.x); f[2] = bf16lo(v.y); f[3] = bf16hi(v.y);
     }
 }
 
 template <bool F32>
-__device__ __forceinline__ uint4 quantize16(const void *src, float scale) {
-    float f[16];
-    load16<F32>(src, f);
-    uint32_t w[4];
+__device__ __forceinline__ uint32_t quantize4(const void *src, float scale) {
+    float f[4];
+    load4<F32>(src, f);
+    uint32_t x = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        uint32_t x = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) x |= e4m3_code(f[4 * j + k] / scale) << (8 * k);
-        w[j] = x;
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
+    for (int k = 0; k < 4; ++k) x |= e4m3_code(f[k] / scale) << (8 * k);
+    return x;
 }
 
 template <bool F32>
 __global__ __launch_bounds__(256) void quantize_cache_kernel(
-    const char *__restrict__ key, const char *__restrict__ value, uint4 *__restrict__ kc,
-    uint4 *__restrict__ vc, const int64_t *__restrict__ slots, const float *__restrict__ k_scale,
-    const float *__restrict__ v_scale, int32_t num_tokens, int32_t pieces_per_row,
+    const char *__restrict__ key, const char *__restrict__ value, uint32_t *__restrict__ kc,
+    uint32_t *__restrict__ vc, const int64_t *__restrict__ slots, const float *__restrict__ k_scale,
+    const float *__restrict__ v_scale, int32_t num_tokens, int32_t quads_per_row,
     int32_t head_dim, int64_t num_slots) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t t = i / pieces_per_row;
-    const int32_t c = (int32_t)(i - t * pieces_per_row);
+    const int64_t t = i / quads_per_row;
+    const int32_t c = (int32_t)(i - t * quads_per_row);
     if (t >= num_tokens) return;
     const int64_t s = slots[t];
     if (s < 0 || s >= num_slots) return;
-    const int32_t h = (c * 16) / head_dim;  // 16 elements never straddle two heads
-    const size_t src = ((size_t)t * pieces_per_row + c) * 16 * (F32 ? 4 : 2);
-    kc[s * pieces_per_row + c] = quantize16<F32>(key + src, k_scale[h]);
-    vc[s * pieces_per_row + c] = quantize16<F32>(value + src, v_scale[h]);
+    const int32_t h = (c * 4) / head_dim;  // 4 elements never straddle two heads
+    const size_t src = ((size_t)t * quads_per_row + c) * 4 * (F32 ? 4 : 2);
+    kc[s * quads_per_row + c] = quantize4<F32>(key + src, k_scale[h]);
+    vc[s * quads_per_row + c] = quantize4<F32>(value + src, v_scale[h]);
 }
 
 __global__ __launch_bounds__(256) void expand_block_tables_kernel(
@@ -149,14 +134,14 @@ hipError_t launch_quantize_cache(const void *key, const void *value, void *kc, v
                                  int32_t head_dim, int64_t num_slots, bool in_f32,
                                  hipStream_t stream) {
     if (num_tokens == 0) return hipSuccess;
-    const int32_t ppr = row_elems / 16;
-    const int64_t total = (int64_t)num_tokens * ppr;
+    const int32_t qpr = row_elems / 4;
+    const int64_t total = (int64_t)num_tokens * qpr;
     const int64_t blocks = (total + 255) / 256;
     auto kernel = in_f32 ? quantize_cache_kernel<true> : quantize_cache_kernel<false>;
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const char *>(key), static_cast<const char *>(value),
-                       static_cast<uint4 *>(kc), static_cast<uint4 *>(vc), slots, k_scale, v_scale,
-                       num_tokens, ppr, head_dim, num_slots);
+                       static_cast<uint32_t *>(kc), static_cast<uint32_t *>(vc), slots, k_scale,
+                       v_scale, num_tokens, qpr, head_dim, num_slots);
     return hipGetLastError();
 }
 
