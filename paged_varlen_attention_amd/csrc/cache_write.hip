@@ -13,9 +13,10 @@
 // quantisation kernels without giving one) stores each element of KV head g
 // as the E4M3 code of the correctly rounded float32 quotient x / scale[g]:
 // nearest code, ties to an even mantissa, saturating at 448, NaN to 0x7F.
-// Each thread turns 4 elements of one head into one 4-byte store: the
-// correctly rounded divisions dominate the kernel, so they are spread over
-// four times the threads of a 16-byte-per-thread form.
+// Each thread turns EPT elements of one head into one EPT-byte store: 16 for
+// large writes (16-byte loads and stores), 4 for smaller ones (decode and
+// mixed batches), whose time is the latency of the correctly rounded
+// divisions, which four times the threads then share.
 //
 // expand_block_tables (unified-memory article, section six) rewrites a table of
 // large cache blocks into the equivalent table of kernel pages: block b of
@@ -61,44 +62,77 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
     return sign | (r - (120u << 3));
 }
 
-// Four consecutive elements (bf16 or float32) as floats.
-template <bool F32>
-__device__ __forceinline__ void load4(const void *src, float (&f)[4]) {
+// N consecutive elements (bf16 or float32) as floats.
+template <bool F32, int N>
+__device__ __forceinline__ void load_n(const void *src, float (&f)[N]) {
     if constexpr (F32) {
-        const float4 v = *reinterpret_cast<const float4 *>(src);
-        f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
-    } else {
+#pragma unroll
+        for (int j = 0; j < N / 4; ++j) {
+            const float4 v = reinterpret_cast<const float4 *>(src)[j];
+            f[4 * j] = v.x; f[4 * j + 1] = v.y; f[4 * j + 2] = v.z; f[4 * j + 3] = v.w;
+        }
+    } else if constexpr (N == 4) {
         const uint2 v = *reinterpret_cast<const uint2 *>(src);
         f[0] = bf16lo(v.x); f[1] = bf16hi(v.x); f[2] = bf16lo(v.y); f[3] = bf16hi(v.y);
+    } else {
+#pragma unroll
+        for (int j = 0; j < N / 8; ++j) {
+            const uint4 v = reinterpret_cast<const uint4 *>(src)[j];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                f[8 * j + 2 * k] = bf16lo(w[k]);
+                f[8 * j + 2 * k + 1] = bf16hi(w[k]);
+            }
+        }
     }
 }
 
-template <bool F32>
-__device__ __forceinline__ uint32_t quantize4(const void *src, float scale) {
-    float f[4];
-    load4<F32>(src, f);
-    uint32_t x = 0;
+// EPT codes packed little-endian into EPT / 4 words.
+template <bool F32, int EPT>
+struct Codes {
+    uint32_t w[EPT / 4];
+};
+template <bool F32, int EPT>
+__device__ __forceinline__ Codes<F32, EPT> quantize_n(const void *src, float scale) {
+    float f[EPT];
+    load_n<F32, EPT>(src, f);
+    Codes<F32, EPT> c;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) x |= e4m3_code(f[k] / scale) << (8 * k);
-    return x;
+    for (int j = 0; j < EPT / 4; ++j) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x |= e4m3_code(f[4 * j + k] / scale) << (8 * k);
+        c.w[j] = x;
+    }
+    return c;
 }
 
-template <bool F32>
+template <bool F32, int EPT>
+__device__ __forceinline__ void store_codes(char *dst, const Codes<F32, EPT> &c) {
+    if constexpr (EPT == 4)
+        *reinterpret_cast<uint32_t *>(dst) = c.w[0];
+    else
+        *reinterpret_cast<uint4 *>(dst) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
+}
+
+template <bool F32, int EPT>
 __global__ __launch_bounds__(256) void quantize_cache_kernel(
-    const char *__restrict__ key, const char *__restrict__ value, uint32_t *__restrict__ kc,
-    uint32_t *__restrict__ vc, const int64_t *__restrict__ slots, const float *__restrict__ k_scale,
-    const float *__restrict__ v_scale, int32_t num_tokens, int32_t quads_per_row,
+    const char *__restrict__ key, const char *__restrict__ value, char *__restrict__ kc,
+    char *__restrict__ vc, const int64_t *__restrict__ slots, const float *__restrict__ k_scale,
+    const float *__restrict__ v_scale, int32_t num_tokens, int32_t pieces_per_row,
     int32_t head_dim, int64_t num_slots) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t t = i / quads_per_row;
-    const int32_t c = (int32_t)(i - t * quads_per_row);
+    const int64_t t = i / pieces_per_row;
+    const int32_t c = (int32_t)(i - t * pieces_per_row);
     if (t >= num_tokens) return;
     const int64_t s = slots[t];
     if (s < 0 || s >= num_slots) return;
-    const int32_t h = (c * 4) / head_dim;  // 4 elements never straddle two heads
-    const size_t src = ((size_t)t * quads_per_row + c) * 4 * (F32 ? 4 : 2);
-    kc[s * quads_per_row + c] = quantize4<F32>(key + src, k_scale[h]);
-    vc[s * quads_per_row + c] = quantize4<F32>(value + src, v_scale[h]);
+    const int32_t h = (c * EPT) / head_dim;  // EPT elements never straddle two heads
+    const size_t src = ((size_t)t * pieces_per_row + c) * EPT * (F32 ? 4 : 2);
+    const size_t dst = ((size_t)s * pieces_per_row + c) * EPT;
+    store_codes<F32, EPT>(kc + dst, quantize_n<F32, EPT>(key + src, k_scale[h]));
+    store_codes<F32, EPT>(vc + dst, quantize_n<F32, EPT>(value + src, v_scale[h]));
 }
 
 __global__ __launch_bounds__(256) void expand_block_tables_kernel(
@@ -134,14 +168,19 @@ hipError_t launch_quantize_cache(const void *key, const void *value, void *kc, v
                                  int32_t head_dim, int64_t num_slots, bool in_f32,
                                  hipStream_t stream) {
     if (num_tokens == 0) return hipSuccess;
-    const int32_t qpr = row_elems / 4;
-    const int64_t total = (int64_t)num_tokens * qpr;
+    // 16 elements a thread unless that leaves fewer than 256K threads (a
+    // 6,000-token write of 512-element rows still gains from 4)
+    const bool small = (int64_t)num_tokens * (row_elems / 16) < 262144;
+    const int32_t ept = small ? 4 : 16;
+    const int32_t ppr = row_elems / ept;
+    const int64_t total = (int64_t)num_tokens * ppr;
     const int64_t blocks = (total + 255) / 256;
-    auto kernel = in_f32 ? quantize_cache_kernel<true> : quantize_cache_kernel<false>;
+    auto kernel = small ? (in_f32 ? quantize_cache_kernel<true, 4> : quantize_cache_kernel<false, 4>)
+                        : (in_f32 ? quantize_cache_kernel<true, 16> : quantize_cache_kernel<false, 16>);
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const char *>(key), static_cast<const char *>(value),
-                       static_cast<uint32_t *>(kc), static_cast<uint32_t *>(vc), slots, k_scale,
-                       v_scale, num_tokens, qpr, head_dim, num_slots);
+                       static_cast<char *>(kc), static_cast<char *>(vc), slots, k_scale, v_scale,
+                       num_tokens, ppr, head_dim, num_slots);
     return hipGetLastError();
 }
 

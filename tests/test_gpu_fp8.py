@@ -69,8 +69,19 @@ def test_fp8_cache_write_bit_exact(dtype, hkv, d):
     """Random rows spanning 12 binades around the scale (so codes saturate and
     reach the subnormals), specials (NaN, +-inf, +-0, tiny), skipped slots:
     every code equal to the oracle's."""
-    g = torch.Generator().manual_seed(hkv * 1000 + d + (dtype == torch.float32))
-    T, nb, bs = 300, 40, 16
+    _bit_exact_write(dtype, hkv, d, 300, 40)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_fp8_cache_write_bit_exact_large(dtype):
+    """A write large enough (4,500 rows of 8 x 128) for the kernel's
+    16-elements-a-thread form; the smaller writes above take 4 a thread."""
+    _bit_exact_write(dtype, 8, 128, 4500, 300)
+
+
+def _bit_exact_write(dtype, hkv, d, T, nb):
+    g = torch.Generator().manual_seed(hkv * 1000 + d + (dtype == torch.float32) + (T if T != 300 else 0))
+    bs = 16
     mag = torch.pow(2.0, torch.empty(T, hkv, d).uniform_(-14.0, 10.0, generator=g))
     sign = torch.where(torch.rand(T, hkv, d, generator=g) < 0.5, -1.0, 1.0)
     key = (mag * sign * 0.01).to(dtype)
