@@ -40,9 +40,11 @@
 //    extra cycle each, which does not limit this memory-bound kernel);
 //  * the waves' states meet in LDS in the accumulator layout: every wave
 //    holds the same (head, dim) at the same lane and register, so each lane
-//    merges one float4 position of all waves and stores 4 consecutive dims
-//    (one workgroup per CU leaves no other workgroup to hide this epilogue, so
-//    it is kept to a few vector LDS reads per lane).
+//    merges one float4 position of all waves (its own from registers) and
+//    stores 4 consecutive dims; the states are parked in the waves' own rings
+//    and the queries sit in per-wave areas, so the kernel has one barrier
+//    (one workgroup per CU leaves no other workgroup to hide the start-up and
+//    the epilogue, so both are kept short).
 #include <cstdlib>
 #include <type_traits>
 
@@ -369,7 +371,8 @@ __global__ __launch_bounds__(NW * 64) void decode_rows_kernel(const AttnParams p
 #pragma unroll
         for (int X = 0; X < NB; ++X) {
 #pragma unroll
-            for (int b = 0; b < C::DB; ++b) mo[(X * C::DB + b) * 64 + lane] = o[X][b];
+            for (int b = 0; b < C::DB; ++b)  // tiles this wave merges stay in registers
+                if ((X * C::DB + b) % NW != wave) mo[(X * C::DB + b) * 64 + lane] = o[X][b];
             if (grp == 0) {
                 mm[X * 16 + col] = mtrue[X];
                 mm[NB * 16 + X * 16 + col] = l[X];
@@ -379,47 +382,51 @@ __global__ __launch_bounds__(NW * 64) void decode_rows_kernel(const AttnParams p
     __syncthreads();
 
     const bool direct = nparts <= 1;
-    for (int j = wave; j < NB * C::DB; j += NW) {
-        const int X = j / C::DB;
-        const int b = j - X * C::DB;
-        float mw[NW];
-        float M = NEG_INF;
+#pragma unroll
+    for (int X = 0; X < NB; ++X) {
+        float fw[NW];
+        float M = NEG_INF, den = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            mw[w] = ring_m(w)[X * 16 + col];
-            M = fmaxf(M, mw[w]);
+            fw[w] = ring_m(w)[X * 16 + col];
+            M = fmaxf(M, fw[w]);
         }
-        f32x4_t num = {0.f, 0.f, 0.f, 0.f};
-        float den = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            const float f = exp2_diff(mw[w], M);
-            num += ring_o(w)[(X * C::DB + b) * 64 + lane] * f;
-            den += ring_m(w)[NB * 16 + X * 16 + col] * f;
+            fw[w] = exp2_diff(fw[w], M);
+            den += ring_m(w)[NB * 16 + X * 16 + col] * fw[w];
         }
-        if (col >= ncol) continue;
-        const int h = X * ncol + col;
-        const int d0 = 16 * b + 4 * grp;
-        if (direct) {
-            float inv = 1.f / den;
-            if (p.sinks) {
-                // the head's sink: one more denominator term, no value (log2 units)
-                const float s2 = p.sinks[h] * LOG2E_F;
-                const float Mx = fmaxf(M, s2);
-                const float a = exp2_diff(M, Mx);
-                inv = a / (den * a + exp2_diff(s2, Mx));
-            }
-            *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.out) +
-                                       ((size_t)q0 * p.hq + h) * D + d0) =
-                make_uint2(pack_bf16(num[0] * inv, num[1] * inv), pack_bf16(num[2] * inv, num[3] * inv));
-        } else {
-            const size_t si = ((size_t)q0 * p.hq + h) * p.max_parts + part;
-            const float inv = 1.f / den;
-            *reinterpret_cast<f32x4_t *>(p.tmp_out + si * D + d0) =
-                f32x4_t{num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv};
-            if (b == 0 && grp == 0) {
-                p.max_logits[si] = M;
-                p.exp_sums[si] = den;
+#pragma unroll
+        for (int b = 0; b < C::DB; ++b) {
+            if ((X * C::DB + b) % NW != wave) continue;
+            f32x4_t num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                num += (w == wave ? o[X][b] : ring_o(w)[(X * C::DB + b) * 64 + lane]) * fw[w];
+            if (col >= ncol) continue;
+            const int h = X * ncol + col;
+            const int d0 = 16 * b + 4 * grp;
+            if (direct) {
+                float inv = 1.f / den;
+                if (p.sinks) {
+                    // the head's sink: one more denominator term, no value (log2 units)
+                    const float s2 = p.sinks[h] * LOG2E_F;
+                    const float Mx = fmaxf(M, s2);
+                    const float a = exp2_diff(M, Mx);
+                    inv = a / (den * a + exp2_diff(s2, Mx));
+                }
+                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.out) +
+                                           ((size_t)q0 * p.hq + h) * D + d0) =
+                    make_uint2(pack_bf16(num[0] * inv, num[1] * inv), pack_bf16(num[2] * inv, num[3] * inv));
+            } else {
+                const size_t si = ((size_t)q0 * p.hq + h) * p.max_parts + part;
+                const float inv = 1.f / den;
+                *reinterpret_cast<f32x4_t *>(p.tmp_out + si * D + d0) =
+                    f32x4_t{num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv};
+                if (b == 0 && grp == 0) {
+                    p.max_logits[si] = M;
+                    p.exp_sums[si] = den;
+                }
             }
         }
     }
