@@ -613,10 +613,14 @@ __global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefil
 #ifndef PA_PREFILL_NST
 #define PA_PREFILL_NST(D) 2
 #endif
+// The 8-wave form (one workgroup per CU) has the LDS for a third stage.
+#ifndef PA_PREFILL_NST_WIDE
+#define PA_PREFILL_NST_WIDE 3
+#endif
 
 template <int D, bool KV8, int NWV>
 hipError_t launch_dw(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
-    constexpr int N = PA_PREFILL_N(D), NST = PA_PREFILL_NST(D);
+    constexpr int N = PA_PREFILL_N(D), NST = NWV == 8 ? PA_PREFILL_NST_WIDE : PA_PREFILL_NST(D);
     const int TPW = 32 / p.group;
     const int BQ = NWV * TPW;
     AttnParams q = p;
