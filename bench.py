@@ -171,7 +171,8 @@ class Step:
         self.graphs[k % len(self.graphs)].replay()
 
     def kernel_ms(self):
-        """Mean durations (ms) of: cache write, table view, attention, reduce."""
+        """Mean durations (ms) of: cache write, table view (only where the
+        step launches one), attention, reduce."""
         n = len(self.events)
         if not n:
             return {}
@@ -179,8 +180,8 @@ class Step:
         for ev in self.events:
             for k in range(4):
                 tot[k] += ev[k].elapsed_time(ev[k + 1])
-        return dict(zip(("cache_write", "table_view", "attention", "reduce"),
-                        (t / n for t in tot)))
+        names = ("cache_write", "table_view", "attention", "reduce")
+        return {k: t / n for k, t in zip(names, tot) if k != "table_view" or self.ratio > 1}
 
 
 def step_bytes(w, include_cache_write, kv_elt_bytes=None):
@@ -332,23 +333,69 @@ def block_offload(device, n_blocks=4096, reps=10):
     return res
 
 
-def cpu_baseline(w, budget_s=10.0):
-    """The fp64 oracle, as it stands, on whole batches of the same workload
-    until about budget_s of wall time has passed."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# Runs in a child process (OMP_NUM_THREADS=1 is read when the oracle's
+# OpenMP runtime starts): prints the median seconds of 3 single-threaded
+# passes of the oracle over the GQA decode batch.
+_ONE_THREAD = """
+import json, sys, time
+sys.path.insert(0, {root!r})
+import oracle, workloads as W
+w = W.gqa_decode_bf16()
+oracle.run_workload(w, rows=[(0, 0)])
+ts = []
+for _ in range(3):
+    t0 = time.perf_counter(); oracle.run_workload(w); ts.append(time.perf_counter() - t0)
+print(json.dumps({{"threads": oracle.num_threads(), "s": sorted(ts)[1]}}))
+"""
+
+
+def cpu_baseline(w, pass_s=3.0):
+    """The fp64 oracle, as it stands, timed on this host: the median of 3
+    passes on all the threads OpenMP gives it (each pass repeats the whole
+    batch for about pass_s seconds), then the median of 3 single-threaded
+    passes in a child process.  Work unit: the workload's algorithmic bytes."""
+    import subprocess
     import oracle
-    oracle.attention  # noqa: B018  (loads / builds the oracle library)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.run_workload(w)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or el / reps * (reps + 1) > 3 * budget_s:
-            break
-    per = el / reps
-    return {"value": round(w.algorithmic_bytes() / per / 1e9, 3), "unit": "GB/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{reps} full passes of the {w.name} batch ({w.num_seqs} requests, all "
-                      f"{w.num_q_heads} heads), {per * 1e3:.1f} ms each, fp64 C oracle, OpenMP"}
+    oracle.run_workload(w, rows=[(0, 0)])  # loads / builds the oracle library
+    t0 = time.perf_counter()
+    oracle.run_workload(w)
+    reps = max(1, int(pass_s / max(time.perf_counter() - t0, 1e-3)))
+    per = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.run_workload(w)
+        per.append((time.perf_counter() - t0) / reps)
+    per = sorted(per)[1]
+    one = None
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", _ONE_THREAD.format(root=ROOT)], env=env,
+                       capture_output=True, text=True, timeout=300)
+    if r.returncode == 0 and r.stdout.strip():
+        one = json.loads(r.stdout.strip().splitlines()[-1])
+    nb = w.algorithmic_bytes()
+    res = {"value": round(nb / per / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+           "kind": "oracle",
+           "sample": f"median of 3 passes, each {reps} full runs of the {w.name} batch "
+                     f"({w.num_seqs} requests, all {w.num_q_heads} heads; {per * 1e3:.1f} ms per "
+                     f"batch), fp64 C oracle, OpenMP over (query row, head)",
+           "cpu_model": cpu_model(), "host_logical_cpus": os.cpu_count(),
+           "affinity_cpus": len(os.sched_getaffinity(0))}
+    if one:
+        res["single_thread"] = {"value": round(nb / one["s"] / 1e9, 3), "unit": "GB/s",
+                                "ms_per_batch": round(one["s"] * 1e3, 1),
+                                "threads": one["threads"], "sample": "median of 3 full batches"}
+    return res
 
 
 def copy_calibration(device, mib=512, reps=5):
@@ -485,20 +532,12 @@ def main():
         # partition sizes: the mixed batches run unsplit (their rows are at
         # most 3,000 keys); the verify batch splits its long contexts so its
         # 164 q-tiles do not leave most of the GPU idle
-        uniform = lambda: W.build(  # noqa: E731
-            "prefill_uniform_bf16", seed=7, q_lens=[4096] * 8, seq_lens=[8192] * 8,
-            num_q_heads=16, num_kv_heads=2, head_dim=256, block_size=16,
-            num_blocks=8 * 8192 // 16 + 8, dtype=torch.bfloat16,
-            description="8 x 4096-token prompt chunks over 4096 cached tokens, 16/2/256")
         for name, P3 in (("mixed_prefill_bf16_A", 0), ("mixed_prefill_bf16_B", 0),
                          ("spec_verify_bf16", 1024), ("prefill_uniform_bf16", 0),
                          ("mixed_prefill_fp8kv_B", 0), ("prefill_uniform_fp8kv", 0)):
             kv8 = "fp8kv" in name
             try:
-                if name.startswith("prefill_uniform"):
-                    w3 = uniform()
-                else:
-                    w3 = W.CONFIGS[name.replace("fp8kv", "bf16")]()
+                w3 = W.CONFIGS[name.replace("fp8kv", "bf16")]()
                 s3, k3, s3w, _ = measure(w3, P3, steps2, 5, 2, device, kv8=kv8)
             except Exception as e:  # report, do not hide: the line says what failed
                 sec_out[name] = {"error": str(e)[:200]}

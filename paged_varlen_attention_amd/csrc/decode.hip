@@ -1,8 +1,8 @@
-// decode.hip -- paged GQA decode attention for gfx950 on the vector ALUs: one
-// workgroup per query token (decode batches over 8-bit caches and fp32
-// batches; every token of fp32 batches, whose key range ends at the token's own
-// causal position).  bf16 decode batches over bf16 caches take the MFMA form
-// in decode_mfma.hip.
+// decode.hip -- paged GQA decode attention for gfx950 on the vector ALUs, for
+// float32 batches: one workgroup per request (decode batches) or per query
+// token (longer windows: every token's key range ends at its own causal
+// position).  bf16 queries take the MFMA kernels (decode_rows.hip,
+// decode_mfma.hip for decode batches, prefill.hip for longer windows).
 //
 // What it computes follows the vllm-metal kernel walkthrough ("What is Paged
 // Attention"; GQA decode tips 1-4): softmax(q.k * scale) v over the keys of one
@@ -22,19 +22,12 @@
 //  * the page-table walk is one wave-wide load of up to 64 entries per window,
 //    then v_readlane per chunk (a scalar broadcast, no shuffles), and the DMA
 //    base addresses are pure scalar arithmetic;
-//  * a token's row is split over L lanes (32 bytes each); QK^T uses
-//    v_dot2c_f32_bf16 on bf16 pairs and a DPP all-reduce over the L lanes;
+//  * a token's row is split over L lanes (32 bytes each: two 16-byte pieces);
+//    QK^T is an fp32 FMA chain plus a DPP all-reduce over the L lanes;
 //  * every lane keeps its own online-softmax state for its token subset; the
 //    loop over a wave's full chunks has no data-dependent branch (only its
 //    last chunk can hold the end of the range and is peeled off), so the
 //    accumulators stay in their registers;
-//  * PV pairs two tokens per lane: p is packed to bf16 pairs and V is
-//    interleaved with v_perm_b32 so one v_dot2c does two multiply-adds;
-//  * 8-bit E4M3 caches (the library's own KV quantisation) move half the
-//    bytes: a lane's 16 elements are two 8-byte LDS pieces, converted to bf16
-//    pairs with gfx950's v_cvt_scalef32_pk_bf16_fp8 (exact: every E4M3 value
-//    is a bf16 value), after which the bf16 path runs unchanged; the head's K
-//    scale is folded into the softmax scale and its V scale into the output;
 //  * at the end, every lane is rescaled to the wave-wide max and the lane
 //    groups of the wave are summed in registers (DPP rotations inside each
 //    16-lane row, then v_permlane16/32_swap across rows only as far as the
@@ -46,80 +39,48 @@
 namespace pa {
 namespace {
 
-// Merge states a wave leaves in LDS: 1 = rows merged in registers first.
-#ifndef PA_DECODE_SPW_MAX
-#define PA_DECODE_SPW_MAX(L) 4
-#endif
-// Wave-priority balancing of co-resident workgroups (see the main loop): on
-// for 8-bit caches, where it measured 4-8% faster; neutral to slightly slower
-// on bf16 caches.
-#ifndef PA_DECODE_PRIO
-#define PA_DECODE_PRIO(KV8) (KV8)
-#endif
-// bf16 decode batches over bf16 caches take the MFMA kernel (decode_mfma.hip).
-#ifndef PA_DECODE_MFMA
-#define PA_DECODE_MFMA 1
-#endif
-#ifndef PA_DECODE_LAZY
-#define PA_DECODE_LAZY 1
-#endif
 // A lane's reference max m is only raised when a chunk's max exceeds it by
 // more than this (log2 units); weights then stay below 2^RESCALE_THRESHOLD.
 constexpr float RESCALE_THRESHOLD = 8.0f;
 
 
-template <typename T, bool KV8_, int D, int GT, int CT_, int NW_, int NST_>
+template <int D, int GT, int CT_, int NW_, int NST_>
 struct DecodeCfg {
-    static constexpr bool BF16 = sizeof(T) == 2;
-    static constexpr bool KV8 = KV8_;            // caches hold E4M3 codes (T is bf16)
-    static constexpr int ELT = sizeof(T);
     static constexpr int CT = CT_;               // tokens per chunk (LDS stage)
-    static constexpr int QR = D * ELT;           // bytes per query row of one head
-    static constexpr int R = KV8 ? D : QR;       // bytes per K/V row of one head
-    static constexpr int L = QR / 32;            // lanes per token (16 or 8 elements each)
-    static constexpr int PIECE = KV8 ? 8 : 16;   // bytes of one of a lane's two row pieces
+    static constexpr int R = D * 4;              // bytes per Q/K/V row of one head
+    static constexpr int L = R / 32;             // lanes per token (8 elements each)
     static constexpr int TPP = 64 / L;           // tokens per pass of the wave
     static constexpr int NP = CT / TPP;          // passes per chunk
-    static constexpr int EPW = 4 / ELT;          // elements per 32-bit word
-    // Bytes one lane moves per DMA instruction: 16, or 4 when 16 would make
-    // one instruction span more than 8 rows (8-bit rows of 64 elements), since
-    // a chunk of 8-token pages switches page after row 8.
-    static constexpr int DW = (R * 8 < 64 * 16) ? 4 : 16;
-    static constexpr int NI = CT * R / (64 * DW);  // DMA instructions per chunk per tensor
-    static constexpr int RPI = 64 * DW / R;        // rows moved by one DMA instruction
+    static constexpr int NI = CT * R / 1024;     // DMA instructions per chunk per tensor
+    static constexpr int RPI = 1024 / R;         // rows moved by one DMA instruction
     static constexpr int SLOT = 2 * CT * R;      // bytes of one LDS stage (K rows, then V rows)
     static constexpr int NW = NW_;
     static constexpr int NST = NST_;
     static constexpr int VM_PER_CHUNK = 2 * NI;
-    // passes paired in one v_dot2 for PV
-    static constexpr int SU = (BF16 && NP >= 2) ? 2 : 1;
-    static constexpr int NE = 32 / ELT;          // elements per lane per row
+    static constexpr int NE = 8;                 // elements per lane per row
     static constexpr int STATE_FLOATS = GT * D + 2 * GT;  // acc, then m, then l
     static constexpr int STAGE_BYTES = NW * NST * SLOT;
     // Merge states per wave: as many row states as fit in the staging LDS
     // (4 rows, or 2 halves when a token spans 32 lanes), else fewer after
     // merging rows in registers.
     static constexpr int ROWS = L <= 16 ? 4 : 2;  // lane groups of a wave (16- or 32-lane rows)
-    static constexpr int SPW_MAX = PA_DECODE_SPW_MAX(L) < ROWS ? PA_DECODE_SPW_MAX(L) : ROWS;
     static constexpr bool fits(int spw) { return NW * spw * STATE_FLOATS * 4 <= STAGE_BYTES; }
-    static constexpr int SPW = fits(SPW_MAX) ? SPW_MAX : (fits(SPW_MAX / 2) ? SPW_MAX / 2 : 1);
+    static constexpr int SPW = fits(ROWS) ? ROWS : (fits(ROWS / 2) ? ROWS / 2 : 1);
     static constexpr int NS = NW * SPW;          // merge states of the workgroup
     static constexpr int MERGE_BYTES = NS * STATE_FLOATS * 4;
     static constexpr int LDS_BYTES = STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES;
-    static_assert(L >= 4 && L <= 32, "row split");
+    static_assert(L >= 8 && L <= 32, "row split");
     static_assert(NP >= 1 && CT % TPP == 0, "chunk covers whole passes");
-    static_assert(NI >= 1 && RPI >= 1 && RPI <= 8 && CT * R % (64 * DW) == 0, "dma shape");
-    static_assert(!KV8 || BF16, "8-bit caches are read with bf16 queries");
+    static_assert(NI >= 1 && RPI >= 1 && RPI <= 8 && CT * R % 1024 == 0, "dma shape");
     static_assert((NST - 1) * VM_PER_CHUNK < 64, "vmcnt range");
-    static_assert(NP % SU == 0, "pass pairing");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
 // Element index (within the head's D) of word w of lane column c.
 template <class C>
 __device__ __forceinline__ int word_elem(int c, int w) {
-    // two pieces per lane: piece i holds elements (i*L + c)*16/ELT onward
-    return ((w / 4) * C::L + c) * (16 / C::ELT) + (w % 4) * C::EPW;
+    // two pieces per lane: piece i holds elements (i*L + c)*4 onward
+    return ((w / 4) * C::L + c) * 4 + (w % 4);
 }
 
 // Wait until this wave's DMA for the chunk `ahead` chunks before the newest
@@ -137,29 +98,13 @@ __device__ __forceinline__ void wait_chunks_ahead(int ahead) {
     }
 }
 
-// Four E4M3 codes -> two bf16 pairs (codes 0,1 and codes 2,3), exact.
-__device__ __forceinline__ void e4m3x4_to_bf16(uint32_t codes, uint32_t &lo, uint32_t &hi) {
-    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false));
-    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true));
-}
-
-// The lane's 8 words of a row (bf16 pairs or fp32 values): its two pieces,
-// converted to bf16 pairs for 8-bit rows.
+// The lane's 8 fp32 words of a row: its two 16-byte pieces.
 template <class C>
 __device__ __forceinline__ void read_row_words(const char *lds_row, int c, uint32_t (&w)[8]) {
-    if constexpr (C::KV8) {
-        const uint2 a = *reinterpret_cast<const uint2 *>(lds_row + c * 8);
-        const uint2 b = *reinterpret_cast<const uint2 *>(lds_row + (C::L + c) * 8);
-        e4m3x4_to_bf16(a.x, w[0], w[1]);
-        e4m3x4_to_bf16(a.y, w[2], w[3]);
-        e4m3x4_to_bf16(b.x, w[4], w[5]);
-        e4m3x4_to_bf16(b.y, w[6], w[7]);
-    } else {
-        const uint4 a = *reinterpret_cast<const uint4 *>(lds_row + c * 16);
-        const uint4 b = *reinterpret_cast<const uint4 *>(lds_row + (C::L + c) * 16);
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-    }
+    const uint4 a = *reinterpret_cast<const uint4 *>(lds_row + c * 16);
+    const uint4 b = *reinterpret_cast<const uint4 *>(lds_row + (C::L + c) * 16);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
 }
 
 // Max over all 64 lanes of the wave.
@@ -226,14 +171,9 @@ __device__ __forceinline__ void chunk_step(GetK getk, GetV getv, int tip, int to
 #pragma unroll
         for (int g = 0; g < GT; ++g) {
             float a = 0.f;
-            if constexpr (C::BF16) {
 #pragma unroll
-                for (int w = 0; w < 8; ++w) a = dot2(qw[g][w], kw[w], a);
-            } else {
-#pragma unroll
-                for (int w = 0; w < 8; ++w)
-                    a = fmaf(__uint_as_float(qw[g][w]), __uint_as_float(kw[w]), a);
-            }
+            for (int w = 0; w < 8; ++w)
+                a = fmaf(__uint_as_float(qw[g][w]), __uint_as_float(kw[w]), a);
             sc[j][g] = a;
         }
     }
@@ -247,7 +187,7 @@ __device__ __forceinline__ void chunk_step(GetK getk, GetV getv, int tip, int to
     // ---- online softmax: new running max, rescale of l and acc ----
     // In an unmasked chunk every score is finite, so the new max is finite and
     // exp2 needs no -inf guard; the masked chunk guards both.
-    if constexpr (PA_DECODE_LAZY && !MASKED) {
+    if constexpr (!MASKED) {
         // Lazy: rescale (all lanes, uniformly) only when some lane's max grew
         // past its reference by more than the threshold.
         float mx[GT];
@@ -296,60 +236,26 @@ __device__ __forceinline__ void chunk_step(GetK getk, GetV getv, int tip, int to
 
     // ---- PV ----
 #pragma unroll
-    for (int j0 = 0; j0 < NP; j0 += C::SU) {
-        uint32_t vw[C::SU][8];
+    for (int j = 0; j < NP; ++j) {
+        uint32_t vw[8];
+        getv(j, vw);
+        if (MASKED && !valid[j]) {
 #pragma unroll
-        for (int j = 0; j < C::SU; ++j) {
-            getv(j0 + j, vw[j]);
-            if (MASKED && !valid[j0 + j]) {
-#pragma unroll
-                for (int w = 0; w < 8; ++w) vw[j][w] = 0u;
-            }
+            for (int w = 0; w < 8; ++w) vw[w] = 0u;
         }
-        if constexpr (C::BF16 && C::SU == 2) {
-            constexpr uint32_t ONES = 0x3F803F80u;  // bf16 pair (1, 1)
-            uint32_t pk[GT];
 #pragma unroll
-            for (int g = 0; g < GT; ++g) {
-                pk[g] = pack_bf16(pr[j0][g], pr[j0 + 1][g]);
-                l[g] = dot2(pk[g], ONES, l[g]);  // the weights actually applied
-            }
+        for (int g = 0; g < GT; ++g) {
+            l[g] += pr[j][g];
 #pragma unroll
-            for (int w = 0; w < 8; ++w) {
-                const uint32_t lo = perm(vw[1][w], vw[0][w], 0x05040100u);
-                const uint32_t hi = perm(vw[1][w], vw[0][w], 0x07060302u);
-#pragma unroll
-                for (int g = 0; g < GT; ++g) {
-                    accv[g][2 * w] = dot2(pk[g], lo, accv[g][2 * w]);
-                    accv[g][2 * w + 1] = dot2(pk[g], hi, accv[g][2 * w + 1]);
-                }
-            }
-        } else if constexpr (C::BF16) {
-#pragma unroll
-            for (int g = 0; g < GT; ++g) {
-                const float pb = bf16hi(pack_bf16(0.f, pr[j0][g]));
-                l[g] += pb;
-#pragma unroll
-                for (int w = 0; w < 8; ++w) {
-                    accv[g][2 * w] = fmaf(pb, bf16lo(vw[0][w]), accv[g][2 * w]);
-                    accv[g][2 * w + 1] = fmaf(pb, bf16hi(vw[0][w]), accv[g][2 * w + 1]);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int g = 0; g < GT; ++g) {
-                l[g] += pr[j0][g];
-#pragma unroll
-                for (int w = 0; w < 8; ++w)
-                    accv[g][w] = fmaf(pr[j0][g], __uint_as_float(vw[0][w]), accv[g][w]);
-            }
+            for (int w = 0; w < 8; ++w)
+                accv[g][w] = fmaf(pr[j][g], __uint_as_float(vw[w]), accv[g][w]);
         }
     }
 }
 
-template <typename T, bool KV8, int D, int GT, int CT, int NW, int NST>
+template <int D, int GT, int CT, int NW, int NST>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
-    using C = DecodeCfg<T, KV8, D, GT, CT, NW, NST>;
+    using C = DecodeCfg<D, GT, CT, NW, NST>;
     __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
 
     // Grid (hkv, rows, parts).  The KV heads of one partition are adjacent,
@@ -423,13 +329,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
     uint32_t qw[GT][8];
     {
         const char *qbase = reinterpret_cast<const char *>(p.q) +
-                            ((size_t)q0 * p.hq + (size_t)kvh * G) * C::QR;
+                            ((size_t)q0 * p.hq + (size_t)kvh * G) * C::R;
 #pragma unroll
         for (int g = 0; g < GT; ++g) {
             if (g < G) {
-                const uint4 a = *reinterpret_cast<const uint4 *>(qbase + g * C::QR + c * 16);
+                const uint4 a = *reinterpret_cast<const uint4 *>(qbase + g * C::R + c * 16);
                 const uint4 b =
-                    *reinterpret_cast<const uint4 *>(qbase + g * C::QR + (C::L + c) * 16);
+                    *reinterpret_cast<const uint4 *>(qbase + g * C::R + (C::L + c) * 16);
                 qw[g][0] = a.x; qw[g][1] = a.y; qw[g][2] = a.z; qw[g][3] = a.w;
                 qw[g][4] = b.x; qw[g][5] = b.y; qw[g][6] = b.z; qw[g][7] = b.w;
             } else {
@@ -457,17 +363,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
 #pragma unroll
         for (int e = 0; e < NE; ++e) accv[g][e] = 0.f;
     }
-    // 8-bit caches: the head's K scale joins the softmax scale
-    const float scale_log2 = KV8 ? p.scale_log2 * p.k_scale[kvh] : p.scale_log2;
+    const float scale_log2 = p.scale_log2;
 
     // Per-lane byte offsets of the rows this lane moves, relative to the row of
     // the chunk's first token (one per DMA instruction).
     uint32_t voff[C::NI];
 #pragma unroll
     for (int ii = 0; ii < C::NI; ++ii) {
-        const int row = ii * C::RPI + lane / (C::R / C::DW);
-        const int piece = lane % (C::R / C::DW);
-        voff[ii] = (uint32_t)row * row_stride + (uint32_t)piece * C::DW;
+        const int row = ii * C::RPI + lane / (C::R / 16);
+        const int piece = lane % (C::R / 16);
+        voff[ii] = (uint32_t)row * row_stride + (uint32_t)piece * 16;
     }
     const uint32_t lds_wave = lds_addr(lds) + (uint32_t)(wave * NST * C::SLOT);
 
@@ -497,11 +402,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
         const uint32_t ldsv = ldsk + CT * C::R;
 #pragma unroll
         for (int ii = 0; ii < C::NI; ++ii)
-            dma_lds<C::DW>(ii * C::RPI >= 8 ? kb1 : kb0, voff[ii], ldsk + ii * 64 * C::DW);
+            dma16(ii * C::RPI >= 8 ? kb1 : kb0, voff[ii], ldsk + ii * 1024);
 #pragma unroll
         for (int ii = 0; ii < C::NI; ++ii)
-            dma_lds<C::DW>((ii * C::RPI >= 8 ? kb1 : kb0) + v_minus_k, voff[ii],
-                           ldsv + ii * 64 * C::DW);
+            dma16((ii * C::RPI >= 8 ? kb1 : kb0) + v_minus_k, voff[ii], ldsv + ii * 1024);
     };
 
 #pragma unroll
@@ -516,23 +420,10 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
         kst = lds + (wave * NST + k % NST) * C::SLOT;
         vst = kst + CT * C::R;
     };
-    // Co-resident workgroups: the hardware favours the oldest waves, so one
-    // workgroup of a CU runs ahead while its neighbour lags and then finishes
-    // alone, streaming slowly.  With PRIO, waves start at high priority and
-    // step it down as they pass quarters of their loop, so lagging waves win
-    // the arbiter.
-    constexpr bool PRIO = PA_DECODE_PRIO(KV8);
-    const int q1 = nmy / 4, q2 = nmy / 2, q3 = (3 * nmy) / 4;
-    if constexpr (PRIO) __builtin_amdgcn_s_setprio(3);
     auto lds_rows = [&](const char *st) {
         return [=](int j, uint32_t (&w)[8]) { read_row_words<C>(st + (j * C::TPP + tip) * C::R, c, w); };
     };
     for (int k = 0; k < nmy - 1; ++k) {
-        if constexpr (PRIO) {
-            if (k == q1) __builtin_amdgcn_s_setprio(2);
-            if (k == q2) __builtin_amdgcn_s_setprio(1);
-            if (k == q3) __builtin_amdgcn_s_setprio(0);
-        }
         const char *kst, *vst;
         stage(k, kst, vst);
         chunk_step<C, GT, false>(lds_rows(kst), lds_rows(vst), tip, 0, 0, scale_log2, qw, m,
@@ -581,13 +472,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
             for (int g = 0; g < GT; ++g)
 #pragma unroll
                 for (int w = 0; w < 8; ++w) {
-                    const int d = word_elem<C>(c, w);
-                    if constexpr (C::BF16) {
-                        st[g * D + d] = accv[g][2 * w];
-                        st[g * D + d + 1] = accv[g][2 * w + 1];
-                    } else {
-                        st[g * D + d] = accv[g][w];
-                    }
+                    st[g * D + word_elem<C>(c, w)] = accv[g][w];
                 }
         }
         if (writer && c == 0) {
@@ -601,7 +486,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
     __syncthreads();
 
     const bool direct = nparts <= 1;
-    const float vscale = KV8 ? p.v_scale[kvh] : 1.0f;  // 8-bit caches: the head's V scale
     for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
         const int g = idx / D;
         const int d = idx - g * D;
@@ -619,21 +503,16 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
         }
         const int h = kvh * G + g;
         float o = num / den;
-        if constexpr (KV8) o *= vscale;
         if (direct && p.sinks) {
             // the head's sink: one more denominator term, no value (log2 units)
             const float s2 = p.sinks[h] * LOG2E_F;
             const float Mx = fmaxf(M, s2);
             const float a = exp2_diff(M, Mx);
             o = num * a / (den * a + exp2_diff(s2, Mx));
-            if constexpr (KV8) o *= vscale;
         }
         if (direct) {
             const size_t oi = ((size_t)q0 * p.hq + h) * D + d;
-            if constexpr (C::BF16)
-                reinterpret_cast<uint16_t *>(p.out)[oi] = to_bf16(o);
-            else
-                reinterpret_cast<float *>(p.out)[oi] = o;
+            reinterpret_cast<float *>(p.out)[oi] = o;
         } else {
             const size_t si = ((size_t)q0 * p.hq + h) * p.max_parts + part;
             p.tmp_out[si * D + d] = o;
@@ -645,71 +524,36 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const AttnParams p) {
     }
 }
 
-// Chunk tokens, waves per workgroup and LDS stages per wave, by K/V row bytes.
-#ifndef PA_DECODE_CT
-#define PA_DECODE_CT(R) ((R) >= 512 ? 8 : 16)
-#endif
-#ifndef PA_DECODE_NW
-#define PA_DECODE_NW(R) ((R) >= 1024 ? 2 : 4)
-#endif
-#ifndef PA_DECODE_NST
-#define PA_DECODE_NST(R) 2
-#endif
+// Chunk tokens and waves per workgroup by K/V row bytes (D = 64 -> 256 B,
+// 128 -> 512 B, 256 -> 1 KB), two LDS stages per wave.
+constexpr int decode_ct(int R) { return R >= 512 ? 8 : 16; }
+constexpr int decode_nw(int R) { return R >= 1024 ? 2 : 4; }
+constexpr int DECODE_NST = 2;
 
-// The same for 8-bit caches (rows of D bytes).
-#ifndef PA_DECODE_CT8
-#define PA_DECODE_CT8(R) 16
-#endif
-#ifndef PA_DECODE_NW8
-#define PA_DECODE_NW8(R) 4
-#endif
-#ifndef PA_DECODE_NST8
-#define PA_DECODE_NST8(R) 2
-#endif
-
-template <typename T, bool KV8, int D, int GT>
-struct DecodeTuning {
-    static constexpr int R = D * (KV8 ? 1 : (int)sizeof(T));
-    static constexpr int CT = KV8 ? PA_DECODE_CT8(R) : PA_DECODE_CT(R);
-    static constexpr int NW = KV8 ? PA_DECODE_NW8(R) : PA_DECODE_NW(R);
-    static constexpr int NST = KV8 ? PA_DECODE_NST8(R) : PA_DECODE_NST(R);
-};
-
-template <typename T, bool KV8, int D, int GT>
+template <int D, int GT>
 hipError_t launch_t(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
-    using Tn = DecodeTuning<T, KV8, D, GT>;
+    constexpr int CT = decode_ct(4 * D), NW = decode_nw(4 * D);
     const int parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
     const int rows = p.per_token ? p.total_q : p.num_seqs;
     const dim3 grid(p.hkv, rows, parts);
-    dim3 block(Tn::NW * 64);
+    dim3 block(NW * 64);
     if (li) *li = LaunchInfo{{(int)grid.x, (int)grid.y, (int)grid.z}, (int)block.x,
-                             {Tn::CT, Tn::NW, Tn::NST}, 0};
-    hipLaunchKernelGGL((decode_kernel<T, KV8, D, GT, Tn::CT, Tn::NW, Tn::NST>), grid, block, 0,
-                       stream, p);
+                             {CT, NW, DECODE_NST}, 0};
+    hipLaunchKernelGGL((decode_kernel<D, GT, CT, NW, DECODE_NST>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
-template <typename T, bool KV8, int D>
+template <int D>
 hipError_t launch_d(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
     switch (p.group) {
-        case 1: return launch_t<T, KV8, D, 1>(p, stream, li);
-        case 2: return launch_t<T, KV8, D, 2>(p, stream, li);
+        case 1: return launch_t<D, 1>(p, stream, li);
+        case 2: return launch_t<D, 2>(p, stream, li);
         case 3:
-        case 4: return launch_t<T, KV8, D, 4>(p, stream, li);
+        case 4: return launch_t<D, 4>(p, stream, li);
         case 5:
-        case 6: return launch_t<T, KV8, D, 6>(p, stream, li);
+        case 6: return launch_t<D, 6>(p, stream, li);
         case 7:
-        case 8: return launch_t<T, KV8, D, 8>(p, stream, li);
-        default: return hipErrorInvalidValue;
-    }
-}
-
-template <typename T, bool KV8>
-hipError_t launch_dt(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
-    switch (p.head_dim) {
-        case 64: return launch_d<T, KV8, 64>(p, stream, li);
-        case 128: return launch_d<T, KV8, 128>(p, stream, li);
-        case 256: return launch_d<T, KV8, 256>(p, stream, li);
+        case 8: return launch_t<D, 8>(p, stream, li);
         default: return hipErrorInvalidValue;
     }
 }
@@ -723,14 +567,21 @@ bool decode_supported(int dtype, int head_dim, int group) {
 
 bool decode_kv8_supported(int head_dim, int group) { return decode_supported(1, head_dim, group); }
 
+// Routing of the decode path: bf16 queries (bf16 or 8-bit caches) to the MFMA
+// kernels, float32 batches to the vector-ALU kernel above.
 hipError_t launch_decode(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
-#if PA_DECODE_MFMA
-    if (decode_rows_supported(p)) return launch_decode_rows(p, stream, li);
-    if (decode_mfma_supported(p)) return launch_decode_mfma(p, stream, li);
-#endif
-    if (p.kv8) return p.dtype == 1 ? launch_dt<bf16_t, true>(p, stream, li) : hipErrorInvalidValue;
-    if (p.dtype == 1) return launch_dt<bf16_t, false>(p, stream, li);
-    return launch_dt<float, false>(p, stream, li);
+    if (p.dtype == 1) {
+        if (decode_rows_supported(p)) return launch_decode_rows(p, stream, li);
+        if (decode_mfma_supported(p)) return launch_decode_mfma(p, stream, li);
+        return hipErrorInvalidValue;
+    }
+    if (p.kv8) return hipErrorInvalidValue;
+    switch (p.head_dim) {
+        case 64: return launch_d<64>(p, stream, li);
+        case 128: return launch_d<128>(p, stream, li);
+        case 256: return launch_d<256>(p, stream, li);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace pa

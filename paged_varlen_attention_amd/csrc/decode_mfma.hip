@@ -322,11 +322,6 @@ __device__ __forceinline__ void mf_chunk8(Frags8<C> &f, const bf16x8_t (&qb)[C::
     }
 }
 
-// 8-bit caches on this kernel (else the vector-ALU decode kernel).
-#ifndef PA_MF_KV8
-#define PA_MF_KV8 1
-#endif
-
 template <int D, bool KV8, int NW, int NST>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const AttnParams p) {
     using C = MfCfg<D, KV8, NW, NST>;
@@ -610,17 +605,13 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(const AttnParams p
 
 // Waves per workgroup and LDS stages per wave: 2 waves at D = 256 keep two
 // workgroups on a CU (4 waves would need 144 KB of LDS).
-#ifndef PA_MF_NW
-#define PA_MF_NW(D) ((D) == 256 ? 2 : 4)
-#endif
-#ifndef PA_MF_NST
-#define PA_MF_NST(D) 2
-#endif
+constexpr int mf_nw(int D) { return D == 256 ? 2 : 4; }
+constexpr int MF_NST = 2;
 
 template <int D, bool KV8>
 hipError_t launch_mf(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
-    constexpr int NW = PA_MF_NW(D);
-    constexpr int NST = PA_MF_NST(D);
+    constexpr int NW = mf_nw(D);
+    constexpr int NST = MF_NST;
     const int parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
     const dim3 grid(p.hkv, p.num_seqs, parts);
     const dim3 block(NW * 64);
@@ -644,7 +635,7 @@ hipError_t launch_mf_d(const AttnParams &p, hipStream_t stream, LaunchInfo *li) 
 }  // namespace
 
 bool decode_mfma_supported(const AttnParams &p) {
-    return !p.per_token && p.dtype == 1 && (!p.kv8 || PA_MF_KV8) && p.group >= 1 &&
+    return !p.per_token && p.dtype == 1 && p.group >= 1 &&
            p.group <= 8 && (p.head_dim == 64 || p.head_dim == 128 || p.head_dim == 256);
 }
 

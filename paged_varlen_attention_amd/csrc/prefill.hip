@@ -125,38 +125,20 @@ __device__ __forceinline__ void wait_tiles_ahead(int ahead) {
     }
 }
 
-// Workgroups per CU the register budget is sized for (2: at most 256
-// registers a lane; D = 256 keeps 192 of them for O^T and Q^T).
-#ifndef PA_PREFILL_MINW
-#define PA_PREFILL_MINW(D) 2
-#endif
+// Waves per SIMD the register budget is sized for: 2 (at most 256 registers
+// a lane; D = 256 keeps 192 of them for O^T and Q^T).
+constexpr int PREFILL_WAVES_PER_SIMD = 2;
 
 // LDS fragment reads in flight ahead of their MFMA (K for S^T, V^T for O^T).
-#ifndef PA_PREFILL_PF_K
-#define PA_PREFILL_PF_K(D) ((D) >= 256 ? 2 : 4)
-#endif
-#ifndef PA_PREFILL_PF_V
-#define PA_PREFILL_PF_V(D) ((D) >= 256 ? 2 : 4)
-#endif
-#ifndef PA_PREFILL_XCD_CHUNK
-#define PA_PREFILL_XCD_CHUNK 8
-#endif
-constexpr int XCD_CHUNK = PA_PREFILL_XCD_CHUNK;
-// Requests ordered by key count in the work order (launches of up to 64
-// requests).
-#ifndef PA_PREFILL_SORT
-#define PA_PREFILL_SORT 1
-#endif
-#ifndef PA_PREFILL_SCHED
-#define PA_PREFILL_SCHED 1
-#endif
-constexpr bool PF_SCHED = PA_PREFILL_SCHED;
+constexpr int prefill_pf(int D) { return D >= 256 ? 2 : 4; }
+// Consecutive work items kept on one XCD (its L2 serves their shared keys).
+constexpr int XCD_CHUNK = 8;
 
 template <int D, int N, int NST, bool KV8, int NWV>
-__global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefill_kernel(
+__global__ __launch_bounds__(NWV * 64, PREFILL_WAVES_PER_SIMD * 4 / NWV) void prefill_kernel(
     const AttnParams p) {
     using C = PrefillCfg<D, N, NST, KV8, NWV>;
-    constexpr int PF_K = PA_PREFILL_PF_K(D), PF_V = PA_PREFILL_PF_V(D);
+    constexpr int PF_K = prefill_pf(D), PF_V = prefill_pf(D);
     __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
@@ -173,7 +155,7 @@ __global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefil
     // q-tiles of a request see more keys.
     const int n_items = p.grid_tiles * p.hkv * p.grid_parts;
     int lam = blockIdx.x;
-    if (XCD_CHUNK > 0) {
+    {
         const int xcd = lam & 7, slot = lam >> 3;
         lam = ((slot / XCD_CHUNK) * 8 + xcd) * XCD_CHUNK + slot % XCD_CHUNK;
     }
@@ -181,7 +163,7 @@ __global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefil
     lam = n_items - 1 - lam;
     const int x = lam % p.grid_tiles;
     int r, tile;
-    if (PA_PREFILL_SORT && p.num_seqs <= 64) {
+    if (p.num_seqs <= 64) {
         // Up to 64 requests: the virtual tiles list the requests by key count,
         // fewest first, each with exactly its own q-tiles, so that the
         // last-first dispatch starts the requests with the most keys (and
@@ -268,7 +250,7 @@ __global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefil
     const int32_t *bt_row = p.bt + (size_t)r * p.bt_stride;
     auto load_window = [&](int page0) {
         const int lp = page0 + lane;
-        int v = lp < seq_pages ? bt_row[lp] : 0;
+        int v = lp < seq_pages && lp < p.bt_stride ? bt_row[lp] : 0;
         return v < 0 ? 0 : (v >= p.num_blocks ? p.num_blocks - 1 : v);
     };
     int win_page = k_lo >> lbs;
@@ -478,7 +460,7 @@ __global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefil
                 if (ks + PF_K < C::KS) ka[ks % PF_K] = kread(ks + PF_K);
                 s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                                qb[ks], s[b], 0, 0, 0);
-                if (PF_SCHED) __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         // ---- mask (boundary tiles only), online softmax on raw scores ----
@@ -542,7 +524,7 @@ __global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefil
                 if (i + PF_V < 2 * C::DB) va[i % PF_V] = vread(i + PF_V);
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, pb),
                                                                 o[db], 0, 0, 0);
-                if (PF_SCHED) __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         // everyone is done with this stage before it is refilled (8-bit caches:
@@ -602,25 +584,15 @@ __global__ __launch_bounds__(NWV * 64, PA_PREFILL_MINW(D) * 4 / NWV) void prefil
 // D = 256 on large batches 8 (one workgroup per CU, each K/V tile in LDS
 // serving 256 rows): 5% faster on long uniform prompts, but 3-4% slower on
 // ragged batches of a few hundred workgroups, whose critical path the larger
-// q-tiles lengthen.  The switch is at PA_PREFILL_WIDE_ITEMS work items of
-// 8-wave size (4 per CU on 256 CUs).
-#ifndef PA_PREFILL_WIDE_ITEMS
-#define PA_PREFILL_WIDE_ITEMS 1024
-#endif
-#ifndef PA_PREFILL_N
-#define PA_PREFILL_N(D) ((D) >= 256 ? 32 : 64)
-#endif
-#ifndef PA_PREFILL_NST
-#define PA_PREFILL_NST(D) 2
-#endif
-// The 8-wave form (one workgroup per CU) has the LDS for a third stage.
-#ifndef PA_PREFILL_NST_WIDE
-#define PA_PREFILL_NST_WIDE 3
-#endif
+// q-tiles lengthen.  The switch is at PREFILL_WIDE_ITEMS work items of
+// 8-wave size (4 per CU on 256 CUs).  The 8-wave form (one workgroup per
+// CU) has the LDS for a third stage.
+constexpr int PREFILL_WIDE_ITEMS = 1024;
+constexpr int prefill_n(int D) { return D >= 256 ? 32 : 64; }
 
 template <int D, bool KV8, int NWV>
 hipError_t launch_dw(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
-    constexpr int N = PA_PREFILL_N(D), NST = NWV == 8 ? PA_PREFILL_NST_WIDE : PA_PREFILL_NST(D);
+    constexpr int N = prefill_n(D), NST = NWV == 8 ? 3 : 2;
     const int TPW = 32 / p.group;
     const int BQ = NWV * TPW;
     AttnParams q = p;
@@ -628,7 +600,7 @@ hipError_t launch_dw(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
     q.grid_parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
     const int64_t items = (int64_t)q.grid_tiles * p.hkv * q.grid_parts;
     if (items > INT32_MAX - 4096) return hipErrorInvalidConfiguration;
-    const int64_t unit = XCD_CHUNK > 0 ? 8 * XCD_CHUNK : 1;
+    const int64_t unit = 8 * XCD_CHUNK;
     const int blocks = (int)((items + unit - 1) / unit * unit);
     if (li) *li = LaunchInfo{{blocks, 1, 1}, NWV * 64, {N, NST, BQ}, 0};
     hipLaunchKernelGGL((prefill_kernel<D, N, NST, KV8, NWV>), dim3(blocks), dim3(NWV * 64), 0,
@@ -642,7 +614,7 @@ hipError_t launch_d(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
         const int64_t bq8 = 8 * (32 / p.group);
         const int64_t parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
         const int64_t items8 = (p.total_q / bq8 + p.num_seqs) * p.hkv * parts;
-        if (items8 >= PA_PREFILL_WIDE_ITEMS) return launch_dw<D, KV8, 8>(p, stream, li);
+        if (items8 >= PREFILL_WIDE_ITEMS) return launch_dw<D, KV8, 8>(p, stream, li);
     }
     return launch_dw<D, KV8, 4>(p, stream, li);
 }

@@ -50,14 +50,42 @@ def test_mixed_chunked_prefill(variant):
 def test_spec_verify_with_cache_write():
     """Verify windows of 1..5 tokens and two 512-token chunks over 1k..8k
     contexts, 144-token blocks seen as 9x16-token pages, new K/V written by
-    pa_reshape_and_cache first; every row, unsplit and split."""
+    pa_reshape_and_cache first; every row, unsplit and split (1,024 is the
+    partition the benchmark times this batch at)."""
+    import paged_varlen_attention_amd as pa
     w = W.spec_verify_bf16()
     ref = oracle.run_workload(w)  # oracle: cache write then attention on 144-token blocks
     b = to_device(w)              # GPU: cache write, 9x16 view, expanded block table
-    for P in (0, 512):
-        out = run_gpu(b, P)
+    assert b.block_tables.shape[1] == w.block_tables.shape[1] * 9
+    for P in (0, 512, 1024):
+        out = run_gpu(b, P, reduce=False)
+        rec = pa.last_dispatch()
+        assert rec["path"] == "tiled" and rec["partition_size"] == P, rec
+        if P:
+            out = run_gpu(b, P)
         torch.cuda.synchronize()
         assert_close(out, ref, torch.bfloat16, f"spec verify P={P}")
+
+
+def test_uniform_prefill_workload():
+    """The benchmark's uniform prefill batch itself (8 x 4,096 new tokens over
+    4,096 cached ones, 16/2/256): it takes the 8-wave, 3-stage form of the
+    tiled kernel, and sampled rows -- every request's first and last tokens
+    among them -- match the oracle."""
+    import paged_varlen_attention_amd as pa
+    from gpu_helpers import sample_rows
+    w = W.prefill_uniform_bf16()
+    rows = sample_rows(w, 96, seed=7)
+    ends = w.cu_seqlens_q[1:].tolist()
+    rows = sorted(set(rows) | {(t - 1, h) for t in ends for h in (0, 9, 15)})
+    ref = oracle.run_workload(w, rows=rows)
+    b = to_device(w)
+    out = run_gpu(b, 0)
+    rec = pa.last_dispatch()
+    assert rec["path"] == "tiled" and rec["block"] == 512 and rec["tile"][1] == 3, rec
+    torch.cuda.synchronize()
+    got = torch.stack([out[t, h] for t, h in rows])
+    assert_close(got, ref, torch.bfloat16, "uniform prefill (sampled rows)")
 
 
 def test_causal_edges():

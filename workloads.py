@@ -273,6 +273,20 @@ def spec_verify_bf16(seed: int = 5, lo: int = 1024, hi: int = 8192, num_blocks: 
                  description="16 req: 14 x 1-5 tok + 2 x 512 chunk, ctx U[1k,8k], 16/2/128, 144->9x16")
 
 
+def prefill_uniform_bf16(seed: int = 7, num_seqs: int = 8, q_len: int = 4096,
+                         ctx: int = 4096) -> Workload:
+    """8 prompt chunks of 4,096 new tokens over 4,096 cached ones each, the
+    mixed batches' head shape (Hq=16 Hkv=2 D=256, 16-token pages), bf16: a
+    long uniform batch that shows the tiled kernel's steady state apart from
+    the load imbalance of short ragged batches."""
+    seq = q_len + ctx
+    return build("prefill_uniform_bf16", seed=seed, q_lens=[q_len] * num_seqs,
+                 seq_lens=[seq] * num_seqs, num_q_heads=16, num_kv_heads=2, head_dim=256,
+                 block_size=16, num_blocks=num_seqs * seq // 16 + 8, dtype=torch.bfloat16,
+                 partition_sizes=[0],
+                 description=f"{num_seqs} x {q_len}-token prompt chunks over {ctx} cached tokens, 16/2/256")
+
+
 def last_token_rows(w: Workload):
     """(key, value, slot_mapping) of each request's newest token, read back
     from the cache: writing them again with reshape_and_cache is the cache
@@ -298,6 +312,7 @@ CONFIGS = {
     "mixed_prefill_bf16_B": lambda seed=3: mixed_prefill_bf16(seed, "B"),
     "long_decode_bf16": long_decode_bf16,
     "spec_verify_bf16": spec_verify_bf16,
+    "prefill_uniform_bf16": prefill_uniform_bf16,
 }
 
 
