@@ -420,6 +420,8 @@ def main():
     ap.add_argument("--secondary", dest="secondary", action="store_true", default=True)
     ap.add_argument("--no-secondary", dest="secondary", action="store_false")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--workloads", default="",
+                    help="comma-separated secondary workloads to run (default: all)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -494,11 +496,18 @@ def main():
     }
 
     # ---------------- secondary workloads ----------------
+    only = {x for x in args.workloads.split(",") if x}
+
+    def wanted(name):
+        return not only or name in only
+
     if args.secondary:
         sec_out = {}
         steps2 = max(10, args.steps // 2)
         w4 = W.long_decode_bf16()
         for P4 in (256, 512):
+            if not wanted(f"long_decode_bf16_P{P4}"):
+                continue
             s4, k4, s4w, _ = measure(w4, P4, steps2, 5, 2, device)
             b4 = w4.algorithmic_bytes()
             sec_out[f"long_decode_bf16_P{P4}"] = {
@@ -514,6 +523,8 @@ def main():
         # batches with half the KV bytes
         for name8, w8, P8 in (("gqa_decode_fp8kv_P512", w, 512), ("gqa_decode_fp8kv_P1024", w, 1024),
                               ("long_decode_fp8kv_P1024", w4, 1024)):
+            if not wanted(name8):
+                continue
             s8, k8, s8w, _ = measure(w8, P8, steps2, 5, args.copies, device, kv8=True)
             b8 = step_bytes(w8, True, kv_elt_bytes=1)
             a8 = w8.algorithmic_bytes(1)
@@ -536,6 +547,8 @@ def main():
                          ("spec_verify_bf16", 1024), ("prefill_uniform_bf16", 0),
                          ("mixed_prefill_fp8kv_B", 0), ("prefill_uniform_fp8kv", 0)):
             kv8 = "fp8kv" in name
+            if not wanted(name):
+                continue
             try:
                 w3 = W.CONFIGS[name.replace("fp8kv", "bf16")]()
                 s3, k3, s3w, _ = measure(w3, P3, steps2, 5, 2, device, kv8=kv8)
@@ -558,8 +571,9 @@ def main():
                 "step_ms_percentiles": k3["step_ms_percentiles"],
                 "warm_ms_per_step": round(s3w * 1e3, 5)}
             log(f"{name}: {sec_out[name]}")
-        sec_out["kv_block_offload_bf16"] = block_offload(device)
-        log(f"kv block offload: {sec_out['kv_block_offload_bf16']}")
+        if wanted("kv_block_offload_bf16"):
+            sec_out["kv_block_offload_bf16"] = block_offload(device)
+            log(f"kv block offload: {sec_out['kv_block_offload_bf16']}")
         result["secondary"] = sec_out
 
     if args.copy_calibration:
