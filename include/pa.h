@@ -209,6 +209,40 @@ int pa_varlen_attention(void *out, const void *q, const void *key_cache, const v
                         int32_t max_partitions, void *stream);
 
 /*
+ * pa_varlen_attention_noalloc -- pa_varlen_attention and, for
+ * partition_size > 0, pa_split_kv_reduce in one call, with the split-KV
+ * partials held in the library's own static device scratch instead of caller
+ * buffers.  For callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * call allocates nothing and calls no allocating routine; the caller passes
+ * the inputs and `out` only, and `out` receives every row.
+ *   Scratch: PA_NOALLOC_SCRATCH_BYTES of device memory per GPU, reserved
+ *   when the library is loaded and held until the process ends.  A call with
+ *   P = partition_size > 0 needs the partials of
+ *   n = ceil(max_seq_len / P) partitions, total_q * num_q_heads * n * (D + 2)
+ *   float32 values (each of the three arrays 256-byte aligned); a call that
+ *   needs more returns PA_EWORKSPACE before anything is enqueued.
+ *   Every call on one GPU shares that GPU's scratch, which keeps the last
+ *   call's contents: calls that overlap on one GPU (other streams, other
+ *   threads) race and must be serialised by the caller.  No part of the
+ *   scratch needs to start at zero: every partial the reduce reads is written
+ *   by the attention launch of the same call.
+ * Other arguments, the result and the errors are those of
+ * pa_varlen_attention.  The dispatch record is the attention launch's.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int pa_varlen_attention_noalloc(void *out, const void *q, const void *key_cache,
+                                const void *value_cache, const int32_t *cu_seqlens_q,
+                                const int32_t *seq_lens, const int32_t *block_tables,
+                                int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                int32_t max_seq_len, int32_t max_blocks_per_seq,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t num_blocks, int32_t block_size, float scale,
+                                const float *sinks, int32_t dtype, int32_t kv_dtype,
+                                const float *k_scale, const float *v_scale,
+                                int32_t partition_size, void *stream);
+
+/*
  * pa_split_kv_reduce -- merge split-KV partials (kernel walkthrough, GQA decode
  * tip 4: the shared reducer).  For every row (t, h) with n >= 2 partitions
  * (n as above): M = max_k max_logits[k], w_k = exp_sums[k] * 2^(max_logits[k] - M),

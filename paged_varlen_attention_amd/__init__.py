@@ -43,6 +43,8 @@ def _load() -> ctypes.CDLL:
     lib.pa_varlen_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, P,
                                         I, I, P, P, I, P, P, P, I, P]
     lib.pa_split_kv_reduce.argtypes = [P, P, P, P, P, P, I, I, I, I, P, I, I, I, P]
+    lib.pa_varlen_attention_noalloc.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I,
+                                                F, P, I, I, P, P, I, P]
     lib.pa_pick_partition_size.argtypes = [P, I, I, I]
     lib.pa_pick_partition_size.restype = ctypes.c_int32
     lib.pa_partials_bytes.argtypes = [I, I, I, I, ctypes.POINTER(ctypes.c_size_t),
@@ -52,6 +54,7 @@ def _load() -> ctypes.CDLL:
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     for f in ("pa_reshape_and_cache", "pa_expand_block_tables", "pa_varlen_attention",
+              "pa_varlen_attention_noalloc",
               "pa_split_kv_reduce", "pa_partials_bytes", "pa_abi_version", "pa_last_dispatch",
               "pa_copy_blocks"):
         getattr(lib, f).restype = ctypes.c_int
@@ -263,6 +266,47 @@ def varlen_attention(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torc
     _check("pa_varlen_attention", st)
     if partition_size and reduce:
         split_kv_reduce(out, partials, cu_seqlens_q, seq_lens, partition_size, sinks=sinks)
+    return out
+
+
+# Bytes of device scratch behind varlen_attention_noalloc (one copy per GPU).
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def varlen_attention_noalloc(q: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                             cu_seqlens_q: torch.Tensor, seq_lens: torch.Tensor,
+                             block_tables: torch.Tensor, out: torch.Tensor, *, max_q_len: int,
+                             max_seq_len: int, scale: float, partition_size: int = 0,
+                             sinks: Optional[torch.Tensor] = None,
+                             k_scale: Optional[torch.Tensor] = None,
+                             v_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """pa_varlen_attention_noalloc: attention and (partition_size > 0) the
+    split-KV reduce in one call, the partials in the library's static device
+    scratch; nothing is allocated, ``out`` (same shape and dtype as q) is the
+    caller's.  Calls that overlap on one GPU share that scratch and race."""
+    TQ, hq, d = q.shape
+    nb, bs, hkv, cd = key_cache.shape
+    if cd != d or value_cache.shape != key_cache.shape or out.shape != q.shape:
+        raise ValueError("shape mismatch")
+    B = seq_lens.shape[0]
+    if cu_seqlens_q.shape != (B + 1,) or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("metadata shape mismatch")
+    if sinks is not None and sinks.shape != (hq,):
+        raise ValueError("sinks must be [num_q_heads]")
+    if value_cache.dtype != key_cache.dtype:
+        raise TypeError("key_cache and value_cache differ in dtype")
+    dev = q.device
+    kv = _kv_code(key_cache, q.dtype)
+    ks, vs = _scales(k_scale, v_scale, kv, hkv, dev)
+    st = lib.pa_varlen_attention_noalloc(
+        _dev(out, "out", q.dtype, dev), _dev(q, "q", device=dev),
+        _dev(key_cache, "key_cache", device=dev), _dev(value_cache, "value_cache", device=dev),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev), _dev(seq_lens, "seq_lens", torch.int32, dev),
+        _dev(block_tables, "block_tables", torch.int32, dev), B, TQ, int(max_q_len),
+        int(max_seq_len), block_tables.shape[1], hq, hkv, d, nb, bs, float(scale),
+        _dev(sinks, "sinks", torch.float32, dev), _dtype_code(q.dtype), kv, ks, vs,
+        int(partition_size), _stream(dev))
+    _check("pa_varlen_attention_noalloc", st)
     return out
 
 

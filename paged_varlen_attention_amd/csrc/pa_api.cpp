@@ -351,6 +351,58 @@ int pa_split_kv_reduce(void *out, const float *tmp_out, const float *max_logits,
     return rec.status;
 }
 
+int pa_varlen_attention_noalloc(void *out, const void *q, const void *key_cache,
+                                const void *value_cache, const int32_t *cu_seqlens_q,
+                                const int32_t *seq_lens, const int32_t *block_tables,
+                                int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                int32_t max_seq_len, int32_t max_blocks_per_seq,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t num_blocks, int32_t block_size, float scale,
+                                const float *sinks, int32_t dtype, int32_t kv_dtype,
+                                const float *k_scale, const float *v_scale,
+                                int32_t partition_size, void *stream) {
+    pa_dispatch_info rec{};
+    rec.status = [&]() -> int {
+        try {
+            float *tmp = nullptr, *ml = nullptr, *es = nullptr;
+            int32_t parts = 0;
+            if (partition_size != 0 && !split_disabled_by_env()) {
+                // Size the partials before anything is enqueued; the checks
+                // pa_varlen_attention makes itself come first.
+                if (!partition_ok(partition_size)) return PA_EUNSUPPORTED;
+                if (total_q < 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len < 0)
+                    return PA_EINVAL;
+                if (num_q_heads > GRID_YZ_MAX) return PA_EUNSUPPORTED;
+                parts = (int32_t)(((int64_t)max_seq_len + partition_size - 1) / partition_size);
+                if (parts < 1) parts = 1;
+                const uint64_t rows = (uint64_t)total_q * num_q_heads * parts;
+                auto up = [](uint64_t b) { return (b + 255) & ~(uint64_t)255; };
+                const uint64_t tmp_b = up(rows * head_dim * 4), st_b = up(rows * 4);
+                if (tmp_b + 2 * st_b > PA_NOALLOC_SCRATCH_BYTES) return PA_EWORKSPACE;
+                void *base = nullptr;
+                if (pa::noalloc_scratch(&base) != hipSuccess || !base) return PA_EHIP;
+                tmp = static_cast<float *>(base);
+                ml = reinterpret_cast<float *>(static_cast<char *>(base) + tmp_b);
+                es = reinterpret_cast<float *>(static_cast<char *>(base) + tmp_b + st_b);
+            }
+            const int st = varlen_attention_impl(
+                rec, out, q, key_cache, value_cache, cu_seqlens_q, seq_lens, block_tables,
+                num_seqs, total_q, max_q_len, max_seq_len, max_blocks_per_seq, num_q_heads,
+                num_kv_heads, head_dim, num_blocks, block_size, scale, sinks, dtype, kv_dtype,
+                k_scale, v_scale, parts ? partition_size : 0, tmp, ml, es, parts, stream);
+            if (st != PA_OK || !parts || total_q == 0 || num_seqs == 0) return st;
+            pa_dispatch_info rrec{};
+            return split_kv_reduce_impl(rrec, out, tmp, ml, es, cu_seqlens_q, seq_lens, num_seqs,
+                                        total_q, num_q_heads, head_dim, sinks, partition_size,
+                                        parts, dtype, stream);
+        } catch (...) {
+            return PA_EHIP;
+        }
+    }();
+    g_last = rec;
+    return rec.status;
+}
+
 int pa_last_dispatch(pa_dispatch_info *info) {
     if (!info) return PA_EINVAL;
     *info = g_last;

@@ -100,6 +100,11 @@ hipError_t launch_decode_mfma(const AttnParams &p, hipStream_t stream, LaunchInf
 hipError_t launch_prefill(const AttnParams &p, hipStream_t stream, LaunchInfo *li);
 hipError_t launch_reduce(const ReduceParams &p, hipStream_t stream, LaunchInfo *li);
 
+// Device address of the calling thread's current device's copy of the
+// library's static scratch (PA_NOALLOC_SCRATCH_BYTES bytes, 256-byte aligned),
+// looked up once per device.
+hipError_t noalloc_scratch(void **ptr);
+
 // Whether a decode instantiation exists for this geometry.
 bool decode_supported(int dtype, int head_dim, int group);
 bool decode_kv8_supported(int head_dim, int group);
