@@ -85,8 +85,10 @@ enum {
 #define PA_MAX_GROUP 8          /* num_q_heads / num_kv_heads */
 #define PA_MAX_SEQS 65535       /* requests per call */
 #define PA_MAX_PARTITION 8192  /* largest partition_size accepted */
-#define PA_SPLIT_FILL_NUM 5     /* the partition policy aims for 5/8 of a workgroup per CU */
-#define PA_SPLIT_FILL_DEN 8
+#define PA_SPLIT_FILL_NUM 9     /* the partition policy aims for 9/16 of a workgroup per CU */
+#define PA_SPLIT_FILL_DEN 16
+#define PA_SPLIT_BALANCE_NUM 3  /* ... with no item longer than 3/2 of the mean */
+#define PA_SPLIT_BALANCE_DEN 2
 
 /*
  * pa_reshape_and_cache -- write new K/V rows into the paged cache
@@ -262,22 +264,32 @@ int pa_split_kv_reduce(void *out, const float *tmp_out, const float *max_logits,
 /*
  * pa_pick_partition_size -- host-only partition policy for decode batches.
  * The pages' rule (kernel walkthrough, "dispatch layer") is a work budget
- * proportional to the number of GPU cores with 512-token partitions tried
- * before 256.  Calibrated on MI355X (decode batches of 1..256 requests,
- * 1K..64K keys, two head shapes), the best partition is the LARGEST one that
- * still gives about one workgroup per CU, because every partition pays a
- * fixed start-up and merge cost.  With
- *   budget  = num_cus * PA_SPLIT_FILL_NUM / PA_SPLIT_FILL_DEN,
- *   unsplit = num_kv_heads * num_seqs    (workgroups without a split),
- *   W(P)    = num_kv_heads * sum_r ceil(seq_lens[r] / P):
- * returns 0 if no sequence is longer than 256 or unsplit >= budget, else the
- * largest P in {256, 512, ..., PA_MAX_PARTITION} (powers of two) with
- * W(P) >= budget, else 256.
- * host_seq_lens is a HOST array.  num_cus <= 0 asks the current device.
- * Returns -1 on bad arguments.  Enqueues nothing.
+ * proportional to the number of GPU cores, larger partitions tried first
+ * (512 before 256).  This rule keeps that shape for the decode kernels the
+ * launch would route to (whole-row or per KV head, which depends on the head
+ * shape, dtype and partition count) and was calibrated on MI355X over decode
+ * batches of 1..256 requests, 1K..64K keys and three head shapes (attention +
+ * reduce as HIP graphs over cold pools): every partition pays a start-up, a
+ * merge and a reduce share, so the largest size that still fills the GPU with
+ * evenly sized workgroups wins.  With
+ *   budget = num_cus * PA_SPLIT_FILL_NUM / PA_SPLIT_FILL_DEN,
+ *   items(P) = sum_r ceil(seq_lens[r] / P)  (P = 0: one per request),
+ *   workgroups(P) = items(P) for the whole-row kernel, items(P) * num_kv_heads
+ *                   for the per-head kernel,
+ * a size qualifies when workgroups(P) >= budget and the longest item streams
+ * at most PA_SPLIT_BALANCE_NUM / PA_SPLIT_BALANCE_DEN times the mean key
+ * count of an item.  Sizes are tried in the order 0, 8192, 4096, ..., 512
+ * (sizes of at least twice the longest sequence skipped), those that route to
+ * the whole-row kernel first where the head shape allows it; the first that
+ * qualifies is returned, else 256.  0 when no sequence is longer than 256.
+ * host_seq_lens is a HOST array.  dtype / kv_dtype as in
+ * pa_varlen_attention.  num_cus <= 0 asks the current device.  Returns -1 on
+ * bad arguments.  Enqueues nothing.
  */
 int32_t pa_pick_partition_size(const int32_t *host_seq_lens, int32_t num_seqs,
-                               int32_t num_kv_heads, int32_t num_cus);
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t dtype, int32_t kv_dtype,
+                               int32_t num_cus);
 
 /*
  * Dispatch record: what the calling thread's last pa_varlen_attention or

@@ -34,7 +34,7 @@ class PAError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m paged_varlen_attention_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python paged_varlen_attention_amd/build.py` "
             "(there is no fallback implementation)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
@@ -45,7 +45,7 @@ def _load() -> ctypes.CDLL:
     lib.pa_split_kv_reduce.argtypes = [P, P, P, P, P, P, I, I, I, I, P, I, I, I, P]
     lib.pa_varlen_attention_noalloc.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I,
                                                 F, P, I, I, P, P, I, P]
-    lib.pa_pick_partition_size.argtypes = [P, I, I, I]
+    lib.pa_pick_partition_size.argtypes = [P, I, I, I, I, I, I, I, I]
     lib.pa_pick_partition_size.restype = ctypes.c_int32
     lib.pa_partials_bytes.argtypes = [I, I, I, I, ctypes.POINTER(ctypes.c_size_t),
                                       ctypes.POINTER(ctypes.c_size_t)]
@@ -351,12 +351,17 @@ def last_dispatch() -> dict:
             "grid": tuple(info.grid), "block": info.block, "tile": tuple(info.tile)}
 
 
-def pick_partition_size(seq_lens: Sequence[int], num_kv_heads: int, num_cus: int = 0) -> int:
-    """Host-side partition policy (0 or a power of two from 256 to 8192);
-    seq_lens is a host sequence."""
+def pick_partition_size(seq_lens: Sequence[int], num_q_heads: int, num_kv_heads: int,
+                        head_dim: int, block_size: int = 16, dtype: torch.dtype = torch.bfloat16,
+                        kv8: bool = False, num_cus: int = 0) -> int:
+    """Host-side partition policy for a decode batch (0 or a power of two from
+    256 to 8192), for the kernel the launch routes to; seq_lens is a host
+    sequence, kv8 selects 8-bit E4M3 caches."""
     arr = (ctypes.c_int32 * len(seq_lens))(*[int(s) for s in seq_lens])
-    r = lib.pa_pick_partition_size(ctypes.cast(arr, ctypes.c_void_p), len(seq_lens), num_kv_heads,
-                                   num_cus)
+    dt = _dtype_code(dtype)
+    r = lib.pa_pick_partition_size(ctypes.cast(arr, ctypes.c_void_p), len(seq_lens), num_q_heads,
+                                   num_kv_heads, head_dim, block_size, dt,
+                                   PA_FP8_E4M3 if kv8 else dt, num_cus)
     if r < 0:
         raise ValueError("pick_partition_size: bad arguments")
     return int(r)

@@ -1,6 +1,6 @@
 """Build libpa.so (the HIP library behind include/pa.h) for gfx950.
 
-Usage: python -m paged_varlen_attention_amd.build [-j N]
+Usage: python paged_varlen_attention_amd/build.py [-j N]   (or __graft_entry__.build())
 Sources are compiled in parallel into _build/ next to this file and linked
 into libpa.so inside the package.  Packed-fp32 instructions are disabled for
 all device code.
@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpa.so")
 SOURCES = ["pa_api.cpp", "cache_write.hip", "decode.hip", "decode_mfma.hip", "decode_rows.hip", "reduce.hip",
-           "prefill.hip", "block_copy.hip", "noalloc.hip"]
+           "prefill.hip", "prefill_wide.hip", "block_copy.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -452,9 +452,14 @@ int pa_copy_blocks(void *dst_key, void *dst_value, const void *src_key, const vo
 }
 
 int32_t pa_pick_partition_size(const int32_t *host_seq_lens, int32_t num_seqs,
-                               int32_t num_kv_heads, int32_t num_cus) {
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t dtype, int32_t kv_dtype,
+                               int32_t num_cus) {
     try {
-        if (num_seqs < 0 || num_kv_heads <= 0 || (num_seqs > 0 && !host_seq_lens)) return -1;
+        if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+            num_q_heads % num_kv_heads != 0 || block_size <= 0 || !elt_bytes(dtype) ||
+            (kv_dtype != dtype && kv_dtype != PA_FP8_E4M3) || (num_seqs > 0 && !host_seq_lens))
+            return -1;
         if (num_cus <= 0) {
             int dev = 0;
             if (hipGetDevice(&dev) != hipSuccess) return -1;
@@ -467,17 +472,56 @@ int32_t pa_pick_partition_size(const int32_t *host_seq_lens, int32_t num_seqs,
             if (host_seq_lens[r] < 0) return -1;
             max_len = host_seq_lens[r] > max_len ? host_seq_lens[r] : max_len;
         }
-        // Workgroups an unsplit launch already has, and the budget: about one
-        // workgroup per CU (calibrated; every partition costs a start-up and a
-        // merge, so the largest partition that fills the GPU wins).
-        const int64_t unsplit = (int64_t)num_kv_heads * num_seqs;
+        if (max_len <= 256) return 0;
+        // The decode kernel each partition size routes to (the same rule the
+        // launch applies): whole-row (one workgroup per request and
+        // partition) or per KV head (one per KV head, request and partition).
+        pa::AttnParams p{};
+        p.num_seqs = num_seqs;
+        p.max_seq_len = max_len;
+        p.hq = num_q_heads;
+        p.hkv = num_kv_heads;
+        p.group = num_q_heads / num_kv_heads;
+        p.head_dim = head_dim;
+        p.block_size = block_size;
+        p.dtype = dtype;
+        p.kv8 = kv_dtype == PA_FP8_E4M3;
+        auto rows_kernel = [&](int32_t P) {
+            p.partition = P;
+            return pa::decode_rows_supported(p);
+        };
         const int64_t budget = (int64_t)num_cus * PA_SPLIT_FILL_NUM / PA_SPLIT_FILL_DEN;
-        if (max_len <= 256 || unsplit >= budget) return 0;
-        for (int32_t P = PA_MAX_PARTITION; P > 256; P /= 2) {
-            int64_t w = 0;
-            for (int32_t r = 0; r < num_seqs; ++r) w += (host_seq_lens[r] + P - 1) / P;
-            if ((int64_t)num_kv_heads * w >= budget) return P;
-        }
+        // A partition size qualifies when its launch has at least `budget`
+        // workgroups and no workgroup streams more than 3/2 of the mean key
+        // count (unequal items leave CUs idle while the longest finishes).
+        auto qualifies = [&](int32_t P) {
+            int64_t items = 0, keys = 0;
+            int32_t longest = 0;
+            for (int32_t r = 0; r < num_seqs; ++r) {
+                const int32_t L = host_seq_lens[r];
+                if (L <= 0) continue;
+                items += P ? (L + P - 1) / P : 1;
+                keys += L;
+                const int32_t lk = P && L > P ? P : L;
+                longest = lk > longest ? lk : longest;
+            }
+            if (!items) return false;
+            const int64_t wgs = rows_kernel(P) ? items : items * num_kv_heads;
+            return wgs >= budget && (int64_t)longest * items * PA_SPLIT_BALANCE_DEN <=
+                                        keys * PA_SPLIT_BALANCE_NUM;
+        };
+        static const int32_t order[] = {0, 8192, 4096, 2048, 1024, 512};
+        // Whole-row launches stream whole cache rows, faster per byte than
+        // per-head slices: where the head shape allows them, the sizes that
+        // route there are tried first.
+        bool any_rows = false;
+        for (int32_t P : order) any_rows = any_rows || ((P == 0 || P < 2 * max_len) && rows_kernel(P));
+        for (int pass = any_rows ? 0 : 1; pass < 2; ++pass)
+            for (int32_t P : order) {
+                if (P && P >= 2 * max_len) continue;  // one partition per request: as P = 0
+                if (pass == 0 && !rows_kernel(P)) continue;
+                if (qualifies(P)) return P;
+            }
         return 256;
     } catch (...) {
         return -1;

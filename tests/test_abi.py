@@ -163,21 +163,35 @@ def test_partials_bytes():
 
 
 def test_partition_policy():
-    """Host-only policy with an explicit CU count (no device query)."""
+    """Host-only policy with an explicit CU count (no device query): budget
+    256 * 9/16 = 144 workgroups, items no longer than 3/2 of the mean; the
+    whole-row kernel takes 32/8/128 bf16 batches with >= 128 (request,
+    partition) items, the per-head kernel the rest (workgroups x Hkv)."""
+    import workloads as W
     import paged_varlen_attention_amd as pa
-    cus = 256                                                         # budget 160 workgroups
-    assert pa.pick_partition_size([100] * 4, 8, cus) == 0             # nothing longer than 256
-    assert pa.pick_partition_size([4000] * 20, 8, cus) == 0           # 160 unsplit >= 160
-    assert pa.pick_partition_size([4000] * 16, 8, cus) == 2048        # 8*16*2 = 256; 4096 gives 128
-    assert pa.pick_partition_size([32768] * 4, 4, cus) == 2048        # 4*4*16 = 256; 4096 gives 128
-    assert pa.pick_partition_size([65536], 8, cus) == 2048            # 8*32 = 256; 4096 gives 128
-    assert pa.pick_partition_size([40960], 8, cus) == 2048            # 8*20 = 160 reaches the budget
-    assert pa.pick_partition_size([30720], 8, cus) == 1024            # 8*30 = 240; 2048 gives 120
-    assert pa.pick_partition_size([700] * 4, 4, cus) == 256           # nothing fills: smallest
-    assert pa.pick_partition_size([8192] * 2, 8, cus) == 512          # 8*2*16 = 256; 1024 gives 128
-    assert pa.pick_partition_size([3000] * 512, 8, cus) == 0          # 4096 unsplit workgroups
+    cus = 256
+    pick = lambda sl, hq, hkv, d, **kw: pa.pick_partition_size(sl, hq, hkv, d, num_cus=cus, **kw)  # noqa: E731
+    assert pick([100] * 4, 32, 8, 128) == 0                  # nothing longer than 256
+    # the GQA decode batch: 512 routes 32 x 8 items to the whole-row kernel,
+    # 156 of them non-empty (>= 144), the longest 512 <= 1.5 x 463 (mean);
+    # 1024 gives 86 and larger sizes route to the per-head kernel (tried later)
+    sl2 = W.gqa_decode_bf16().seq_lens.tolist()
+    assert sum(-(-s // 512) for s in sl2) == 156 and sum(-(-s // 1024) for s in sl2) == 86
+    assert pick(sl2, 32, 8, 128) == 512
+    # the 32K-token decode (24/4/256: per-head kernel only): 2048 gives
+    # 4 x 16 x 4 = 256 workgroups; 4096 gives 128 < 144
+    assert pick([32768] * 4, 24, 4, 256) == 2048
+    # 256 requests of 4096 keys: unsplit is 256 whole-row workgroups, balanced
+    assert pick([4096] * 256, 32, 8, 128) == 0
+    # one long request among short ones: no size both fills and balances
+    assert pick([512] * 31 + [8000], 32, 8, 128) == 256
+    # 8-bit caches (per-head kernel): 16 x 4000 keys -> 2048 gives 16 x 2 x 8 = 256
+    assert pick([4000] * 16, 32, 8, 128, kv8=True) == 2048
+    assert pick([4000] * 16, 32, 8, 128, kv8=True) == 2048
     with pytest.raises(ValueError):
-        pa.pick_partition_size([-5], 1, cus)
+        pick([-5], 8, 1, 128)
+    with pytest.raises(ValueError):
+        pick([1000], 12, 8, 128)                             # 12 % 8 != 0
 
 
 def test_dispatch_record_and_no_split_switch(monkeypatch):
