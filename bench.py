@@ -302,6 +302,45 @@ def pmc_traffic():
         return None
 
 
+PREFILL_SOURCES = ("paged_varlen_attention_amd/csrc/prefill.hip",
+                   "paged_varlen_attention_amd/csrc/pa_device.h",
+                   "paged_varlen_attention_amd/csrc/pa_internal.h")
+PREFILL_PMC_SUMMARY = "profiles/prefill_tiles_pmc.md"
+
+
+def _summary_fields(path, sources):
+    """The machine-readable `key: value` lines of a committed rocprofv3
+    summary, or None when the summary is missing or the kernel sources changed
+    since it was taken (sha256 over `sources`)."""
+    import hashlib
+    path = os.path.join(ROOT, path)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "|", " ")):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in sources:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return kv if kv.get("kernel_sources_sha256") == h.hexdigest() else None
+
+
+def prefill_counters(name):
+    """Counter-derived MFMA figures of the tile kernel on workload `name` from
+    the committed rocprofv3 summary: executed MFMA flops (every MFMA issued) per
+    trace-average duration against the bf16 peak, and MFMA-busy cycles per
+    SIMD per 2.4 GHz cycle; None if the kernel changed since."""
+    kv = _summary_fields(PREFILL_PMC_SUMMARY, PREFILL_SOURCES)
+    if not kv or f"{name}.frac_mfma_counters" not in kv:
+        return None
+    return {"frac_mfma_counters": float(kv[f"{name}.frac_mfma_counters"]),
+            "mfma_busy_frac": float(kv[f"{name}.mfma_busy_frac_2p4ghz"]),
+            "rocprof_trace_avg_ms": round(float(kv[f"{name}.trace_avg_us"]) * 1e-3, 5),
+            "source": PREFILL_PMC_SUMMARY}
+
+
 def block_offload(device, n_blocks=4096, reps=10):
     """pa_copy_blocks between the GPU cache and a pinned host pool: 4,096
     blocks of 16 tokens x 8 KV heads x 128 bf16 (32 KiB each for K and for V,
@@ -569,7 +608,8 @@ def main():
                 "GB/s": round(b3 / s3 / 1e9, 2),
                 "algorithmic_flops": f3, "algorithmic_bytes": b3,
                 "step_ms_percentiles": k3["step_ms_percentiles"],
-                "warm_ms_per_step": round(s3w * 1e3, 5)}
+                "warm_ms_per_step": round(s3w * 1e3, 5),
+                "counters": prefill_counters(name)}
             log(f"{name}: {sec_out[name]}")
         if wanted("kv_block_offload_bf16"):
             sec_out["kv_block_offload_bf16"] = block_offload(device)

@@ -1,0 +1,620 @@
+// prefill_tile.h -- the tiled bf16-MFMA attention kernel template shared by
+// prefill.hip (one 32-row block per wave) and prefill_wide.hip (two 32-row
+// blocks per wave sharing every K and V^T fragment; compiled separately so
+// its accumulators may live in AGPRs).  What it computes and how is
+// described at the top of prefill.hip.
+#pragma once
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units
+
+template <int D, int N_, int NST_, bool KV8_ = false, int NWV_ = 4, int RB_ = 1>
+struct PrefillCfg {
+    static constexpr bool KV8 = KV8_;             // caches hold E4M3 codes
+    static constexpr int NWV = NWV_;              // waves per workgroup (4 or 8)
+    static constexpr int RB = RB_;                // 32-row column blocks per wave (1 or 2)
+    static constexpr int NTH = NWV * 64;          // threads per workgroup
+    static constexpr int N = N_;                  // keys per tile
+    static constexpr int NST = NST_;              // LDS stages
+    static constexpr int NB = N / 32;             // 32-key blocks of S^T per tile
+    static constexpr int R = D * 2;               // bytes of a K/V row of one head
+    static constexpr int KS = D / 16;             // MFMA k-steps of QK^T
+    static constexpr int DB = D / 32;             // 32-row blocks of O^T
+    static constexpr int T_BYTES = N * R;         // one K (or V) tile
+    static constexpr int STAGE = 2 * T_BYTES;     // K tile, then V tile
+    static constexpr int PPR = R / 16;            // 16-byte pieces per row
+    static constexpr int KG = 8;                  // keys per group in the tile layout
+    static constexpr int GROUP_BYTES = KG * R;    // one key group: PPR pieces x KG keys
+    static constexpr int IPG = GROUP_BYTES / 1024;  // DMA instructions per key group
+    static constexpr int NI = T_BYTES / 1024;     // DMA instructions per tile
+    static constexpr int NI_W = NI / NWV;         // per wave, per tensor
+    // 8-bit caches: NST raw stages (K tile, then V tile, N*D bytes each) ahead
+    // of one bf16 stage the MFMAs read
+    static constexpr int RG = KV8 ? D : R;        // bytes of a cached K/V row of one head
+    static constexpr int RAW_T = N * D;           // one 8-bit tile
+    static constexpr int RAW_STAGE = 2 * RAW_T;
+    // 8-bit DMA: D >= 128 moves 8 keys x 128 bytes per instruction (16 bytes a
+    // lane); 64-byte rows (D = 64) move 4 whole rows per instruction (4 bytes
+    // a lane), landing row-major
+    static constexpr bool ROWS8 = D < 128;
+    static constexpr int DW8 = ROWS8 ? 4 : 16;
+    static constexpr int IPG8 = ROWS8 ? 1 : D / 128;  // instructions per 8-key group (D >= 128)
+    static constexpr int NI8_W = RAW_T / (64 * DW8) / NWV;  // per wave, per tensor, 8-bit
+    static constexpr int RAW_BYTES = KV8 ? NST * RAW_STAGE : 0;
+    static constexpr int LDS_BYTES = KV8 ? RAW_BYTES + STAGE : NST * STAGE;
+    static_assert(!KV8 || ((D == 64 || D >= 128) && RAW_T % (64 * DW8 * NWV) == 0),
+                  "8-bit tile shape");
+    static_assert(NI % NWV == 0, "tile split over the waves");
+    static_assert(RB == 1 || (RB == 2 && !KV8 && NWV == 4), "two row blocks: bf16 caches, 4 waves");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    static_assert(2 * NI_W * (NST - 1) < 64, "vmcnt range");
+    static_assert(2 * NI8_W * NST < 64, "vmcnt range");
+};
+
+// Tile layout in LDS (K and V alike).  Keys come in groups of KG = 8; a
+// group stores piece-major: piece p (16 bytes: elements 8p..8p+7) of its 8
+// keys is one 128-byte line.  Odd key groups store the two lines of each
+// piece pair swapped (stored piece s = p ^ (group & 1)), and the key slot is
+// XORed with 4 when bits 0 and 1 of s differ:
+//   off(key, p) = (key / 8) * 8R + s * 128 + ((key % 8) ^ 4 ((s ^ s / 2) & 1)) * 16.
+// The LDS serves 256 bytes (64 banks) a cycle, so every 16 lanes of a
+// ds_read_b128 and every 32 lanes of a ds_read_b64_tr_b16 must cover all
+// banks (the counters showed half of the LDS cycles lost to conflicts with
+// the plain piece-major layout; with this one there are none):
+// * S^T A operand (ds_read_b128): 8 consecutive lanes read 8 keys of one
+//   piece -- one line -- and the next 8 lanes the same piece of the next key
+//   group, which the swap puts on the other half of the banks; the address
+//   changes with the k-step by an immediate (two bases, by k-step parity).
+// * V^T A operand (ds_read_b64_tr_b16): 32 lanes read 4 keys x 4 adjacent
+//   pieces; the slot XOR puts the four 64-byte runs on four bank quarters.
+// * DMA: one global_load_lds_dwordx4 fills 1 KB = 8 pieces of one key group
+//   with 128 contiguous bytes of each key row (one 8-key group never spans
+//   two pages since pages hold a multiple of 8 keys); a lane's source offset
+//   inside the page is one of two values (even or odd key group).
+template <class C>
+__device__ __forceinline__ int tile_off(int key, int piece) {
+    const int sp = piece ^ ((key >> 3) & 1);  // odd key groups swap the lines of a piece pair
+    return (key >> 3) * C::GROUP_BYTES + sp * 128 + (((key & 7) ^ (((sp ^ (sp >> 1)) & 1) << 2)) << 4);
+}
+
+// Wait until the DMA of the tile `ahead` tiles before the newest one landed.
+template <int VM, int MAXA>
+__device__ __forceinline__ void wait_tiles_ahead(int ahead) {
+    if constexpr (MAXA > 0) {
+        if (ahead >= MAXA) {
+            wait_vmcnt<MAXA * VM>();
+            return;
+        }
+        wait_tiles_ahead<VM, MAXA - 1>(ahead);
+    } else {
+        wait_vmcnt<0>();
+    }
+}
+
+// Waves per SIMD the register budget is sized for: 2 (at most 256 registers
+// a lane; D = 256 keeps 192 of them for O^T and Q^T).
+constexpr int PREFILL_WAVES_PER_SIMD = 2;
+
+// LDS fragment reads in flight ahead of their MFMA (K for S^T, V^T for O^T).
+constexpr int prefill_pf(int D) { return D >= 256 ? 2 : 4; }
+// Consecutive work items kept on one XCD (its L2 serves their shared keys).
+constexpr int XCD_CHUNK = 8;
+
+template <int D, int N, int NST, bool KV8, int NWV, int RB>
+__global__ __launch_bounds__(NWV * 64, RB == 1 ? PREFILL_WAVES_PER_SIMD * 4 / NWV : 1) void prefill_kernel(
+    const AttnParams p) {
+    using C = PrefillCfg<D, N, NST, KV8, NWV, RB>;
+    constexpr int PF_K = prefill_pf(D), PF_V = prefill_pf(D);
+    __shared__ __attribute__((aligned(1024))) char lds[C::LDS_BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = p.group;
+    const int TPW = 32 * RB / G;  // tokens per wave
+    const int BQ = C::NWV * TPW;  // tokens per workgroup
+
+    // ---- which request and which q-tile (later virtual tiles first) ----
+    // ---- XCD-aware order.  Workgroups go to the 8 XCDs round-robin by launch
+    // index L; groups of XCD_CHUNK consecutive work items (q-tiles of one
+    // request and KV head, which read the same keys) are kept on one XCD so
+    // its L2 serves the repeats.  Work items are taken last-first: later
+    // q-tiles of a request see more keys.
+    const int n_items = p.grid_tiles * p.hkv * p.grid_parts;
+    int lam = blockIdx.x;
+    {
+        const int xcd = lam & 7, slot = lam >> 3;
+        lam = ((slot / XCD_CHUNK) * 8 + xcd) * XCD_CHUNK + slot % XCD_CHUNK;
+    }
+    if (lam >= n_items) return;
+    lam = n_items - 1 - lam;
+    const int x = lam % p.grid_tiles;
+    int r, tile;
+    if (p.num_seqs <= 64) {
+        // Up to 64 requests: the virtual tiles list the requests by key count,
+        // fewest first, each with exactly its own q-tiles, so that the
+        // last-first dispatch starts the requests with the most keys (and
+        // their longest q-tiles) first -- a decode row over a long context
+        // costs as much as a prompt's last q-tile and must not come last.
+        // Every wave computes the same table, one request per lane.
+        const int i = lane;
+        int ql = 0, sl = 0;
+        if (i < p.num_seqs) {
+            ql = p.cu_q[i + 1] - p.cu_q[i];
+            sl = p.seq_lens[i];
+        }
+        const int nt = ql > 0 ? (ql + BQ - 1) / BQ : 0;
+        int start = 0;
+        for (int j = 0; j < p.num_seqs; ++j) {
+            const int slj = __builtin_amdgcn_readlane(sl, j);
+            const int ntj = __builtin_amdgcn_readlane(nt, j);
+            start += (slj < sl || (slj == sl && j < i)) ? ntj : 0;
+        }
+        const uint64_t mine = __ballot(i < p.num_seqs && x >= start && x < start + nt);
+        if (!mine) return;  // surplus virtual tile
+        r = (int)__builtin_ctzll(mine);
+        tile = x - __builtin_amdgcn_readlane(start, r);
+    } else {
+        int lo = 0, hi = p.num_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.cu_q[mid] / BQ + mid <= x) lo = mid; else hi = mid - 1;
+        }
+        r = lo;
+        tile = x - (p.cu_q[r] / BQ + r);
+    }
+    const int q_begin = p.cu_q[r];
+    const int q_len = p.cu_q[r + 1] - q_begin;
+    const int j0 = tile * BQ;  // first token of the tile within the request
+    if (tile < 0 || j0 >= q_len) return;
+    const int seq_len = p.seq_lens[r];
+    const int ctx = seq_len - q_len;
+    const int kvh = (lam / p.grid_tiles) % p.hkv;
+    const int part = lam / (p.grid_tiles * p.hkv);
+    const int j_last = min(q_len, j0 + BQ) - 1;
+    // keys of this workgroup: the partition, cut at the last token's position
+    const int k_lo = p.partition ? part * p.partition : 0;
+    const int k_part_end = p.partition ? k_lo + p.partition : seq_len;
+    const int k_hi = min(k_part_end, ctx + j_last + 1);
+    if (k_lo >= k_hi) return;
+
+    // ---- this lane's query rows (column q of each of the RB S^T blocks):
+    // row i = 32 blk + q of the wave is token i / G, head i % G ----
+    const int q = lane & 31;
+    const int h = lane >> 5;
+    bool row_valid[RB];
+    int pos[RB], t_glob[RB], head[RB];
+#pragma unroll
+    for (int blk = 0; blk < RB; ++blk) {
+        const int ri = 32 * blk + q;
+        const int tl = min(wave * TPW + ri / G, j_last - j0);  // padding rows repeat the last token
+        row_valid[blk] = ri < TPW * G && j0 + wave * TPW + ri / G <= j_last;
+        const int jq = j0 + tl;       // token index within the request
+        pos[blk] = ctx + jq;          // absolute position: sees keys 0..pos
+        t_glob[blk] = q_begin + jq;
+        head[blk] = kvh * G + ri % G;
+    }
+
+    // Q^T B operand: 8 bf16 of d = 16*ks + 8*h .. +8 of this row, per k-step
+    // A negative scale is folded into Q (flipping bf16 sign bits is exact), so
+    // the running max can be taken on the raw scores and the scale applied
+    // inside the exponent; a zero scale becomes the smallest normal float,
+    // which leaves every visible weight exactly 1 and masked ones 0.
+    // (8-bit caches: S holds code units of K, so the head's K scale joins it)
+    const float sl2 =
+        fmaxf(fabsf(p.scale_log2) * (KV8 ? p.k_scale[kvh] : 1.f),
+              1.17549435e-38f);
+    bf16x8_t qb[RB][C::KS];
+    {
+        const uint32_t flip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
+#pragma unroll
+        for (int blk = 0; blk < RB; ++blk) {
+            const uint4 *qrow = reinterpret_cast<const uint4 *>(
+                reinterpret_cast<const uint16_t *>(p.q) + ((size_t)t_glob[blk] * p.hq + head[blk]) * D);
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) {
+                uint4 v = qrow[2 * ks + h];
+                v.x ^= flip; v.y ^= flip; v.z ^= flip; v.w ^= flip;
+                qb[blk][ks] = __builtin_bit_cast(bf16x8_t, v);
+            }
+        }
+    }
+
+    // ---- block-table window: lane i holds page (win_page + i) of the request ----
+    const int bs = p.block_size, lbs = p.log2_bs;
+    const int seq_pages = (seq_len + bs - 1) >> lbs;
+    const int32_t *bt_row = p.bt + (size_t)r * p.bt_stride;
+    auto load_window = [&](int page0) {
+        const int lp = page0 + lane;
+        int v = lp < seq_pages && lp < p.bt_stride ? bt_row[lp] : 0;
+        return v < 0 ? 0 : (v >= p.num_blocks ? p.num_blocks - 1 : v);
+    };
+    int win_page = k_lo >> lbs;
+    int btv = load_window(win_page);
+
+    const uint32_t row_stride = (uint32_t)p.hkv * C::RG;
+    const uint64_t page_bytes = (uint64_t)bs * row_stride;
+    const uint64_t head_off = (uint64_t)kvh * C::RG;
+    const char *kc = reinterpret_cast<const char *>(p.kc);
+    const int64_t v_minus_k = reinterpret_cast<const char *>(p.vc) - kc;
+
+    // DMA: this wave moves instructions c = wave*NI_W + i of each tile.
+    // Instruction c covers key group c / IPG, pieces 8*(c % IPG) .. +7; lane l
+    // brings piece 8*(c % IPG) + l/8 of key slot l%8 (its key is the slot
+    // XORed back, which is the same involution).
+    const uint32_t dma_voff =
+        (uint32_t)((lane & 7) ^ ((((lane >> 3) ^ (lane >> 4)) & 1) << 2)) * row_stride +
+        (uint32_t)(lane >> 3) * 16u;
+    // odd key groups: the line of stored piece 8q + l/8 holds piece 8q + (l/8 ^ 1)
+    const uint32_t dma_voff_odd = dma_voff + (uint32_t)((((lane >> 3) ^ 1) - (lane >> 3)) * 16);
+    const uint32_t lds0 = lds_addr(lds);
+
+    auto issue = [&](int kt, int stage) {
+        const int lp0 = kt >> lbs;
+        if (lp0 + ((C::N - 1) >> lbs) - win_page >= 64) {  // long ranges: slide the window
+            win_page = lp0;
+            btv = load_window(win_page);
+        }
+#pragma unroll
+        for (int i = 0; i < C::NI_W; ++i) {
+            const int c = wave * C::NI_W + i;
+            const int k8 = kt + C::KG * (c / C::IPG);  // first key of the group
+            const int lp = min(k8 >> lbs, seq_pages - 1);
+            const int phys = __builtin_amdgcn_readlane(btv, lp - win_page);
+            const char *base = kc + (uint64_t)phys * page_bytes + head_off +
+                               (uint32_t)(k8 & (bs - 1)) * row_stride + 128 * (c % C::IPG);
+            const uint32_t l = lds0 + stage * C::STAGE + c * 1024;
+            const uint32_t vo = ((c / C::IPG) & 1) ? dma_voff_odd : dma_voff;
+            dma16(base, vo, l);
+            dma16(base + v_minus_k, vo, l + C::T_BYTES);
+        }
+    };
+
+    // 8-bit caches: instruction c of a raw tile covers key group c / IPG8,
+    // bytes 128*(c % IPG8) .. +128 of those 8 rows; lane l brings 16 codes of
+    // key l%8, piece l/8, landing at c*1024 + 16*l of the raw tile.  With
+    // 64-byte rows, instruction c covers keys 4c .. 4c+3 whole (lane l: key
+    // l/16, bytes 4*(l%16)), landing row-major at c*256 + 4*l.
+    const uint32_t dma_voff8 =
+        C::ROWS8 ? (uint32_t)(lane >> 4) * row_stride + (uint32_t)(lane & 15) * 4u
+                 : (uint32_t)(lane & 7) * row_stride + (uint32_t)(lane >> 3) * 16u;
+    auto issue8 = [&](int kt, int stage) {
+        const int lp0 = kt >> lbs;
+        if (lp0 + ((C::N - 1) >> lbs) - win_page >= 64) {  // long ranges: slide the window
+            win_page = lp0;
+            btv = load_window(win_page);
+        }
+#pragma unroll
+        for (int i = 0; i < C::NI8_W; ++i) {
+            const int c = wave * C::NI8_W + i;
+            // first key of the instruction (a 4- or 8-key group: never two pages)
+            const int k8 = kt + (C::ROWS8 ? 4 * c : C::KG * (c / C::IPG8));
+            const int lp = min(k8 >> lbs, seq_pages - 1);
+            const int phys = __builtin_amdgcn_readlane(btv, lp - win_page);
+            const char *base = kc + (uint64_t)phys * page_bytes + head_off +
+                               (uint32_t)(k8 & (bs - 1)) * row_stride +
+                               (C::ROWS8 ? 0 : 128 * (c % C::IPG8));
+            const uint32_t l = lds0 + stage * C::RAW_STAGE + c * 64 * C::DW8;
+            dma_lds<C::DW8>(base, dma_voff8, l);
+            dma_lds<C::DW8>(base + v_minus_k, dma_voff8, l + C::RAW_T);
+        }
+    };
+
+    // ---- online softmax state (column q) ----
+    f32x16_t o[RB][C::DB];
+#pragma unroll
+    for (int blk = 0; blk < RB; ++blk)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) o[blk][db][j] = 0.f;
+    // m: reference max of the row's scaled scores (log2 units), shared by the
+    // lane pair; it is only raised when a tile's max exceeds it by more than
+    // RESCALE_THRESHOLD, so weights stay below 2^RESCALE_THRESHOLD.
+    float m[RB], mtrue[RB], l[RB];  // reference max, true running max, this lane's half of the exp-sum
+    int lim0[RB];
+    const int k_vis_end = min(k_hi, seq_len);  // keys past this are never visible
+#pragma unroll
+    for (int blk = 0; blk < RB; ++blk) {
+        m[blk] = NEG_INF;
+        mtrue[blk] = NEG_INF;
+        l[blk] = 0.f;
+        // register j of key block b holds key kt + 32*b + 8*(j/4) + 4*h + (j%4);
+        // it is visible when that offset from kt + 4*h is <= lim0 - kt
+        lim0[blk] = min(pos[blk], k_vis_end - 1) - 4 * h;
+    }
+
+    // Per-lane LDS bases; everything else in a fragment address is an
+    // immediate.  K: lane reads key 32b + (lane&31), piece 2ks + h.  V^T: in
+    // each 16-lane group, lane s points at key 4h + s/4 (+ 8 for the second
+    // read, + 16 per k-step, + 32 per block) and at d = 32db + 16*(group&1)
+    // + 4*(s%4), i.e. piece 4db + 2*(group&1) + (s/2)%2, byte 8*(s%2).
+    const int tg = lane >> 4;
+    const int ts = lane & 15;
+    const int kg = (lane & 31) >> 3;  // key group of the lane's key; odd ones swap line pairs
+    const int kp = h ^ (kg & 1);
+    // the key slot's XOR follows the parity of the stored piece's two low
+    // bits, which alternates with the k-step
+    const int k_base = kg * C::GROUP_BYTES + kp * 128 + (((lane & 7) ^ (kp << 2)) << 4);
+    const int k_base_odd = kg * C::GROUP_BYTES + kp * 128 + (((lane & 7) ^ ((kp ^ 1) << 2)) << 4);
+    const int v_pb = (ts >> 1) & 1;
+    const int v_base = (2 * (tg & 1) + v_pb) * 128 +
+                       (((4 * h + (ts >> 2)) ^ ((v_pb ^ (tg & 1)) << 2)) << 4) + 8 * (ts & 1);
+    // the same key slot in the odd key group (key + 8): its piece pair swapped
+    const int v_base_odd = C::GROUP_BYTES + (2 * (tg & 1) + (v_pb ^ 1)) * 128 +
+                           (((4 * h + (ts >> 2)) ^ ((v_pb ^ 1 ^ (tg & 1)) << 2)) << 4) + 8 * (ts & 1);
+
+    const int ntiles = (k_hi - k_lo + C::N - 1) / C::N;
+    constexpr int VM = 2 * C::NI_W;
+    constexpr int VM8 = 2 * C::NI8_W;
+    if constexpr (KV8) {
+#pragma unroll
+        for (int s = 0; s < NST; ++s)
+            if (s < ntiles) issue8(k_lo + s * C::N, s);
+    } else {
+#pragma unroll
+        for (int s = 0; s < NST - 1; ++s)
+            if (s < ntiles) issue(k_lo + s * C::N, s);
+    }
+
+    for (int it = 0; it < ntiles; ++it) {
+        const int kt = k_lo + it * C::N;
+        const int stage = it % NST;
+        const char *kst;
+        char *vst;
+        if constexpr (KV8) {
+            // raw tile `it` is in once this wave's older DMA has landed; the
+            // barrier also means every wave is done with the bf16 stage
+            wait_tiles_ahead<VM8, NST - 1>(min(NST - 1, ntiles - 1 - it));
+            __syncthreads();
+            kst = lds + C::RAW_BYTES;
+            vst = const_cast<char *>(kst) + C::T_BYTES;
+            const char *raw = lds + stage * C::RAW_STAGE;
+            // 16 codes (key `key`, 16-byte piece rp of its row) -> bf16 pieces
+            // 2rp and 2rp+1; keys vary fastest so reads and writes are
+            // conflict-free; V rows past the sequence become zeros (NaN codes
+            // would survive p = 0 inside the MFMA)
+            constexpr int CH = C::N * (D / 16);  // 16-byte raw pieces per tensor
+            for (int i = threadIdx.x; i < 2 * CH; i += C::NTH) {
+                const bool isv = i >= CH;
+                const int ii = isv ? i - CH : i;
+                const int key = ii % C::N, rp = ii / C::N;
+                const int roff = C::ROWS8 ? key * D + rp * 16
+                                          : ((key >> 3) * C::IPG8 + (rp >> 3)) * 1024 +
+                                                (((rp & 7) << 3) + (key & 7)) * 16;
+                const uint4 w = *reinterpret_cast<const uint4 *>(raw + (isv ? C::RAW_T : 0) + roff);
+                uint4 lo, hi;
+                if (isv && kt + key >= seq_len) {
+                    lo = make_uint4(0, 0, 0, 0);
+                    hi = lo;
+                } else {
+                    lo.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false));
+                    lo.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true));
+                    lo.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false));
+                    lo.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true));
+                    hi.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.z, 1.0f, false));
+                    hi.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.z, 1.0f, true));
+                    hi.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.w, 1.0f, false));
+                    hi.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.w, 1.0f, true));
+                }
+                char *dst = (isv ? vst : const_cast<char *>(kst));
+                *reinterpret_cast<uint4 *>(dst + tile_off<C>(key, 2 * rp)) = lo;
+                *reinterpret_cast<uint4 *>(dst + tile_off<C>(key, 2 * rp + 1)) = hi;
+            }
+            __syncthreads();  // the bf16 tile is complete and the raw stage is free
+            if (it + NST < ntiles) issue8(kt + NST * C::N, stage);
+        } else {
+            if (it + NST - 1 < ntiles) issue(kt + (NST - 1) * C::N, (it + NST - 1) % NST);
+            wait_tiles_ahead<VM, NST - 1>(min(NST - 1, ntiles - 1 - it));
+            kst = lds + stage * C::STAGE;
+            vst = const_cast<char *>(kst) + C::T_BYTES;
+            if (kt + C::N > seq_len) {
+                // V rows past the sequence may hold anything (NaN): zero them, since
+                // p = 0 does not cancel a NaN inside the MFMA
+                __syncthreads();
+                for (int i = threadIdx.x; i < C::N * C::PPR; i += C::NTH) {
+                    const int row = i / C::PPR;
+                    if (kt + row >= seq_len)
+                        *reinterpret_cast<uint4 *>(vst + tile_off<C>(row, i % C::PPR)) =
+                            make_uint4(0, 0, 0, 0);
+                }
+            }
+            __syncthreads();  // every wave's DMA share of this tile is in
+        }
+
+        // ---- S^T = K Q^T, 32-key blocks ----
+        // K fragments are streamed PF_K reads ahead of their MFMA (the
+        // scheduling barriers keep the compiler from hoisting all of them,
+        // which would cost registers the occupancy target does not have)
+        f32x16_t s[RB][C::NB];
+#pragma unroll
+        for (int b = 0; b < C::NB; ++b) {
+#pragma unroll
+            for (int blk = 0; blk < RB; ++blk) s[blk][b] = f32x16_t{};
+            auto kread = [&](int ks) {
+                return *reinterpret_cast<const uint4 *>(kst + ((ks & 1) ? k_base_odd : k_base) +
+                                                        b * 4 * C::GROUP_BYTES + ks * 256);
+            };
+            uint4 ka[PF_K];
+#pragma unroll
+            for (int ks = 0; ks < PF_K; ++ks) ka[ks] = kread(ks);
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) {
+                const uint4 a = ka[ks % PF_K];
+                if (ks + PF_K < C::KS) ka[ks % PF_K] = kread(ks + PF_K);
+                // one K fragment serves every row block of the wave
+#pragma unroll
+                for (int blk = 0; blk < RB; ++blk)
+                    s[blk][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8_t, a), qb[blk][ks], s[blk][b], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // ---- mask (boundary tiles only), online softmax on raw scores ----
+        if (kt + C::N - 1 > ctx + j0 || kt + C::N > k_vis_end) {
+#pragma unroll
+            for (int blk = 0; blk < RB; ++blk) {
+                const int lim = lim0[blk] - kt;
+#pragma unroll
+                for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        if (32 * b + 8 * (j >> 2) + (j & 3) > lim) s[blk][b][j] = NEG_INF;
+            }
+        }
+        float mx[RB];
+        bool up_any = false;
+#pragma unroll
+        for (int blk = 0; blk < RB; ++blk) {
+            mx[blk] = NEG_INF;
+#pragma unroll
+            for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) mx[blk] = fmaxf(mx[blk], s[blk][b][j]);
+            const RowPair pm = row_pair32(mx[blk]);
+            mx[blk] = fmaxf(pm.a, pm.b) * sl2;
+            mtrue[blk] = fmaxf(mtrue[blk], mx[blk]);
+            up_any = up_any || mx[blk] > m[blk] + RESCALE_THRESHOLD;
+        }
+        if (__builtin_amdgcn_ballot_w64(up_any)) {
+#pragma unroll
+            for (int blk = 0; blk < RB; ++blk) {
+                const bool up = mx[blk] > m[blk] + RESCALE_THRESHOLD;
+                const float alpha = up ? __builtin_amdgcn_exp2f(m[blk] - mx[blk]) : 1.f;
+                m[blk] = up ? mx[blk] : m[blk];
+                l[blk] *= alpha;
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) o[blk][db][j] *= alpha;
+            }
+        }
+        float msub[RB];
+#pragma unroll
+        for (int blk = 0; blk < RB; ++blk)
+            msub[blk] = m[blk] == NEG_INF ? 0.f : m[blk];  // rows with no visible key yet
+        // ---- per 32-key block: P (bf16), then O^T += V^T P^T over its two k-steps ----
+#pragma unroll
+        for (int b = 0; b < C::NB; ++b) {
+            uint32_t pk[RB][8];
+#pragma unroll
+            for (int blk = 0; blk < RB; ++blk)
+#pragma unroll
+                for (int j = 0; j < 16; j += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[blk][b][j], sl2, -msub[blk]));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[blk][b][j + 1], sl2, -msub[blk]));
+                    pk[blk][j / 2] = pack_bf16(p0, p1);
+                    // sums the bf16 weights actually applied
+                    l[blk] = dot2(pk[blk][j / 2], 0x3F803F80u, l[blk]);
+                }
+            // V^T fragments, streamed PF_V MFMAs ahead; MFMA i = (ks2, db)
+            auto vread = [&](int i) {
+                const char *a = vst + v_base + (4 * b + 2 * (i / C::DB)) * C::GROUP_BYTES +
+                                (i % C::DB) * 512;
+                const s16x4_t lo = lds_read_tr16(a);
+                const s16x4_t hi = lds_read_tr16(a - v_base + v_base_odd);
+                const s16x4_t av[2] = {lo, hi};
+                return __builtin_bit_cast(bf16x8_t, av);
+            };
+            bf16x8_t va[PF_V];
+#pragma unroll
+            for (int i = 0; i < PF_V; ++i) va[i] = vread(i);
+#pragma unroll
+            for (int i = 0; i < 2 * C::DB; ++i) {
+                const int ks2 = i / C::DB, db = i % C::DB;
+                const bf16x8_t a = va[i % PF_V];
+                if (i + PF_V < 2 * C::DB) va[i % PF_V] = vread(i + PF_V);
+                // one V^T fragment serves every row block of the wave
+#pragma unroll
+                for (int blk = 0; blk < RB; ++blk) {
+                    const u32x4_t pb = {pk[blk][4 * ks2], pk[blk][4 * ks2 + 1], pk[blk][4 * ks2 + 2],
+                                        pk[blk][4 * ks2 + 3]};
+                    o[blk][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        a, __builtin_bit_cast(bf16x8_t, pb), o[blk][db], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // everyone is done with this stage before it is refilled (8-bit caches:
+        // the next iteration's first barrier protects the bf16 stage)
+        if constexpr (!KV8) __syncthreads();
+    }
+
+    // ---- finish: full exp-sum of each row, normalise, store ----
+#pragma unroll
+    for (int blk = 0; blk < RB; ++blk) {
+        const RowPair pl = row_pair32(l[blk]);
+        const float lb = pl.a + pl.b;
+        if (!row_valid[blk]) continue;
+        const int n_parts = p.partition ? pos[blk] / p.partition + 1 : 1;
+        if (p.partition && part >= n_parts) continue;  // no keys of this row here
+        // 8-bit caches: O holds code units of V, so the head's V scale joins 1/l
+        float inv = (KV8 ? p.v_scale[kvh] : 1.f) / lb;
+        if (n_parts == 1 && p.sinks) {
+            // the head's sink: one more denominator term, no value (log2 units)
+            const float s2 = p.sinks[head[blk]] * LOG2E_F;
+            const float Mx = fmaxf(m[blk], s2);
+            const float a = exp2_diff(m[blk], Mx);
+            inv = (KV8 ? p.v_scale[kvh] : 1.f) * a / (lb * a + exp2_diff(s2, Mx));
+        }
+        if (n_parts == 1) {
+            uint16_t *orow =
+                reinterpret_cast<uint16_t *>(p.out) + ((size_t)t_glob[blk] * p.hq + head[blk]) * D;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int d = db * 32 + 8 * a + 4 * h;
+                    uint2 w;
+                    w.x = pack_bf16(o[blk][db][4 * a] * inv, o[blk][db][4 * a + 1] * inv);
+                    w.y = pack_bf16(o[blk][db][4 * a + 2] * inv, o[blk][db][4 * a + 3] * inv);
+                    *reinterpret_cast<uint2 *>(orow + d) = w;
+                }
+        } else {
+            const size_t si = ((size_t)t_glob[blk] * p.hq + head[blk]) * p.max_parts + part;
+            float *orow = p.tmp_out + si * D;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int d = db * 32 + 8 * a + 4 * h;
+                    float4 w = {o[blk][db][4 * a] * inv, o[blk][db][4 * a + 1] * inv,
+                                o[blk][db][4 * a + 2] * inv, o[blk][db][4 * a + 3] * inv};
+                    *reinterpret_cast<float4 *>(orow + d) = w;
+                }
+            if (h == 0) {
+                p.max_logits[si] = mtrue[blk];
+                p.exp_sums[si] = lb * __builtin_amdgcn_exp2f(m[blk] - mtrue[blk]);
+            }
+        }
+    }
+}
+
+// Launch of the tile kernel over the whole batch: a 1-D grid of virtual work
+// items (q-tile, KV head, partition), padded to whole XCD chunks; surplus
+// workgroups exit at once.
+template <int D, int N, int NST, bool KV8, int NWV, int RB>
+hipError_t launch_tiles(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
+    const int TPW = 32 * RB / p.group;
+    const int BQ = NWV * TPW;
+    AttnParams q = p;
+    q.grid_tiles = p.total_q / BQ + p.num_seqs;
+    q.grid_parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
+    const int64_t items = (int64_t)q.grid_tiles * p.hkv * q.grid_parts;
+    if (items > INT32_MAX - 4096) return hipErrorInvalidConfiguration;
+    const int64_t unit = 8 * XCD_CHUNK;
+    const int blocks = (int)((items + unit - 1) / unit * unit);
+    if (li) *li = LaunchInfo{{blocks, 1, 1}, NWV * 64, {N, NST, BQ}, 0};
+    hipLaunchKernelGGL((prefill_kernel<D, N, NST, KV8, NWV, RB>), dim3(blocks), dim3(NWV * 64), 0,
+                       stream, q);
+    return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace pa
