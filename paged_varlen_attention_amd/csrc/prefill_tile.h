@@ -120,12 +120,17 @@ __global__ __launch_bounds__(NWV * 64, RB == 1 ? PREFILL_WAVES_PER_SIMD * 4 / NW
     const int TPW = 32 * RB / G;  // tokens per wave
     const int BQ = C::NWV * TPW;  // tokens per workgroup
 
-    // ---- which request and which q-tile (later virtual tiles first) ----
-    // ---- XCD-aware order.  Workgroups go to the 8 XCDs round-robin by launch
-    // index L; groups of XCD_CHUNK consecutive work items (q-tiles of one
-    // request and KV head, which read the same keys) are kept on one XCD so
-    // its L2 serves the repeats.  Work items are taken last-first: later
-    // q-tiles of a request see more keys.
+    // ---- which request, q-tile, KV head and partition (XCD-aware order) ----
+    // Workgroups go to the 8 XCDs round-robin by launch index L.  Work items
+    // come in chunks of XCD_CHUNK consecutive virtual q-tiles of one (KV head,
+    // partition) -- q-tiles of one request that read the same keys -- and each
+    // chunk is kept on one XCD so its L2 serves the repeats.  Chunks are taken
+    // last-first (later q-tiles see more keys).  Unsplit launches interleave
+    // the KV heads chunk by chunk, so the longest q-tiles of every head start
+    // first (uniform 8 x 4,096-token prefill 8-9% faster than head after head);
+    // split launches take the partitions slowest, which measured faster for
+    // them (the verify batch at 1,024-key partitions: 99 against 115 us).
+    // (grid_tiles is a multiple of XCD_CHUNK.)
     const int n_items = p.grid_tiles * p.hkv * p.grid_parts;
     int lam = blockIdx.x;
     {
@@ -134,7 +139,17 @@ __global__ __launch_bounds__(NWV * 64, RB == 1 ? PREFILL_WAVES_PER_SIMD * 4 / NW
     }
     if (lam >= n_items) return;
     lam = n_items - 1 - lam;
-    const int x = lam % p.grid_tiles;
+    int part, kvh, x;
+    if (p.grid_parts == 1) {
+        const int chunk = lam / XCD_CHUNK;
+        part = 0;
+        kvh = chunk % p.hkv;
+        x = (chunk / p.hkv) * XCD_CHUNK + lam % XCD_CHUNK;
+    } else {
+        x = lam % p.grid_tiles;
+        kvh = (lam / p.grid_tiles) % p.hkv;
+        part = lam / (p.grid_tiles * p.hkv);
+    }
     int r, tile;
     if (p.num_seqs <= 64) {
         // Up to 64 requests: the virtual tiles list the requests by key count,
@@ -175,8 +190,6 @@ __global__ __launch_bounds__(NWV * 64, RB == 1 ? PREFILL_WAVES_PER_SIMD * 4 / NW
     if (tile < 0 || j0 >= q_len) return;
     const int seq_len = p.seq_lens[r];
     const int ctx = seq_len - q_len;
-    const int kvh = (lam / p.grid_tiles) % p.hkv;
-    const int part = lam / (p.grid_tiles * p.hkv);
     const int j_last = min(q_len, j0 + BQ) - 1;
     // keys of this workgroup: the partition, cut at the last token's position
     const int k_lo = p.partition ? part * p.partition : 0;
@@ -604,7 +617,7 @@ hipError_t launch_tiles(const AttnParams &p, hipStream_t stream, LaunchInfo *li)
     const int TPW = 32 * RB / p.group;
     const int BQ = NWV * TPW;
     AttnParams q = p;
-    q.grid_tiles = p.total_q / BQ + p.num_seqs;
+    q.grid_tiles = (p.total_q / BQ + p.num_seqs + XCD_CHUNK - 1) / XCD_CHUNK * XCD_CHUNK;
     q.grid_parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
     const int64_t items = (int64_t)q.grid_tiles * p.hkv * q.grid_parts;
     if (items > INT32_MAX - 4096) return hipErrorInvalidConfiguration;
