@@ -382,30 +382,14 @@ def cpu_model():
     return "unknown"
 
 
-# Runs in a child process (OMP_NUM_THREADS=1 is read when the oracle's
-# OpenMP runtime starts): prints the median seconds of 3 single-threaded
-# passes of the oracle over the GQA decode batch.
-_ONE_THREAD = """
-import json, sys, time
-sys.path.insert(0, {root!r})
-import oracle, workloads as W
-w = W.gqa_decode_bf16()
-oracle.run_workload(w, rows=[(0, 0)])
-ts = []
-for _ in range(3):
-    t0 = time.perf_counter(); oracle.run_workload(w); ts.append(time.perf_counter() - t0)
-print(json.dumps({{"threads": oracle.num_threads(), "s": sorted(ts)[1]}}))
-"""
-
-
 def cpu_baseline(w, pass_s=3.0):
     """The fp64 oracle, as it stands, timed on this host: the median of 3
     passes on all the threads OpenMP gives it (each pass repeats the whole
     batch for about pass_s seconds), then the median of 3 single-threaded
-    passes in a child process.  Work unit: the workload's algorithmic bytes."""
-    import subprocess
+    passes.  Work unit: the workload's algorithmic bytes."""
     import oracle
     oracle.run_workload(w, rows=[(0, 0)])  # loads / builds the oracle library
+    threads = oracle.num_threads()
     t0 = time.perf_counter()
     oracle.run_workload(w)
     reps = max(1, int(pass_s / max(time.perf_counter() - t0, 1e-3)))
@@ -416,25 +400,27 @@ def cpu_baseline(w, pass_s=3.0):
             oracle.run_workload(w)
         per.append((time.perf_counter() - t0) / reps)
     per = sorted(per)[1]
-    one = None
-    env = dict(os.environ, OMP_NUM_THREADS="1")
-    r = subprocess.run([sys.executable, "-c", _ONE_THREAD.format(root=ROOT)], env=env,
-                       capture_output=True, text=True, timeout=300)
-    if r.returncode == 0 and r.stdout.strip():
-        one = json.loads(r.stdout.strip().splitlines()[-1])
+    oracle.set_num_threads(1)
+    one = []
+    try:
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.run_workload(w)
+            one.append(time.perf_counter() - t0)
+        one_threads = oracle.num_threads()
+    finally:
+        oracle.set_num_threads(threads)
+    one = sorted(one)[1]
     nb = w.algorithmic_bytes()
-    res = {"value": round(nb / per / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
-           "kind": "oracle",
-           "sample": f"median of 3 passes, each {reps} full runs of the {w.name} batch "
-                     f"({w.num_seqs} requests, all {w.num_q_heads} heads; {per * 1e3:.1f} ms per "
-                     f"batch), fp64 C oracle, OpenMP over (query row, head)",
-           "cpu_model": cpu_model(), "host_logical_cpus": os.cpu_count(),
-           "affinity_cpus": len(os.sched_getaffinity(0))}
-    if one:
-        res["single_thread"] = {"value": round(nb / one["s"] / 1e9, 3), "unit": "GB/s",
-                                "ms_per_batch": round(one["s"] * 1e3, 1),
-                                "threads": one["threads"], "sample": "median of 3 full batches"}
-    return res
+    return {"value": round(nb / per / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"median of 3 passes, each {reps} full runs of the {w.name} batch "
+                      f"({w.num_seqs} requests, all {w.num_q_heads} heads; {per * 1e3:.1f} ms per "
+                      f"batch), fp64 C oracle, OpenMP over (query row, head)",
+            "cpu_model": cpu_model(), "host_logical_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "single_thread": {"value": round(nb / one / 1e9, 3), "unit": "GB/s",
+                              "ms_per_batch": round(one * 1e3, 1), "threads": one_threads,
+                              "sample": "median of 3 full batches"}}
 
 
 def copy_calibration(device, mib=512, reps=5):
@@ -477,8 +463,11 @@ def main():
 
     # ---------------- headline: GQA decode batch ----------------
     w = W.gqa_decode_bf16()
-    P = 512
-    log(f"workload {w.name}: {w.description}; P={P}")
+    P = 512  # the workload's partition size
+    import paged_varlen_attention_amd as pa
+    P_policy = pa.pick_partition_size(w.seq_lens.tolist(), w.num_q_heads, w.num_kv_heads,
+                                      w.head_dim, w.block_size, w.dtype)
+    log(f"workload {w.name}: {w.description}; P={P} (partition policy picks {P_policy})")
     sec, km, sec_warm, km_warm = measure(w, P, args.steps, args.warmup, args.copies, device)
     nbytes = step_bytes(w, include_cache_write=True)
     value = nbytes / sec / 1e9
@@ -486,6 +475,10 @@ def main():
     achieved = attn_bytes / (km["attention_back_to_back"] * 1e-3) / 1e9
     log(f"decode step {sec * 1e3:.4f} ms ({value:.1f} GB/s); kernels {km}; warm step "
         f"{sec_warm * 1e3:.4f} ms, kernels {km_warm}")
+    policy_step_ms = sec * 1e3
+    if P_policy != P:  # the policy's pick, timed the same way
+        sec_p, _, _, _ = measure(w, P_policy, args.steps, args.warmup, args.copies, device)
+        policy_step_ms = sec_p * 1e3
 
     result = {
         "metric": METRIC,
@@ -509,6 +502,8 @@ def main():
             "page_size": w.block_size,
             "pool_blocks": w.num_blocks,
             "partition_size": P,
+            "partition_policy_pick": P_policy,
+            "partition_policy_ms_per_step": round(policy_step_ms, 5),
             "step": "reshape_and_cache + varlen_attention + split_kv_reduce",
             "algorithmic_bytes_per_step": nbytes,
             "kv_pool_copies_cycled": args.copies,
@@ -544,7 +539,12 @@ def main():
         sec_out = {}
         steps2 = max(10, args.steps // 2)
         w4 = W.long_decode_bf16()
-        for P4 in (256, 512):
+        # the workload's fixed sizes (256, 512) and the size the library's
+        # partition policy picks for it on this GPU
+        import paged_varlen_attention_amd as pa
+        P4_policy = pa.pick_partition_size(w4.seq_lens.tolist(), w4.num_q_heads, w4.num_kv_heads,
+                                           w4.head_dim, w4.block_size, w4.dtype)
+        for P4 in sorted({256, 512, P4_policy}):
             if not wanted(f"long_decode_bf16_P{P4}"):
                 continue
             s4, k4, s4w, _ = measure(w4, P4, steps2, 5, 2, device)
@@ -556,7 +556,8 @@ def main():
                 "attention_GB/s": round(b4 / (k4["attention_back_to_back"] * 1e-3) / 1e9, 2),
                 "frac_hbm": round(b4 / s4 / 1e9 / HBM_PEAK_GBS, 4),
                 "step_ms_percentiles": k4["step_ms_percentiles"],
-                "warm_ms_per_step": round(s4w * 1e3, 5)}
+                "warm_ms_per_step": round(s4w * 1e3, 5),
+                "partition_policy_pick": P4 == P4_policy}
             log(f"long decode P={P4}: {sec_out[f'long_decode_bf16_P{P4}']}")
         # 8-bit E4M3 caches (the library's KV quantisation): the same decode
         # batches with half the KV bytes

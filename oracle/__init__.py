@@ -52,6 +52,8 @@ def _load(path: Optional[str] = None):
 def _declare(lib):
     P, I, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_double
     lib.pa_ref_num_threads.restype = ctypes.c_int
+    lib.pa_ref_set_num_threads.argtypes = [ctypes.c_int]
+    lib.pa_ref_set_num_threads.restype = None
     lib.pa_ref_reshape_and_cache.argtypes = [P, P, P, P, P, I, I, I, I, I, I]
     lib.pa_ref_expand_block_tables.argtypes = [P, P, I, I, I, I, I]
     lib.pa_ref_copy_blocks.argtypes = [P, P, P, P, P, I, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
@@ -171,6 +173,12 @@ def quantize_cache(cache: torch.Tensor, scale, lib=None) -> torch.Tensor:
 
 def num_threads(lib=None) -> int:
     return int((lib or _load()).pa_ref_num_threads())
+
+
+def set_num_threads(n: int, lib=None) -> None:
+    """Threads of the oracle's row loop (timing only: each row's arithmetic is
+    the same whatever the count)."""
+    (lib or _load()).pa_ref_set_num_threads(int(n))
 
 
 def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, lib=None) -> None:

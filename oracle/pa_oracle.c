@@ -25,6 +25,15 @@ int pa_ref_num_threads(void) {
 #endif
 }
 
+/* Threads of the row loop from now on (the CPU baseline times 1 and all). */
+void pa_ref_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Exact widening of one stored element to double.  bfloat16 is the upper
  * half of an IEEE float32, so shifting it up 16 bits gives that float. */
 static double load_elem(const void *base, size_t idx, int dtype) {

@@ -77,6 +77,8 @@ int pa_ref_e4m3_encode_f32(uint8_t *out, const float *y, int64_t n);
 
 /* Threads the OpenMP runtime will use for the row loops. */
 int pa_ref_num_threads(void);
+/* Set the thread count of the row loop (timing only; results do not depend on it). */
+void pa_ref_set_num_threads(int n);
 
 /* Cache write: for t in [0, T): s = slot_mapping[t]; s < 0 -> skip;
  * caches[s / bs][s % bs][:][:] = rows[t][:][:], for K and V.  A byte copy. */

@@ -46,3 +46,21 @@ def test_no_split_switch(monkeypatch, max_q):
     assert pa.last_dispatch()["path"] == "reduce_skipped"
     torch.cuda.synchronize()
     assert_close(out, ref, torch.bfloat16, "PA_NO_SPLIT")
+
+
+@pytest.mark.parametrize("name,expect", [("gqa_decode_bf16", 512), ("long_decode_bf16", 2048)])
+def test_policy_pick_on_the_device(name, expect):
+    """pa_pick_partition_size with the device's own CU count (num_cus = 0) on
+    the two benchmark decode batches: it picks the partition size the
+    calibration found fastest for them on MI355X (256 CUs), and attention +
+    reduce at that size match the oracle on every row."""
+    import paged_varlen_attention_amd as pa
+    w = W.CONFIGS[name]()
+    P = pa.pick_partition_size(w.seq_lens.tolist(), w.num_q_heads, w.num_kv_heads, w.head_dim,
+                               w.block_size, w.dtype)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert P == expect, P
+    ref = oracle.run_workload(w)
+    out = run_gpu(to_device(w), P)
+    torch.cuda.synchronize()
+    assert_close(out, ref, torch.bfloat16, f"{name} at the policy's P={P}")
