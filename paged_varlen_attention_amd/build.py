@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpa.so")
 SOURCES = ["pa_api.cpp", "cache_write.hip", "decode.hip", "decode_mfma.hip", "decode_rows.hip", "reduce.hip",
-           "prefill.hip", "prefill_wide.hip", "block_copy.hip", "noalloc.hip"]
+           "prefill.hip", "block_copy.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -98,8 +98,6 @@ bool decode_rows_supported(const AttnParams &p);
 hipError_t launch_decode_rows(const AttnParams &p, hipStream_t stream, LaunchInfo *li);
 hipError_t launch_decode_mfma(const AttnParams &p, hipStream_t stream, LaunchInfo *li);
 hipError_t launch_prefill(const AttnParams &p, hipStream_t stream, LaunchInfo *li);
-// bf16 tiles with two 32-row blocks per wave (head_dim 128 or 256).
-hipError_t launch_prefill_wide(const AttnParams &p, hipStream_t stream, LaunchInfo *li);
 hipError_t launch_reduce(const ReduceParams &p, hipStream_t stream, LaunchInfo *li);
 
 // Device address of the calling thread's current device's copy of the

@@ -34,8 +34,6 @@
 //    v_cvt_scalef32_pk_bf16_fp8 (exact), zeroing V rows past the sequence;
 //    the MFMA code is unchanged.  The head's K scale joins the softmax scale
 //    and its V scale the final normaliser.
-#include <cstdlib>
-
 #include "prefill_tile.h"
 
 namespace pa {
@@ -86,11 +84,6 @@ hipError_t launch_prefill(const AttnParams &p, hipStream_t stream, LaunchInfo *l
             case 256: return launch_d<256, true>(p, stream, li);
             default: return hipErrorInvalidValue;
         }
-    }
-    {  // experiment switch: two row blocks per wave
-        const char *e = std::getenv("PA_TILE_ROWS");
-        if (e && e[0] == '2' && (p.head_dim == 128 || p.head_dim == 256))
-            return launch_prefill_wide(p, stream, li);
     }
     switch (p.head_dim) {
         case 64: return launch_d<64, false>(p, stream, li);

@@ -1,8 +1,11 @@
-// prefill_tile.h -- the tiled bf16-MFMA attention kernel template shared by
-// prefill.hip (one 32-row block per wave) and prefill_wide.hip (two 32-row
-// blocks per wave sharing every K and V^T fragment; compiled separately so
-// its accumulators may live in AGPRs).  What it computes and how is
-// described at the top of prefill.hip.
+// prefill_tile.h -- the tiled bf16-MFMA attention kernel template and its
+// launcher (instantiated in prefill.hip; what it computes and how is
+// described there).  RB is the number of 32-row column blocks a wave holds;
+// every K and V^T fragment read from LDS feeds RB MFMAs.  The library builds
+// RB = 1: two blocks per wave (64 query rows, one wave per SIMD, accumulators
+// in AGPRs) were parity-green but 19% slower on uniform D = 128 prefill and
+// spilled at D = 256, since one wave per SIMD leaves the LDS and MFMA
+// latencies exposed.
 #pragma once
 
 #include "pa_device.h"
