@@ -127,54 +127,72 @@ __global__ __launch_bounds__(NWV * 64, RB == 1 ? PREFILL_WAVES_PER_SIMD * 4 / NW
     // Workgroups go to the 8 XCDs round-robin by launch index L.  Work items
     // come in chunks of XCD_CHUNK consecutive virtual q-tiles of one (KV head,
     // partition) -- q-tiles of one request that read the same keys -- and each
-    // chunk is kept on one XCD so its L2 serves the repeats.  Chunks are taken
-    // last-first (later q-tiles see more keys).  Unsplit launches interleave
-    // the KV heads chunk by chunk, so the longest q-tiles of every head start
-    // first (uniform 8 x 4,096-token prefill 8-9% faster than head after head);
-    // split launches take the partitions slowest, which measured faster for
-    // them (the verify batch at 1,024-key partitions: 99 against 115 us).
+    // chunk is kept on one XCD so its L2 serves the repeats; round k of the
+    // launch hands chunks 8k..8k+7 to the 8 XCDs.  Chunks are taken last-first
+    // (later q-tiles see more keys).
+    // Unsplit launches interleave the KV heads chunk by chunk, so the longest
+    // q-tiles of every head start first, and deal the rounds serpentine (XCD x
+    // takes the x-th chunk of even rounds and the (7-x)-th of odd ones): costs
+    // fall steadily along that order, and the two directions even them out
+    // over the XCDs.  The deal starts at the last real q-tile, surplus virtual
+    // tiles come last, so the pairing keeps its phase.
+    // Against plain rounds with the surplus first, this deal measured 4-5%
+    // faster on the uniform 8 x 4,096-token prefill and the mixed batch of
+    // eight ~750-token prompts.  Split launches take the partitions slowest,
+    // in plain rounds, which measured faster for them (the verify batch at
+    // 1,024-key partitions: 99 against 115 us head-interleaved, 101 against
+    // 106 serpentine).
     // (grid_tiles is a multiple of XCD_CHUNK.)
     const int n_items = p.grid_tiles * p.hkv * p.grid_parts;
-    int lam = blockIdx.x;
+    int lam;
     {
-        const int xcd = lam & 7, slot = lam >> 3;
-        lam = ((slot / XCD_CHUNK) * 8 + xcd) * XCD_CHUNK + slot % XCD_CHUNK;
+        const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, round = slot / XCD_CHUNK;
+        const int cx = (p.grid_parts == 1 && (round & 1)) ? 7 - xcd : xcd;
+        lam = (round * 8 + cx) * XCD_CHUNK + slot % XCD_CHUNK;
     }
     if (lam >= n_items) return;
-    lam = n_items - 1 - lam;
-    int part, kvh, x;
-    if (p.grid_parts == 1) {
-        const int chunk = lam / XCD_CHUNK;
-        part = 0;
-        kvh = chunk % p.hkv;
-        x = (chunk / p.hkv) * XCD_CHUNK + lam % XCD_CHUNK;
-    } else {
-        x = lam % p.grid_tiles;
-        kvh = (lam / p.grid_tiles) % p.hkv;
-        part = lam / (p.grid_tiles * p.hkv);
-    }
-    int r, tile;
-    if (p.num_seqs <= 64) {
-        // Up to 64 requests: the virtual tiles list the requests by key count,
-        // fewest first, each with exactly its own q-tiles, so that the
-        // last-first dispatch starts the requests with the most keys (and
-        // their longest q-tiles) first -- a decode row over a long context
-        // costs as much as a prompt's last q-tile and must not come last.
-        // Every wave computes the same table, one request per lane.
+    // Up to 64 requests, the virtual tiles list the requests by key count,
+    // fewest first, each with exactly its own q-tiles, so that the last-first
+    // dispatch starts the requests with the most keys (and their longest
+    // q-tiles) first -- a decode row over a long context costs as much as a
+    // prompt's last q-tile and must not come last.  Every wave computes the
+    // same table, one request per lane.  Beyond 64 requests request r owns
+    // virtual tiles from cu_q[r] / BQ + r on (one more than it can fill).
+    const bool listed = p.num_seqs <= 64;
+    int start = 0, nt = 0, real_tiles = p.grid_tiles;
+    if (listed) {
         const int i = lane;
         int ql = 0, sl = 0;
         if (i < p.num_seqs) {
             ql = p.cu_q[i + 1] - p.cu_q[i];
             sl = p.seq_lens[i];
         }
-        const int nt = ql > 0 ? (ql + BQ - 1) / BQ : 0;
-        int start = 0;
+        nt = ql > 0 ? (ql + BQ - 1) / BQ : 0;
+        real_tiles = 0;
         for (int j = 0; j < p.num_seqs; ++j) {
             const int slj = __builtin_amdgcn_readlane(sl, j);
             const int ntj = __builtin_amdgcn_readlane(nt, j);
             start += (slj < sl || (slj == sl && j < i)) ? ntj : 0;
+            real_tiles += ntj;
         }
-        const uint64_t mine = __ballot(i < p.num_seqs && x >= start && x < start + nt);
+    }
+    int part, kvh, x;
+    if (p.grid_parts == 1) {
+        const int chunk = lam / XCD_CHUNK;
+        part = 0;
+        kvh = chunk % p.hkv;
+        const int xc = (real_tiles + XCD_CHUNK - 1) / XCD_CHUNK - 1 - chunk / p.hkv;
+        if (xc < 0) return;  // surplus chunk
+        x = xc * XCD_CHUNK + XCD_CHUNK - 1 - lam % XCD_CHUNK;
+    } else {
+        lam = n_items - 1 - lam;
+        x = lam % p.grid_tiles;
+        kvh = (lam / p.grid_tiles) % p.hkv;
+        part = lam / (p.grid_tiles * p.hkv);
+    }
+    int r, tile;
+    if (listed) {
+        const uint64_t mine = __ballot(lane < p.num_seqs && x >= start && x < start + nt);
         if (!mine) return;  // surplus virtual tile
         r = (int)__builtin_ctzll(mine);
         tile = x - __builtin_amdgcn_readlane(start, r);
