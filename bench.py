@@ -281,19 +281,8 @@ def pmc_traffic():
     """HBM bytes per launch of the decode kernel from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summary (each scaled by its copy-kernel
     calibration), or None when the kernel sources changed since it was taken."""
-    import hashlib
-    path = os.path.join(ROOT, PMC_SUMMARY)
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    for line in open(path):
-        if ":" in line and not line.startswith(("#", "|", " ")):
-            k, v = line.split(":", 1)
-            kv[k.strip()] = v.strip()
-    h = hashlib.sha256()
-    for f in DECODE_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if kv.get("kernel_sources_sha256") != h.hexdigest():
+    kv = _summary_fields(PMC_SUMMARY, DECODE_SOURCES)
+    if not kv:
         return None
     try:
         return int(round((float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_factor"]) +
@@ -303,6 +292,7 @@ def pmc_traffic():
 
 
 PREFILL_SOURCES = ("paged_varlen_attention_amd/csrc/prefill.hip",
+                   "paged_varlen_attention_amd/csrc/prefill_tile.h",
                    "paged_varlen_attention_amd/csrc/pa_device.h",
                    "paged_varlen_attention_amd/csrc/pa_internal.h")
 PREFILL_PMC_SUMMARY = "profiles/prefill_tiles_pmc.md"

@@ -186,6 +186,29 @@ def test_wide_workgroups(kv8):
         assert_close(got, ref, torch.bfloat16, f"wide P={P}")
 
 
+def test_wide_workgroups_many_short():
+    """8-wave workgroups over 80 short requests (1..40 new tokens on 0..400
+    cached, 64/8 heads, D=256): more than 64 requests, so q-tiles are found by
+    the search over cu_seqlens_q; workgroups walk from one to fourteen key
+    tiles, so first and last tiles (prefetch start, masking, the sequence
+    end) weigh in.  The whole output is compared, unsplit and split at 256
+    keys."""
+    import paged_varlen_attention_amd as pa
+    w = W.random_case(8080, num_seqs=80, max_q=40, max_ctx=400, num_q_heads=64,
+                      num_kv_heads=8, head_dim=256, block_size=16, dtype=torch.bfloat16)
+    ref = oracle.run_workload(w)
+    b = to_device(w)
+    for P in (0, 256):
+        parts = (pa.alloc_partials(w.total_q, 64, 256, pa.max_partitions(w.max_seq_len, P), "cuda")
+                 if P else None)
+        out = run_gpu(b, P, partials=parts, reduce=False)
+        assert pa.last_dispatch()["block"] == 512  # 8 waves
+        if P:
+            pa.split_kv_reduce(out, parts, b.cu_seqlens_q, b.seq_lens, P, sinks=b.sinks)
+        torch.cuda.synchronize()
+        assert_close(out, ref, torch.bfloat16, f"wide many short P={P}")
+
+
 @pytest.mark.parametrize("bs", [8, 16, 32])
 def test_wide_workgroups_long_prompts(bs):
     """8-wave workgroups (64/8 heads, D=256) over prompts of 1,500..2,000
