@@ -413,6 +413,31 @@ def cpu_baseline(w, pass_s=3.0):
                               "sample": "median of 3 full batches"}}
 
 
+def gemm_reference(device, n=16384, reps=5):
+    """The dense bf16 rate a plain library GEMM reaches on this GPU (torch.matmul,
+    i.e. hipBLASLt; not the library's own kernels): an n x n x n product timed
+    with HIP events, as the measured matrix-core reference beside the published
+    2.5 PFLOP/s."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(11)
+    a = torch.randn((n, n), device=device, generator=g).to(torch.bfloat16)
+    b = torch.randn((n, n), device=device, generator=g).to(torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tf = 2 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b, c
+    return {"op": f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt)", "ms": round(ms, 4),
+            "TFLOP/s": round(tf, 1), "frac_of_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
+
+
 def copy_calibration(device, mib=512, reps=5):
     """A plain device copy of known size, for scaling rocprof FETCH/WRITE counters."""
     import torch
@@ -605,6 +630,9 @@ def main():
         if wanted("kv_block_offload_bf16"):
             sec_out["kv_block_offload_bf16"] = block_offload(device)
             log(f"kv block offload: {sec_out['kv_block_offload_bf16']}")
+        if wanted("bf16_gemm_reference"):
+            sec_out["bf16_gemm_reference"] = gemm_reference(device)
+            log(f"bf16 GEMM reference: {sec_out['bf16_gemm_reference']}")
         result["secondary"] = sec_out
 
     if args.copy_calibration:
