@@ -438,6 +438,29 @@ def gemm_reference(device, n=16384, reps=5):
             "TFLOP/s": round(tf, 1), "frac_of_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
 
 
+def copy_reference(device, mib=1024, reps=5):
+    """The HBM rate a plain library copy reaches (torch's device-to-device copy,
+    not the library's kernels): bytes read plus bytes written per HIP-event
+    time, beside the published 8 TB/s."""
+    import torch
+    a = torch.empty(mib * 2 ** 20 // 4, dtype=torch.float32, device=device).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = 2 * mib * 2 ** 20 / (ms * 1e-3) / 1e9
+    del a, b
+    return {"op": f"torch copy_ of {mib} MiB (read + write)", "ms": round(ms, 4),
+            "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def copy_calibration(device, mib=512, reps=5):
     """A plain device copy of known size, for scaling rocprof FETCH/WRITE counters."""
     import torch
@@ -630,6 +653,9 @@ def main():
         if wanted("kv_block_offload_bf16"):
             sec_out["kv_block_offload_bf16"] = block_offload(device)
             log(f"kv block offload: {sec_out['kv_block_offload_bf16']}")
+        if wanted("hbm_copy_reference"):
+            sec_out["hbm_copy_reference"] = copy_reference(device)
+            log(f"HBM copy reference: {sec_out['hbm_copy_reference']}")
         if wanted("bf16_gemm_reference"):
             sec_out["bf16_gemm_reference"] = gemm_reference(device)
             log(f"bf16 GEMM reference: {sec_out['bf16_gemm_reference']}")
