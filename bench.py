@@ -272,6 +272,7 @@ def measure(w, P, steps, warmup, copies, device, write_cache=True, kv8=False):
 DECODE_SOURCES = ("paged_varlen_attention_amd/csrc/decode.hip",
                   "paged_varlen_attention_amd/csrc/decode_mfma.hip",
                   "paged_varlen_attention_amd/csrc/decode_rows.hip",
+                  "paged_varlen_attention_amd/csrc/decode_rows8.hip",
                   "paged_varlen_attention_amd/csrc/pa_device.h",
                   "paged_varlen_attention_amd/csrc/pa_internal.h")
 PMC_SUMMARY = "profiles/decode_gqa_decode_bf16_pmc.md"

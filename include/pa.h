@@ -298,13 +298,14 @@ int32_t pa_pick_partition_size(const int32_t *host_seq_lens, int32_t num_seqs,
  *   PA_NO_SPLIT=1  pa_varlen_attention ignores partition_size (every row is
  *                  finished in place, partial buffers untouched) and
  *                  pa_split_kv_reduce does nothing.
- *   PA_DECODE_ROWS=0|1|2  decode batches over bf16 caches: 0 keeps the
+ *   PA_DECODE_ROWS=0|1|2  decode batches with bf16 queries: 0 keeps the
  *                  per-KV-head decode kernel (grid = KV heads x requests x
- *                  partitions); 2 takes the whole-row kernel (grid = requests
+ *                  partitions); 2 takes a whole-row kernel (grid = requests
  *                  x partitions, every KV head per workgroup) whenever the
  *                  head shape allows it; 1 (default) takes it when the launch
- *                  has at least 128 (request, partition) items.  Results agree
- *                  within rounding either way.
+ *                  has at least 128 (request, partition) items over bf16
+ *                  caches, 256 over 8-bit caches.  Results agree within
+ *                  rounding either way.
  */
 enum {
     PA_PATH_NONE = 0,        /* rejected, or nothing to do (empty batch) */

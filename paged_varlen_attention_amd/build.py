@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_api.cpp", "cache_write.hip", "decode.hip", "decode_mfma.hip", "decode_rows.hip", "reduce.hip",
+SOURCES = ["pa_api.cpp", "cache_write.hip", "decode.hip", "decode_mfma.hip", "decode_rows.hip", "decode_rows8.hip", "reduce.hip",
            "prefill.hip", "block_copy.hip", "noalloc.hip"]
 ARCH = "gfx950"
 

@@ -115,15 +115,6 @@ __device__ __forceinline__ int kv8_off(int t, int p) {
     return t * D + ((p ^ kv8_f<D>(t)) << 4);
 }
 
-// Eight E4M3 codes (two words) -> eight bf16 (exact).
-__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
-    const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
-    const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
-    const auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
-    const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
-    return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
 // Wait until this wave's DMA for the chunk `ahead` chunks before the newest
 // one has landed in LDS (vmcnt counts instructions and completes in order).
 template <int VM, int MAXA>

@@ -470,29 +470,43 @@ hipError_t launch_rows_128(const AttnParams &p, hipStream_t stream, LaunchInfo *
 
 }  // namespace
 
-// PA_DECODE_ROWS (read at every call): 0 never uses this kernel, 2 uses it
-// whenever the shape allows, otherwise (default) when the launch has enough
-// (request, partition) items to occupy most CUs with one workgroup each.
+// PA_DECODE_ROWS (read at every call): 0 never uses the whole-row kernels, 2
+// uses them whenever the shape allows, otherwise (default) when the launch
+// has enough (request, partition) items to occupy most CUs with one
+// workgroup each.
+// 8-bit caches take the whole-row kernel of decode_rows8.hip where its shape
+// rule allows, under the same launch-size rule.
 bool decode_rows_supported(const AttnParams &p) {
-    if (p.per_token || p.kv8 || p.dtype != 1) return false;
-    if (p.head_dim != 128 && p.head_dim != 256) return false;
-    if (p.group < 1 || p.group > 8 || p.hkv < 2) return false;
-    const int hpb = rows_hpb(p.group, p.hkv);
-    if (hpb < 2 || (p.hkv != hpb && p.hkv != 2 * hpb)) return false;
-    if (16 / hpb > p.block_size) return false;  // a chunk stays inside one page
-    // Two blocks of D = 256 make 16 KB tiles: 32 DMA instructions a chunk leave
-    // room for one ring stage only (vmcnt counts to 63), and that form measured
-    // slower than the per-head kernel.
-    if (p.head_dim == 256 && p.hkv == 2 * hpb) return false;
+    if (p.kv8) {
+        if (!decode_rows8_shape(p)) return false;
+    } else {
+        if (p.per_token || p.dtype != 1) return false;
+        if (p.head_dim != 128 && p.head_dim != 256) return false;
+        if (p.group < 1 || p.group > 8 || p.hkv < 2) return false;
+        const int hpb = rows_hpb(p.group, p.hkv);
+        if (hpb < 2 || (p.hkv != hpb && p.hkv != 2 * hpb)) return false;
+        if (16 / hpb > p.block_size) return false;  // a chunk stays inside one page
+        // Two blocks of D = 256 make 16 KB tiles: 32 DMA instructions a chunk
+        // leave room for one ring stage only (vmcnt counts to 63), and that form
+        // measured slower than the per-head kernel.
+        if (p.head_dim == 256 && p.hkv == 2 * hpb) return false;
+    }
     const char *e = std::getenv("PA_DECODE_ROWS");
     const int mode = e && e[0] ? std::atoi(e) : 1;
     if (mode == 0) return false;
     if (mode == 2) return true;
+    // Launch-size rule: enough (request, partition) items for most CUs.  The
+    // grid counts partitions up to the longest request, so short requests
+    // leave some empty; 8-bit rows carry half the bytes of a workgroup's
+    // chunks and need more items (GQA decode batch: 128 items, 86 of them
+    // non-empty, took 52.5 us against 42.7 on the per-head kernel; 256 items,
+    // 156 non-empty, 34.5 against 42.4).
     const long parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
-    return (long)p.num_seqs * parts >= 128;
+    return (long)p.num_seqs * parts >= (p.kv8 ? 256 : 128);
 }
 
 hipError_t launch_decode_rows(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
+    if (p.kv8) return launch_decode_rows8(p, stream, li);
     switch (p.head_dim) {
         case 128: return launch_rows_128(p, stream, li);
         case 256: return launch_rows_h<256, 1>(p, stream, li);

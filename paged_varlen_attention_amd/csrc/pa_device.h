@@ -194,6 +194,28 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(const void *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t *)(p));
 }
 
+// Eight E4M3 codes (two words, byte 0 first) -> eight bf16, exactly
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1).
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+    const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    const auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// gfx950 LDS transpose read of bytes (ds_read_b64_tr_b8).  Every lane passes
+// the address of 8 consecutive bytes; within each group of 16 lanes, lane i
+// receives byte i%8 of the chunks of lanes i/8, i/8+2, .., i/8+14, in that
+// order (lanes 2m and 2m+1 together hold row m of an 8 x 16 byte block, and
+// lane i gets its column i).  `p` must point into LDS.
+__device__ __forceinline__ uint2 lds_read_tr8(const void *p) {
+    typedef __attribute__((ext_vector_type(2))) int i32x2_t;
+    const i32x2_t w =
+        __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t *)(p));
+    return make_uint2((uint32_t)w[0], (uint32_t)w[1]);
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)p;
 }

@@ -94,8 +94,13 @@ hipError_t launch_copy_blocks(void *dst_k, void *dst_v, const void *src_k, const
 hipError_t launch_decode(const AttnParams &p, hipStream_t stream, LaunchInfo *li);
 // bf16 decode batches (one token per request, bf16 caches, group <= 8) on MFMA.
 bool decode_mfma_supported(const AttnParams &p);
+// The whole-row decode kernels (bf16 or 8-bit caches): whether a launch
+// takes one (shape and launch-size rule, PA_DECODE_ROWS) and its launcher.
 bool decode_rows_supported(const AttnParams &p);
 hipError_t launch_decode_rows(const AttnParams &p, hipStream_t stream, LaunchInfo *li);
+// Shape rule and launcher of the 8-bit whole-row kernel.
+bool decode_rows8_shape(const AttnParams &p);
+hipError_t launch_decode_rows8(const AttnParams &p, hipStream_t stream, LaunchInfo *li);
 hipError_t launch_decode_mfma(const AttnParams &p, hipStream_t stream, LaunchInfo *li);
 hipError_t launch_prefill(const AttnParams &p, hipStream_t stream, LaunchInfo *li);
 hipError_t launch_reduce(const ReduceParams &p, hipStream_t stream, LaunchInfo *li);
