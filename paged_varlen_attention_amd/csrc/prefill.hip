@@ -28,24 +28,30 @@
 //  * requests are mapped to workgroups without a host pass: virtual tile x
 //    belongs to the last request r with cu[r]/BQ + r <= x (surplus tiles exit);
 //  * 8-bit E4M3 caches (the library's own KV quantisation): tiles arrive by
-//    DMA into an 8-bit LDS ring (one instruction = 8 keys x 128 bytes, or 4
-//    whole 64-byte rows, so it never crosses a page), and after a barrier all threads
-//    convert the tile into the bf16 tile layout above with
-//    v_cvt_scalef32_pk_bf16_fp8 (exact), zeroing V rows past the sequence;
-//    the MFMA code is unchanged.  The head's K scale joins the softmax scale
-//    and its V scale the final normaliser.
+//    DMA as raw codes (key rows in key order, 16-byte pieces swizzled by key;
+//    one instruction = whole rows of one page), and the fragment reads take
+//    them directly -- K by ds_read_b64, V^T by ds_read_b64_tr_b8 (8 keys x 1
+//    dim per lane, the same k-slots as the bf16 path) -- widened in registers
+//    by v_cvt_scalef32_pk_bf16_fp8 (exact) right before their MFMA; V codes
+//    of keys past the sequence are zeroed in registers.  Half the LDS bytes
+//    and no conversion pass: the same one barrier per tile as bf16 caches.
+//    The head's K scale joins the softmax scale and its V scale the final
+//    normaliser.
 #include "prefill_tile.h"
 
 namespace pa {
 namespace {
 
 // Keys per tile and LDS stages by head size.  Waves per workgroup: 4, or at
-// D = 256 on large batches 8 (one workgroup per CU, each K/V tile in LDS
-// serving 256 rows): 5% faster on long uniform prompts, but 3-4% slower on
-// ragged batches of a few hundred workgroups, whose critical path the larger
-// q-tiles lengthen.  The switch is at PREFILL_WIDE_ITEMS work items of
-// 8-wave size (4 per CU on 256 CUs).  The 8-wave form (one workgroup per
-// CU) has the LDS for a third stage.
+// D = 256 on large batches over bf16 caches 8 (one workgroup per CU, each K/V
+// tile in LDS serving 256 rows): 5% faster on long uniform prompts, but 3-4%
+// slower on ragged batches of a few hundred workgroups, whose critical path
+// the larger q-tiles lengthen.  The switch is at PREFILL_WIDE_ITEMS work
+// items of 8-wave size (4 per CU on 256 CUs).  The 8-wave form (one
+// workgroup per CU) has the LDS for a third stage.  Over 8-bit caches the
+// 8-wave form runs short of registers (3 stages: spills inside the key loop,
+// 4,057 against 2,984 us on the uniform prefill; 2 stages: 3,135-3,146
+// against 3,083-3,106 us for 4 waves), so 8-bit caches keep 4 waves.
 constexpr int PREFILL_WIDE_ITEMS = 1024;
 constexpr int prefill_n(int D) { return D >= 256 ? 32 : 64; }
 
@@ -56,7 +62,7 @@ hipError_t launch_dw(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
 
 template <int D, bool KV8>
 hipError_t launch_d(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
-    if constexpr (D >= 256) {
+    if constexpr (D >= 256 && !KV8) {
         const int64_t bq8 = 8 * (32 / p.group);
         const int64_t parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
         const int64_t items8 = (p.total_q / bq8 + p.num_seqs) * p.hkv * parts;

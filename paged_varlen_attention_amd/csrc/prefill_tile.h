@@ -8,6 +8,8 @@
 // latencies exposed.
 #pragma once
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -38,27 +40,28 @@ struct PrefillCfg {
     static constexpr int IPG = GROUP_BYTES / 1024;  // DMA instructions per key group
     static constexpr int NI = T_BYTES / 1024;     // DMA instructions per tile
     static constexpr int NI_W = NI / NWV;         // per wave, per tensor
-    // 8-bit caches: NST raw stages (K tile, then V tile, N*D bytes each) ahead
-    // of one bf16 stage the MFMAs read
+    // 8-bit caches: NST stages of raw tiles (K tile, then V tile, N*D bytes
+    // each, row-major by key with swizzled 16-byte pieces) that the MFMA
+    // fragment reads take directly
     static constexpr int RG = KV8 ? D : R;        // bytes of a cached K/V row of one head
     static constexpr int RAW_T = N * D;           // one 8-bit tile
     static constexpr int RAW_STAGE = 2 * RAW_T;
-    // 8-bit DMA: D >= 128 moves 8 keys x 128 bytes per instruction (16 bytes a
-    // lane); 64-byte rows (D = 64) move 4 whole rows per instruction (4 bytes
-    // a lane), landing row-major
+    // 8-bit DMA: D >= 128 moves 1024 / D whole rows per instruction (16 bytes
+    // a lane); 64-byte rows (D = 64) move 4 rows per instruction (4 bytes a
+    // lane).  Either way an instruction never spans two pages.
     static constexpr bool ROWS8 = D < 128;
     static constexpr int DW8 = ROWS8 ? 4 : 16;
-    static constexpr int IPG8 = ROWS8 ? 1 : D / 128;  // instructions per 8-key group (D >= 128)
+    static constexpr int RPI8 = 64 * DW8 / D;     // rows per 8-bit DMA instruction
+    static constexpr int PPR8 = D / 16;           // 16-byte pieces per 8-bit row
     static constexpr int NI8_W = RAW_T / (64 * DW8) / NWV;  // per wave, per tensor, 8-bit
-    static constexpr int RAW_BYTES = KV8 ? NST * RAW_STAGE : 0;
-    static constexpr int LDS_BYTES = KV8 ? RAW_BYTES + STAGE : NST * STAGE;
+    static constexpr int LDS_BYTES = KV8 ? NST * RAW_STAGE : NST * STAGE;
     static_assert(!KV8 || ((D == 64 || D >= 128) && RAW_T % (64 * DW8 * NWV) == 0),
                   "8-bit tile shape");
     static_assert(NI % NWV == 0, "tile split over the waves");
     static_assert(RB == 1 || (RB == 2 && !KV8 && NWV == 4), "two row blocks: bf16 caches, 4 waves");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
     static_assert(2 * NI_W * (NST - 1) < 64, "vmcnt range");
-    static_assert(2 * NI8_W * NST < 64, "vmcnt range");
+    static_assert(2 * NI8_W * (NST - 1) < 64, "vmcnt range");
 };
 
 // Tile layout in LDS (K and V alike).  Keys come in groups of KG = 8; a
@@ -85,6 +88,27 @@ template <class C>
 __device__ __forceinline__ int tile_off(int key, int piece) {
     const int sp = piece ^ ((key >> 3) & 1);  // odd key groups swap the lines of a piece pair
     return (key >> 3) * C::GROUP_BYTES + sp * 128 + (((key & 7) ^ (((sp ^ (sp >> 1)) & 1) << 2)) << 4);
+}
+
+// 8-bit tile layout in LDS (K and V alike): key rows of D bytes in key order;
+// the 16-byte piece p of key k's row is stored at piece slot p ^ kv8_swz(k)
+// (kv8_swz < D / 16 depends on bits 0-3 of the key only).  The LDS serves 256
+// bytes a cycle; per 32 lanes:
+// * K (S^T A operand, ds_read_b64): the 32 keys of a block, one 8-byte half
+//   of one piece each.  Every 16-byte slot of the 256-byte bank window is hit
+//   by exactly 2 keys -- the least possible, since a piece's other half is
+//   not read -- so a read takes 4 cycles for 512 bytes, as the bf16 b128
+//   reads take for 1 KB.
+// * V^T (O^T A operand, ds_read_b64_tr_b8): in each 16 lanes, lanes 2m and
+//   2m+1 point at the two halves of one piece of key row m, the 8 rows being
+//   keys 4h .. 4h+3 and 8+4h .. 11+4h (the k-slot order of the bf16 path),
+//   and the two 16-lane groups of a half wave read pieces 2db and 2db+1: the
+//   swizzle gives the 16 (row, piece) pairs 16 distinct slots.
+template <int D>
+__device__ __forceinline__ int kv8_swz(int k) {
+    if constexpr (D == 256) return ((k & 3) << 1) | (((k >> 3) & 1) << 3) | ((k >> 2) & 1);
+    else if constexpr (D == 128) return (((k >> 1) & 1) << 1) | (((k >> 3) & 1) << 2) | ((k >> 2) & 1);
+    else return (((k >> 3) & 1) << 1) | ((k >> 2) & 1);
 }
 
 // Wait until the DMA of the tile `ahead` tiles before the newest one landed.
@@ -310,14 +334,24 @@ __global__ __launch_bounds__(NWV * 64, RB == 1 ? PREFILL_WAVES_PER_SIMD * 4 / NW
         }
     };
 
-    // 8-bit caches: instruction c of a raw tile covers key group c / IPG8,
-    // bytes 128*(c % IPG8) .. +128 of those 8 rows; lane l brings 16 codes of
-    // key l%8, piece l/8, landing at c*1024 + 16*l of the raw tile.  With
-    // 64-byte rows, instruction c covers keys 4c .. 4c+3 whole (lane l: key
-    // l/16, bytes 4*(l%16)), landing row-major at c*256 + 4*l.
-    const uint32_t dma_voff8 =
-        C::ROWS8 ? (uint32_t)(lane >> 4) * row_stride + (uint32_t)(lane & 15) * 4u
-                 : (uint32_t)(lane & 7) * row_stride + (uint32_t)(lane >> 3) * 16u;
+    // 8-bit caches: instruction c of a raw tile covers key rows c RPI8 ..
+    // c RPI8 + RPI8 - 1 and lands at c * 64 DW8 of the tile; lane l writes
+    // slot l % PPR8 (16 bytes; D = 64: dword l % 4 of slot (l % 16) / 4) of
+    // row l / (PPR8 or 16), fetching that row's piece slot ^ kv8_swz(row).
+    uint32_t voff8[C::NI8_W];
+#pragma unroll
+    for (int i = 0; i < C::NI8_W; ++i) {
+        const int c = wave * C::NI8_W + i;
+        if constexpr (C::ROWS8) {
+            const int row = 4 * c + (lane >> 4);
+            voff8[i] = (uint32_t)(lane >> 4) * row_stride +
+                       (uint32_t)((((lane & 15) >> 2) ^ kv8_swz<D>(row)) << 4) + (uint32_t)(lane & 3) * 4u;
+        } else {
+            const int row = C::RPI8 * c + lane / C::PPR8;
+            voff8[i] = (uint32_t)(lane / C::PPR8) * row_stride +
+                       (uint32_t)(((lane % C::PPR8) ^ kv8_swz<D>(row)) << 4);
+        }
+    }
     auto issue8 = [&](int kt, int stage) {
         const int lp0 = kt >> lbs;
         if (lp0 + ((C::N - 1) >> lbs) - win_page >= 64) {  // long ranges: slide the window
@@ -327,16 +361,14 @@ __global__ __launch_bounds__(NWV * 64, RB == 1 ? PREFILL_WAVES_PER_SIMD * 4 / NW
 #pragma unroll
         for (int i = 0; i < C::NI8_W; ++i) {
             const int c = wave * C::NI8_W + i;
-            // first key of the instruction (a 4- or 8-key group: never two pages)
-            const int k8 = kt + (C::ROWS8 ? 4 * c : C::KG * (c / C::IPG8));
+            const int k8 = kt + C::RPI8 * c;  // first key of the instruction
             const int lp = min(k8 >> lbs, seq_pages - 1);
             const int phys = __builtin_amdgcn_readlane(btv, lp - win_page);
             const char *base = kc + (uint64_t)phys * page_bytes + head_off +
-                               (uint32_t)(k8 & (bs - 1)) * row_stride +
-                               (C::ROWS8 ? 0 : 128 * (c % C::IPG8));
+                               (uint32_t)(k8 & (bs - 1)) * row_stride;
             const uint32_t l = lds0 + stage * C::RAW_STAGE + c * 64 * C::DW8;
-            dma_lds<C::DW8>(base, dma_voff8, l);
-            dma_lds<C::DW8>(base + v_minus_k, dma_voff8, l + C::RAW_T);
+            dma_lds<C::DW8>(base, voff8[i], l);
+            dma_lds<C::DW8>(base + v_minus_k, voff8[i], l + C::RAW_T);
         }
     };
 
@@ -384,12 +416,20 @@ __global__ __launch_bounds__(NWV * 64, RB == 1 ? PREFILL_WAVES_PER_SIMD * 4 / NW
     const int v_base_odd = C::GROUP_BYTES + (2 * (tg & 1) + (v_pb ^ 1)) * 128 +
                            (((4 * h + (ts >> 2)) ^ ((v_pb ^ 1 ^ (tg & 1)) << 2)) << 4) + 8 * (ts & 1);
 
+    // 8-bit fragment bases (the k-step or dim block enters by an XOR of bits
+    // 4..7, the key block and k-step pair by an immediate): K key lane & 31,
+    // half h; V^T key row k0 of the lane's 16-lane group (the bf16 path's
+    // k-slot order), piece 2db + (group & 1), half ts & 1.
+    const int k8_base = (((lane & 31) * D + 8 * h) | (kv8_swz<D>(lane & 31) << 4));
+    const int v8_k0 = (ts >> 1) < 4 ? 4 * h + (ts >> 1) : 8 + 4 * h + (ts >> 1) - 4;
+    const int v8_base = ((v8_k0 * D + 8 * (ts & 1)) | (((tg & 1) ^ kv8_swz<D>(v8_k0)) << 4));
+
     const int ntiles = (k_hi - k_lo + C::N - 1) / C::N;
     constexpr int VM = 2 * C::NI_W;
     constexpr int VM8 = 2 * C::NI8_W;
     if constexpr (KV8) {
 #pragma unroll
-        for (int s = 0; s < NST; ++s)
+        for (int s = 0; s < NST - 1; ++s)
             if (s < ntiles) issue8(k_lo + s * C::N, s);
     } else {
 #pragma unroll
@@ -403,46 +443,11 @@ __global__ __launch_bounds__(NWV * 64, RB == 1 ? PREFILL_WAVES_PER_SIMD * 4 / NW
         const char *kst;
         char *vst;
         if constexpr (KV8) {
-            // raw tile `it` is in once this wave's older DMA has landed; the
-            // barrier also means every wave is done with the bf16 stage
+            if (it + NST - 1 < ntiles) issue8(kt + (NST - 1) * C::N, (it + NST - 1) % NST);
             wait_tiles_ahead<VM8, NST - 1>(min(NST - 1, ntiles - 1 - it));
-            __syncthreads();
-            kst = lds + C::RAW_BYTES;
-            vst = const_cast<char *>(kst) + C::T_BYTES;
-            const char *raw = lds + stage * C::RAW_STAGE;
-            // 16 codes (key `key`, 16-byte piece rp of its row) -> bf16 pieces
-            // 2rp and 2rp+1; keys vary fastest so reads and writes are
-            // conflict-free; V rows past the sequence become zeros (NaN codes
-            // would survive p = 0 inside the MFMA)
-            constexpr int CH = C::N * (D / 16);  // 16-byte raw pieces per tensor
-            for (int i = threadIdx.x; i < 2 * CH; i += C::NTH) {
-                const bool isv = i >= CH;
-                const int ii = isv ? i - CH : i;
-                const int key = ii % C::N, rp = ii / C::N;
-                const int roff = C::ROWS8 ? key * D + rp * 16
-                                          : ((key >> 3) * C::IPG8 + (rp >> 3)) * 1024 +
-                                                (((rp & 7) << 3) + (key & 7)) * 16;
-                const uint4 w = *reinterpret_cast<const uint4 *>(raw + (isv ? C::RAW_T : 0) + roff);
-                uint4 lo, hi;
-                if (isv && kt + key >= seq_len) {
-                    lo = make_uint4(0, 0, 0, 0);
-                    hi = lo;
-                } else {
-                    lo.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false));
-                    lo.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true));
-                    lo.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false));
-                    lo.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true));
-                    hi.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.z, 1.0f, false));
-                    hi.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.z, 1.0f, true));
-                    hi.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.w, 1.0f, false));
-                    hi.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.w, 1.0f, true));
-                }
-                char *dst = (isv ? vst : const_cast<char *>(kst));
-                *reinterpret_cast<uint4 *>(dst + tile_off<C>(key, 2 * rp)) = lo;
-                *reinterpret_cast<uint4 *>(dst + tile_off<C>(key, 2 * rp + 1)) = hi;
-            }
-            __syncthreads();  // the bf16 tile is complete and the raw stage is free
-            if (it + NST < ntiles) issue8(kt + NST * C::N, stage);
+            kst = lds + stage * C::RAW_STAGE;
+            vst = const_cast<char *>(kst) + C::RAW_T;
+            __syncthreads();  // every wave's DMA share of this tile is in
         } else {
             if (it + NST - 1 < ntiles) issue(kt + (NST - 1) * C::N, (it + NST - 1) % NST);
             wait_tiles_ahead<VM, NST - 1>(min(NST - 1, ntiles - 1 - it));
@@ -471,16 +476,25 @@ __global__ __launch_bounds__(NWV * 64, RB == 1 ? PREFILL_WAVES_PER_SIMD * 4 / NW
         for (int b = 0; b < C::NB; ++b) {
 #pragma unroll
             for (int blk = 0; blk < RB; ++blk) s[blk][b] = f32x16_t{};
-            auto kread = [&](int ks) {
-                return *reinterpret_cast<const uint4 *>(kst + ((ks & 1) ? k_base_odd : k_base) +
-                                                        b * 4 * C::GROUP_BYTES + ks * 256);
+            // (8-bit caches: the raw 8 codes are in flight, widened at use)
+            using KFrag = std::conditional_t<KV8, uint2, uint4>;
+            auto kread = [&](int ks) -> KFrag {
+                if constexpr (KV8)
+                    return *reinterpret_cast<const uint2 *>(kst + (k8_base ^ (ks << 4)) + b * 32 * D);
+                else
+                    return *reinterpret_cast<const uint4 *>(kst + ((ks & 1) ? k_base_odd : k_base) +
+                                                            b * 4 * C::GROUP_BYTES + ks * 256);
             };
-            uint4 ka[PF_K];
+            KFrag ka[PF_K];
 #pragma unroll
             for (int ks = 0; ks < PF_K; ++ks) ka[ks] = kread(ks);
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
-                const uint4 a = ka[ks % PF_K];
+                uint4 a;
+                if constexpr (KV8)
+                    a = __builtin_bit_cast(uint4, e4m3x8_to_bf16(ka[ks % PF_K].x, ka[ks % PF_K].y));
+                else
+                    a = ka[ks % PF_K];
                 if (ks + PF_K < C::KS) ka[ks % PF_K] = kread(ks + PF_K);
                 // one K fragment serves every row block of the wave
 #pragma unroll
@@ -548,21 +562,48 @@ __global__ __launch_bounds__(NWV * 64, RB == 1 ? PREFILL_WAVES_PER_SIMD * 4 / NW
                     l[blk] = dot2(pk[blk][j / 2], 0x3F803F80u, l[blk]);
                 }
             // V^T fragments, streamed PF_V MFMAs ahead; MFMA i = (ks2, db)
-            auto vread = [&](int i) {
-                const char *a = vst + v_base + (4 * b + 2 * (i / C::DB)) * C::GROUP_BYTES +
-                                (i % C::DB) * 512;
-                const s16x4_t lo = lds_read_tr16(a);
-                const s16x4_t hi = lds_read_tr16(a - v_base + v_base_odd);
-                const s16x4_t av[2] = {lo, hi};
-                return __builtin_bit_cast(bf16x8_t, av);
+            // 8-bit caches: V codes of keys past the sequence may be anything
+            // (NaN codes), and p = 0 does not cancel a NaN inside the MFMA, so
+            // their bytes are zeroed in registers: byte m of a V^T fragment is
+            // key 32b + 16 ks2 + 4h + m (m < 4) or + 8 + 4h + m - 4.
+            uint2 vmask[2] = {make_uint2(~0u, ~0u), make_uint2(~0u, ~0u)};
+            if constexpr (KV8) {
+                if (kt + 32 * (b + 1) > seq_len) {
+                    auto bytes_below = [](int n) -> uint32_t {  // bytes 0 .. n-1 kept
+                        return n >= 4 ? ~0u : (n <= 0 ? 0u : (1u << (8 * n)) - 1u);
+                    };
+#pragma unroll
+                    for (int ks2 = 0; ks2 < 2; ++ks2) {
+                        const int lim = seq_len - kt - 32 * b - 16 * ks2 - 4 * h;
+                        vmask[ks2] = make_uint2(bytes_below(lim), bytes_below(lim - 8));
+                    }
+                }
+            }
+            using VFrag = std::conditional_t<KV8, uint2, bf16x8_t>;
+            auto vread = [&](int i) -> VFrag {
+                if constexpr (KV8) {
+                    return lds_read_tr8(vst + (v8_base ^ ((2 * (i % C::DB)) << 4)) +
+                                        (16 * (i / C::DB) + 32 * b) * D);
+                } else {
+                    const char *a = vst + v_base + (4 * b + 2 * (i / C::DB)) * C::GROUP_BYTES +
+                                    (i % C::DB) * 512;
+                    const s16x4_t lo = lds_read_tr16(a);
+                    const s16x4_t hi = lds_read_tr16(a - v_base + v_base_odd);
+                    const s16x4_t av[2] = {lo, hi};
+                    return __builtin_bit_cast(bf16x8_t, av);
+                }
             };
-            bf16x8_t va[PF_V];
+            VFrag va[PF_V];
 #pragma unroll
             for (int i = 0; i < PF_V; ++i) va[i] = vread(i);
 #pragma unroll
             for (int i = 0; i < 2 * C::DB; ++i) {
                 const int ks2 = i / C::DB, db = i % C::DB;
-                const bf16x8_t a = va[i % PF_V];
+                bf16x8_t a;
+                if constexpr (KV8)
+                    a = e4m3x8_to_bf16(va[i % PF_V].x & vmask[ks2].x, va[i % PF_V].y & vmask[ks2].y);
+                else
+                    a = va[i % PF_V];
                 if (i + PF_V < 2 * C::DB) va[i % PF_V] = vread(i + PF_V);
                 // one V^T fragment serves every row block of the wave
 #pragma unroll
@@ -575,9 +616,8 @@ __global__ __launch_bounds__(NWV * 64, RB == 1 ? PREFILL_WAVES_PER_SIMD * 4 / NW
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // everyone is done with this stage before it is refilled (8-bit caches:
-        // the next iteration's first barrier protects the bf16 stage)
-        if constexpr (!KV8) __syncthreads();
+        // everyone is done with this stage before it is refilled
+        __syncthreads();
     }
 
     // ---- finish: full exp-sum of each row, normalise, store ----
