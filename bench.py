@@ -601,7 +601,7 @@ def main():
         # 8-bit E4M3 caches (the library's KV quantisation): the same decode
         # batches with half the KV bytes
         for name8, w8, P8 in (("gqa_decode_fp8kv_P512", w, 512), ("gqa_decode_fp8kv_P1024", w, 1024),
-                              ("long_decode_fp8kv_P1024", w4, 1024)):
+                              ("long_decode_fp8kv_P2048", w4, 2048)):
             if not wanted(name8):
                 continue
             s8, k8, s8w, _ = measure(w8, P8, steps2, 5, args.copies, device, kv8=True)

@@ -48,16 +48,23 @@ def test_no_split_switch(monkeypatch, max_q):
     assert_close(out, ref, torch.bfloat16, "PA_NO_SPLIT")
 
 
-@pytest.mark.parametrize("name,expect", [("gqa_decode_bf16", 512), ("long_decode_bf16", 2048)])
-def test_policy_pick_on_the_device(name, expect):
+@pytest.mark.parametrize("name,expect,kv8", [("gqa_decode_bf16", 512, False), ("long_decode_bf16", 2048, False),
+                                             ("gqa_decode_bf16", 512, True), ("long_decode_bf16", 2048, True)],
+                         ids=["gqa", "long", "gqa-fp8kv", "long-fp8kv"])
+def test_policy_pick_on_the_device(name, expect, kv8):
     """pa_pick_partition_size with the device's own CU count (num_cus = 0) on
-    the two benchmark decode batches: it picks the partition size the
-    calibration found fastest for them on MI355X (256 CUs), and attention +
-    reduce at that size match the oracle on every row."""
+    the two benchmark decode batches, over bf16 and over 8-bit caches: it
+    picks the partition size measured fastest for them on MI355X (256 CUs;
+    8-bit GQA batch: 34 us at 512 against 40 / 42 at 256 / 1024; 8-bit long
+    decode: step 69.3-69.6 us at 2048 against 70.3-70.9 at 1024), and
+    attention + reduce at that size match the oracle on every row."""
     import paged_varlen_attention_amd as pa
+    import oracle_pins as pins
     w = W.CONFIGS[name]()
+    if kv8:
+        w = pins.fp8_case(w, 7)
     P = pa.pick_partition_size(w.seq_lens.tolist(), w.num_q_heads, w.num_kv_heads, w.head_dim,
-                               w.block_size, w.dtype)
+                               w.block_size, w.dtype, kv8=kv8)
     if torch.cuda.get_device_properties(0).multi_processor_count == 256:
         assert P == expect, P
     ref = oracle.run_workload(w)
