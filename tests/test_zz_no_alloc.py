@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import oracle
+import oracle_pins as pins
 import workloads as W
 from gpu_helpers import assert_close, run_gpu, to_device
 
@@ -25,8 +26,8 @@ def _noalloc(b, P, out):
 
 
 CASES = [
-    # (what, workload factory, partition sizes): decode batches on both MFMA
-    # decode kernels and a mixed batch on the tiles, the larger first
+    # (what, workload factory, partition sizes): decode batches on the MFMA
+    # decode kernels and mixed batches on the tiles, the larger first
     ("gqa decode", lambda: W.gqa_decode_bf16(), (512, 256)),
     ("small decode", lambda: W.random_case(71, num_seqs=5, max_q=1, max_ctx=1500, num_q_heads=16,
                                            num_kv_heads=2, head_dim=128, block_size=16,
@@ -37,6 +38,12 @@ CASES = [
     ("fp32 decode", lambda: W.random_case(73, num_seqs=3, max_q=1, max_ctx=700, num_q_heads=8,
                                           num_kv_heads=2, head_dim=64, block_size=16,
                                           dtype=torch.float32), (256,)),
+    # 8-bit caches: the whole-row 8-bit decode (256 and 512 launch items) and the tiles
+    ("gqa decode fp8kv", lambda: pins.fp8_case(W.gqa_decode_bf16(), 2), (512, 256)),
+    ("mixed fp8kv", lambda: pins.fp8_case(W.random_case(75, num_seqs=6, max_q=90, max_ctx=900,
+                                                         num_q_heads=16, num_kv_heads=2, head_dim=256,
+                                                         block_size=16, dtype=torch.bfloat16), 3),
+     (512, 0)),
 ]
 
 
