@@ -15,24 +15,34 @@ def _step_fn(w, b, P, new_rows, out, partials):
 
     def step():
         nk, nv, sm = new_rows
-        pa.reshape_and_cache(nk, nv, b.key_cache, b.value_cache, sm)
+        pa.reshape_and_cache(nk, nv, b.key_cache, b.value_cache, sm, k_scale=b.k_scale,
+                             v_scale=b.v_scale)
         pa.varlen_attention(b.q, b.key_cache, b.value_cache, b.cu_seqlens_q, b.seq_lens,
                             b.block_tables, max_q_len=b.max_q_len, max_seq_len=b.max_seq_len,
-                            scale=b.scale, partition_size=P, out=out, partials=partials)
+                            scale=b.scale, partition_size=P, out=out, partials=partials,
+                            k_scale=b.k_scale, v_scale=b.v_scale)
     return step
 
 
-@pytest.mark.parametrize("name,P", [("gqa_decode_bf16", 512), ("spec_verify_bf16", 0),
-                                    ("tiny_decode_f32", 0)])
-def test_graph_replays_match_eager(name, P):
+# (workload, partition size, 8-bit caches): the 8-bit GQA step runs the
+# quantising cache write and the whole-row 8-bit decode, the 8-bit mixed B
+# step the raw 8-bit tiles
+@pytest.mark.parametrize("name,P,kv8", [("gqa_decode_bf16", 512, False), ("spec_verify_bf16", 0, False),
+                                        ("tiny_decode_f32", 0, False), ("gqa_decode_bf16", 512, True),
+                                        ("mixed_prefill_bf16_B", 0, True)],
+                         ids=["gqa", "verify", "tiny-f32", "gqa-fp8kv", "mixed-B-fp8kv"])
+def test_graph_replays_match_eager(name, P, kv8):
     import paged_varlen_attention_amd as pa
-    w = W.CONFIGS[name]()
+    import oracle_pins as pins
+    w0 = W.CONFIGS[name]()
+    w = pins.fp8_case(w0, 11) if kv8 else w0
     b = to_device(w, write_cache=False)
     if w.slot_mapping is not None:
         # a slot addresses the same bytes in the 144-token and the 16-token page view
         rows = (w.new_key.cuda(), w.new_value.cuda(), w.slot_mapping.cuda())
     else:
-        k, v, s = W.last_token_rows(w)
+        # (8-bit caches: the bf16 rows, quantised again by the cache write)
+        k, v, s = W.last_token_rows(w0)
         rows = (k.cuda(), v.cuda(), s.cuda())
     out = torch.empty_like(b.q)
     partials = (pa.alloc_partials(w.total_q, w.num_q_heads, w.head_dim,
