@@ -185,9 +185,14 @@ def test_partition_policy():
     assert pick([4096] * 256, 32, 8, 128) == 0
     # one long request among short ones: no size both fills and balances
     assert pick([512] * 31 + [8000], 32, 8, 128) == 256
-    # 8-bit caches (per-head kernel): 16 x 4000 keys -> 2048 gives 16 x 2 x 8 = 256
+    # 8-bit caches: 16 x 4000 keys -> the whole-row 8-bit kernel needs 256 items (512 gives
+    # 16 x 8 = 128), so the per-head kernel at 2048 (16 x 2 x 8 = 256 workgroups)
     assert pick([4000] * 16, 32, 8, 128, kv8=True) == 2048
-    assert pick([4000] * 16, 32, 8, 128, kv8=True) == 2048
+    # the GQA batch over 8-bit caches: 512 routes 32 x 8 = 256 items to the whole-row 8-bit
+    # kernel (156 non-empty >= 144)
+    assert pick(sl2, 32, 8, 128, kv8=True) == 512
+    # 24/4/256 (group 6) has no 8-bit whole-row form: per-head, as over bf16 caches
+    assert pick([32768] * 4, 24, 4, 256, kv8=True) == 2048
     with pytest.raises(ValueError):
         pick([-5], 8, 1, 128)
     with pytest.raises(ValueError):
