@@ -184,11 +184,12 @@ __global__ __launch_bounds__(NWV * 64, RB == 1 ? PREFILL_WAVES_PER_SIMD * 4 / NW
     // virtual tiles from cu_q[r] / BQ + r on (one more than it can fill).
     const bool listed = p.num_seqs <= 64;
     int start = 0, nt = 0, real_tiles = p.grid_tiles;
+    int c0 = 0, ql = 0, sl = 0;  // listed: request `lane`'s first token, token and key counts
     if (listed) {
         const int i = lane;
-        int ql = 0, sl = 0;
         if (i < p.num_seqs) {
-            ql = p.cu_q[i + 1] - p.cu_q[i];
+            c0 = p.cu_q[i];
+            ql = p.cu_q[i + 1] - c0;
             sl = p.seq_lens[i];
         }
         nt = ql > 0 ? (ql + BQ - 1) / BQ : 0;
@@ -214,12 +215,17 @@ __global__ __launch_bounds__(NWV * 64, RB == 1 ? PREFILL_WAVES_PER_SIMD * 4 / NW
         kvh = (lam / p.grid_tiles) % p.hkv;
         part = lam / (p.grid_tiles * p.hkv);
     }
-    int r, tile;
+    // (listed: the request's bounds come from the lane that loaded them, so
+    // no second round of loads stands between the mapping and the first DMA)
+    int r, tile, q_begin, q_len, seq_len;
     if (listed) {
         const uint64_t mine = __ballot(lane < p.num_seqs && x >= start && x < start + nt);
         if (!mine) return;  // surplus virtual tile
         r = (int)__builtin_ctzll(mine);
         tile = x - __builtin_amdgcn_readlane(start, r);
+        q_begin = __builtin_amdgcn_readlane(c0, r);
+        q_len = __builtin_amdgcn_readlane(ql, r);
+        seq_len = __builtin_amdgcn_readlane(sl, r);
     } else {
         int lo = 0, hi = p.num_seqs - 1;
         while (lo < hi) {
@@ -228,12 +234,12 @@ __global__ __launch_bounds__(NWV * 64, RB == 1 ? PREFILL_WAVES_PER_SIMD * 4 / NW
         }
         r = lo;
         tile = x - (p.cu_q[r] / BQ + r);
+        q_begin = p.cu_q[r];
+        q_len = p.cu_q[r + 1] - q_begin;
+        seq_len = p.seq_lens[r];
     }
-    const int q_begin = p.cu_q[r];
-    const int q_len = p.cu_q[r + 1] - q_begin;
     const int j0 = tile * BQ;  // first token of the tile within the request
     if (tile < 0 || j0 >= q_len) return;
-    const int seq_len = p.seq_lens[r];
     const int ctx = seq_len - q_len;
     const int j_last = min(q_len, j0 + BQ) - 1;
     // keys of this workgroup: the partition, cut at the last token's position
