@@ -43,10 +43,11 @@ namespace pa {
 namespace {
 
 // Keys per tile and LDS stages by head size.  Waves per workgroup: 4, or at
-// D = 256 on large batches over bf16 caches 8 (one workgroup per CU, each K/V
-// tile in LDS serving 256 rows): 5% faster on long uniform prompts, but 3-4%
-// slower on ragged batches of a few hundred workgroups, whose critical path
-// the larger q-tiles lengthen.  The switch is at PREFILL_WIDE_ITEMS work
+// D >= 128 on large batches over bf16 caches 8 (one workgroup per CU, each
+// K/V tile in LDS serving 256 rows): 5% faster on long uniform prompts at
+// D = 256 and 6% at D = 128 (8 x 4,096 new tokens over 4,096 cached: 1.55
+// against 1.65 ms), but 3-4% slower on ragged batches of a few hundred
+// workgroups, whose critical path the larger q-tiles lengthen.  The switch is at PREFILL_WIDE_ITEMS work
 // items of 8-wave size (4 per CU on 256 CUs).  The 8-wave form (one
 // workgroup per CU) has the LDS for a third stage.  Over 8-bit caches the
 // 8-wave form runs short of registers (3 stages: spills inside the key loop,
@@ -62,7 +63,7 @@ hipError_t launch_dw(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
 
 template <int D, bool KV8>
 hipError_t launch_d(const AttnParams &p, hipStream_t stream, LaunchInfo *li) {
-    if constexpr (D >= 256 && !KV8) {
+    if constexpr (D >= 128 && !KV8) {
         const int64_t bq8 = 8 * (32 / p.group);
         const int64_t parts = p.partition ? (p.max_seq_len + p.partition - 1) / p.partition : 1;
         const int64_t items8 = (p.total_q / bq8 + p.num_seqs) * p.hkv * parts;

@@ -159,24 +159,25 @@ def test_large_partitions(max_q):
         assert_close(out, ref, torch.bfloat16, f"max_q={max_q} P={P}")
 
 
+@pytest.mark.parametrize("d", [256, 128])
 @pytest.mark.parametrize("kv8", [False, True], ids=["bf16", "fp8"])
-def test_wide_workgroups(kv8):
-    """A D=256 batch large enough for 8-wave workgroups (64/8 heads, ten
-    450..500-token prompts over short prefixes): the launch takes the 8-wave
-    kernel over bf16 caches and the 4-wave kernel over 8-bit caches (which
-    keep 4 waves), and sampled rows match the oracle."""
+def test_wide_workgroups(kv8, d):
+    """A batch large enough for 8-wave workgroups (64/8 heads, ten 450..500-
+    token prompts over short prefixes, D = 256 and 128): the launch takes the
+    8-wave kernel over bf16 caches and the 4-wave kernel over 8-bit caches
+    (which keep 4 waves), and sampled rows match the oracle."""
     import paged_varlen_attention_amd as pa
     import oracle_pins as pins
     from gpu_helpers import sample_rows
-    w = W.random_case(4242, num_seqs=10, min_q=450, max_q=500, max_ctx=200, num_q_heads=64,
-                      num_kv_heads=8, head_dim=256, block_size=16, dtype=torch.bfloat16)
+    w = W.random_case(4242 + d, num_seqs=10, min_q=450, max_q=500, max_ctx=200, num_q_heads=64,
+                      num_kv_heads=8, head_dim=d, block_size=16, dtype=torch.bfloat16)
     if kv8:
         w = pins.fp8_case(w, seed=42)
     rows = sample_rows(w, 160, seed=3)
     ref = oracle.run_workload(w, rows=rows)
     b = to_device(w)
     for P in (0, 256):
-        parts = (pa.alloc_partials(w.total_q, 64, 256, pa.max_partitions(w.max_seq_len, P), "cuda")
+        parts = (pa.alloc_partials(w.total_q, 64, d, pa.max_partitions(w.max_seq_len, P), "cuda")
                  if P else None)
         out = run_gpu(b, P, partials=parts, reduce=False)
         assert pa.last_dispatch()["block"] == (256 if kv8 else 512)  # waves x 64
